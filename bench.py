@@ -1,0 +1,228 @@
+"""Benchmark of the DynamicRad block-sparse attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--mode static|dynamic]
+
+One step = one pass of the whole hot path over one batch of synthetic input
+already resident in HBM: candidate build (asynchronous form), block mean
+pooling + scoring + selection, and block-sparse flash attention. The dense
+kernel is timed separately as the speedup denominator. Prints one JSON line.
+
+Metric: sparse-attention effective TFLOP/s (4 * B_s^2 * D per kept block,
+kept blocks only) with the speedup over the on-GPU dense kernel, on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "sparse-attn effective TFLOP/s + speedup vs dense at ≥80% sparsity, 1 GPU"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="wan14b_720p")
+    ap.add_argument("--mode", default="static", choices=["static", "dynamic"])
+    ap.add_argument("--stage-iters", type=int, default=20)
+    ap.add_argument("--dense-iters", type=int, default=3)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--cpu-blocks", type=int, default=160, help="query blocks in the CPU oracle sample")
+    return ap.parse_args()
+
+
+def event_ms(fn, iters, torch):
+    """Average ms per call from HIP events on the current stream (the stream
+    the library launches on)."""
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    s.record()
+    for _ in range(iters):
+        fn()
+    e.record()
+    e.synchronize()
+    return s.elapsed_time(e) / iters
+
+
+def kernel_source_digest():
+    p = os.path.join(ROOT, "block_sparse_attention_candidates_amd", "csrc", "attention.hip")
+    return hashlib.sha256(open(p, "rb").read()).hexdigest()
+
+
+def traffic_record(workload, mode):
+    """HBM bytes per sparse-attention launch from committed rocprofv3 PMC
+    counters, if they were taken on the current kernel source."""
+    p = os.path.join(ROOT, "profiles", "sparse_attn_traffic.json")
+    if not os.path.exists(p):
+        return None
+    rec = json.load(open(p)).get(f"{workload}/{mode}")
+    if not rec or rec.get("attention_hip_sha256") != kernel_source_digest():
+        return None
+    return rec
+
+
+def cpu_baseline(w, mode, ratio, tau, n_blocks):
+    """The CPU oracle, untuned, on a bounded sample: one head, n_blocks query
+    blocks spread over the sequence; every step of the path for those blocks
+    (candidate rows, pooling, scores, selection, attention)."""
+    import workloads
+    from oracle import dynrad_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        cores = 1
+    q, k, v = (x.astype(np.float64) for x in workloads.head_qkv(w, 0, 0))
+    Sb = w.num_blocks
+    blocks = np.unique(np.linspace(0, Sb - 1, n_blocks).astype(int))
+    t0 = time.perf_counter()
+    table = O.distance_table(w.num_frames, w.tokens_per_frame, w.block_size, w.gamma, w.lam)
+    qbar, kbar = O.pool_blocks(q, w.block_size), O.pool_blocks(k, w.block_size)
+    kept = {}
+    for a in blocks:
+        cols = O.candidate_row(int(a), w.num_frames, w.tokens_per_frame, w.block_size, w.gamma, w.lam,
+                               w.theta_c, w.theta_m, table=table)
+        s = (kbar[cols] @ qbar[a]) / math.sqrt(w.head_dim)
+        kept[int(a)] = O.select_row(s, cols, mode, ratio=ratio, tau=tau)
+    klist = [kept.get(a, np.zeros(0, dtype=np.int64)) for a in range(Sb)]
+    O.sparse_attention_rows(q, k, v, w.block_size, klist, [int(a) for a in blocks])
+    dt = time.perf_counter() - t0
+    flops = 4.0 * w.block_size ** 2 * w.head_dim * sum(len(kept[int(a)]) for a in blocks)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "seconds": round(dt, 3),
+            "sample": f"{w.name} head 0, {len(blocks)} of {Sb} query blocks (evenly spaced), all stages "
+                      f"(candidate rows, pooling, scores, {mode} selection, attention), float64 NumPy"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); multi-GPU execution is not part of "
+              f"this build", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import block_sparse_attention_candidates_amd as dr
+    import workloads
+    from block_sparse_attention_candidates_amd import _lib
+
+    if not os.path.exists(_lib.LIB_PATH):
+        from block_sparse_attention_candidates_amd import build
+        build.build()
+    w = workloads.get_workload(args.workload)
+    ratio = w.static_ratio if args.mode == "static" else 1.0
+    tau = w.dynamic_tau if args.mode == "dynamic" else 1.0
+    print(f"# generating {w.name}: B={w.batch} H={w.heads} S={w.seq_len} D={w.head_dim}", file=sys.stderr, flush=True)
+    qb, kb, vb = workloads.qkv_bits_parallel(w, workers=16)
+    q, k, v = (torch.from_numpy(x).view(torch.bfloat16).cuda() for x in (qb, kb, vb))
+    del qb, kb, vb
+    cfg = dr.radial_cfg(w.num_frames, w.tokens_per_frame, w.block_size, w.gamma, w.lam, w.theta_c, w.theta_m)
+    cand = dr.build_candidates(cfg)           # setup: sizes the buffers (reports nnz)
+    sel_kw = dict(mode=args.mode, ratio=ratio, tau=tau)
+    kept = dr.score_select(q, k, cand, **sel_kw)
+    import ctypes
+    L = _lib.lib()
+    out = torch.empty_like(q)
+    # preallocated buffers for the timed step (no allocation inside it)
+    dims = _lib.Dims(w.batch, w.heads, w.head_dim, 0)
+    selc = dr._select_cfg(args.mode, ratio, tau, 0)
+    wsb = ctypes.c_size_t(0)
+    _lib.check(L.dr_score_select_workspace(ctypes.byref(dims), ctypes.byref(cfg), ctypes.byref(selc), cand.nnz,
+                                           ctypes.byref(wsb)))
+    ws = torch.empty(wsb.value, dtype=torch.uint8, device="cuda")
+    row_ptr = torch.empty_like(cand.row_ptr)
+    cols = torch.empty_like(cand.cols)
+    kept_col, kept_cnt = torch.empty_like(kept.kept_col), torch.empty_like(kept.kept_cnt)
+    scale = 1.0 / math.sqrt(w.head_dim)
+
+    def stream():
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def step_candidates():
+        _lib.check(L.dr_build_candidates(ctypes.byref(cfg), row_ptr.data_ptr(), cols.data_ptr(), cand.nnz, None,
+                                         stream()))
+
+    def step_select():
+        _lib.check(L.dr_score_select(ctypes.byref(dims), ctypes.byref(cfg), ctypes.byref(selc), q.data_ptr(),
+                                     k.data_ptr(), row_ptr.data_ptr(), cols.data_ptr(), cand.nnz,
+                                     kept_col.data_ptr(), kept_cnt.data_ptr(), None, ws.data_ptr(), ws.numel(),
+                                     stream()))
+
+    def step_attn():
+        _lib.check(L.dr_sparse_attn(ctypes.byref(dims), ctypes.byref(cfg), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                    row_ptr.data_ptr(), cand.nnz, kept_col.data_ptr(), kept_cnt.data_ptr(),
+                                    ctypes.c_float(scale), out.data_ptr(), stream()))
+
+    def step():
+        step_candidates()
+        step_select()
+        step_attn()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+
+    # per-stage HIP-event timing on the launch stream
+    ms_cand = event_ms(step_candidates, args.stage_iters, torch)
+    ms_sel = event_ms(step_select, args.stage_iters, torch)
+    ms_attn = event_ms(step_attn, args.stage_iters, torch)
+    kept_total = int(kept_cnt.sum().item())
+    Sb = cand.num_blocks
+    flops = 4.0 * w.block_size ** 2 * w.head_dim * kept_total
+    sparsity = 1.0 - kept_total / (w.batch * w.heads * Sb * Sb)
+    ms_dense = None
+    if not args.no_dense:
+        dense_out = torch.empty_like(q)
+        dr.attn(q, k, v, out=dense_out)
+        ms_dense = event_ms(lambda: dr.attn(q, k, v, out=dense_out), args.dense_iters, torch)
+    dense_flops = 4.0 * w.batch * w.heads * w.seq_len ** 2 * w.head_dim
+    value = flops / (ms_step * 1e-3) / 1e12
+    achieved = flops / (ms_attn * 1e-3) / 1e12
+    tr = traffic_record(w.name, args.mode)
+    res = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "mode": args.mode, "ratio": ratio if args.mode == "static" else None,
+                   "tau": tau if args.mode == "dynamic" else None, "batch": w.batch, "heads": w.heads,
+                   "seq_len": w.seq_len, "head_dim": w.head_dim, "block_size": w.block_size, "gamma": w.gamma,
+                   "lambda": w.lam, "parallelism": "single-gpu"},
+        "sparsity": round(sparsity, 4),
+        "candidate_density": round(cand.nnz / Sb ** 2, 4),
+        "kept_blocks": kept_total,
+        "speedup_vs_dense": round(ms_dense / ms_step, 3) if ms_dense else None,
+        "speedup_vs_dense_attention_only": round(ms_dense / ms_attn, 3) if ms_dense else None,
+        "stage_ms": {"build_candidates": round(ms_cand, 4), "score_select": round(ms_sel, 4),
+                     "sparse_attn": round(ms_attn, 4), "dense_attn": round(ms_dense, 3) if ms_dense else None},
+        "dense_tflops": round(dense_flops / (ms_dense * 1e-3) / 1e12, 2) if ms_dense else None,
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": tr["hbm_bytes_per_launch"] if tr else None,
+                     "kernel": "dr_sparse_attn (attn_kernel<128,B_s,sparse>)"},
+    }
+    if not args.no_cpu:
+        print("# timing the CPU oracle sample", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(w, args.mode, ratio, tau, args.cpu_blocks)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

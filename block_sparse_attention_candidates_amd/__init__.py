@@ -1,0 +1,186 @@
+"""DynamicRad block-sparse attention hot path for MI355X (gfx950).
+
+Thin Python binding over libdynrad.so (include/dynrad.h). Every step of the
+path runs in the library's HIP kernels; this module only checks tensor
+shapes/dtypes, allocates outputs with PyTorch and passes raw device pointers
+plus the current HIP stream. Method: "DynamicRad: Content-Adaptive Sparse
+Attention for Long Video Diffusion" (arXiv 2604.20470).
+
+    cand = build_candidates(radial_cfg(num_frames, tokens_per_frame, block_size, gamma, lam))
+    kept = score_select(q, k, cand, mode="static", ratio=0.15)      # or mode="dynamic", tau=0.8
+    out  = sparse_attn(q, k, v, cand, kept)
+    ref  = attn(q, k, v)                                            # dense baseline
+
+q, k, v: torch.bfloat16 [B, H, S, D] contiguous CUDA (HIP) tensors,
+S = num_frames * tokens_per_frame.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import math
+from typing import Optional
+
+import numpy as np
+
+from . import _lib as _L
+from ._lib import Dims, DynradError, RadialCfg, SelectCfg, check, lib
+
+__all__ = ["radial_cfg", "num_blocks", "distance_table", "Candidates", "Kept", "build_candidates",
+           "score_select", "sparse_attn", "attn", "DynradError", "kept_from_lists"]
+
+
+def radial_cfg(num_frames: int, tokens_per_frame: int, block_size: int, gamma: float, lam: float,
+               theta_c: float = 0.0, theta_m: float = 0.0) -> RadialCfg:
+    return RadialCfg(int(num_frames), int(tokens_per_frame), int(block_size), 0, float(gamma), float(lam),
+                     float(theta_c), float(theta_m))
+
+
+def num_blocks(cfg: RadialCfg) -> int:
+    n = lib().dr_num_blocks(ctypes.byref(cfg))
+    if n < 0:
+        check(int(-n))
+    return int(n)
+
+
+def distance_table(cfg: RadialCfg):
+    """Host per-distance table (w(t), sf(t)) exactly as the candidate kernel uses it."""
+    w = np.zeros(cfg.num_frames, dtype=np.int32)
+    sf = np.zeros(cfg.num_frames, dtype=np.int32)
+    check(lib().dr_distance_table(ctypes.byref(cfg), w.ctypes.data, sf.ctypes.data))
+    return w, sf
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream(device):
+    return ctypes.c_void_p(_torch().cuda.current_stream(device).cuda_stream)
+
+
+@dataclasses.dataclass
+class Candidates:
+    cfg: RadialCfg
+    row_ptr: "object"   # torch.int32 [S_b + 1], device
+    cols: "object"      # torch.int32 [nnz], device
+    nnz: int
+    num_blocks: int
+
+
+@dataclasses.dataclass
+class Kept:
+    kept_col: "object"  # torch.int32 [B * H * nnz]
+    kept_cnt: "object"  # torch.int32 [B * H * S_b]
+    scores: "object" = None
+
+
+def build_candidates(cfg: RadialCfg, device="cuda") -> Candidates:
+    torch = _torch()
+    Sb = num_blocks(cfg)
+    row_ptr = torch.empty(Sb + 1, dtype=torch.int32, device=device)
+    cap = min(Sb * Sb, 1 << 22)
+    cols = torch.empty(cap, dtype=torch.int32, device=device)
+    nnz = ctypes.c_int64(0)
+    st = lib().dr_build_candidates(ctypes.byref(cfg), row_ptr.data_ptr(), cols.data_ptr(), cap,
+                                   ctypes.byref(nnz), _stream(row_ptr.device))
+    if st == _L.DR_ERR_CAPACITY:
+        cols = torch.empty(nnz.value, dtype=torch.int32, device=device)
+        st = lib().dr_build_candidates(ctypes.byref(cfg), row_ptr.data_ptr(), cols.data_ptr(), nnz.value,
+                                       ctypes.byref(nnz), _stream(row_ptr.device))
+    check(st)
+    return Candidates(cfg, row_ptr, cols[:nnz.value], int(nnz.value), Sb)
+
+
+def _check_qkv(*ts):
+    torch = _torch()
+    shape = ts[0].shape
+    for t in ts:
+        if t.dtype != torch.bfloat16 or t.dim() != 4 or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError("q, k, v must be contiguous torch.bfloat16 CUDA tensors [B, H, S, D]")
+        if t.shape != shape:
+            raise ValueError("q, k, v must have the same shape")
+    return shape
+
+
+def _dims(shape) -> Dims:
+    return Dims(int(shape[0]), int(shape[1]), int(shape[3]), 0)
+
+
+def _select_cfg(mode: str, ratio: float, tau: float, score_heads: int) -> SelectCfg:
+    m = {"static": _L.DR_STATIC_RATIO, "static_ratio": _L.DR_STATIC_RATIO,
+         "dynamic": _L.DR_DYNAMIC_THRESHOLD, "dynamic_threshold": _L.DR_DYNAMIC_THRESHOLD}[mode]
+    return SelectCfg(m, int(score_heads), float(ratio), float(tau))
+
+
+def score_select(q, k, cand: Candidates, mode: str = "static", ratio: float = 1.0, tau: float = 1.0,
+                 score_heads: int = 0, return_scores: bool = False, workspace=None) -> Kept:
+    torch = _torch()
+    shape = _check_qkv(q, k)
+    if shape[2] != cand.cfg.num_frames * cand.cfg.tokens_per_frame:
+        raise ValueError("sequence length does not match the candidate configuration")
+    dims = _dims(shape)
+    sel = _select_cfg(mode, ratio, tau, score_heads)
+    B, H = int(shape[0]), int(shape[1])
+    ws_bytes = ctypes.c_size_t(0)
+    check(lib().dr_score_select_workspace(ctypes.byref(dims), ctypes.byref(cand.cfg), ctypes.byref(sel),
+                                          cand.nnz, ctypes.byref(ws_bytes)))
+    if workspace is None or workspace.numel() < ws_bytes.value:
+        workspace = torch.empty(ws_bytes.value, dtype=torch.uint8, device=q.device)
+    kept_col = torch.empty(B * H * cand.nnz, dtype=torch.int32, device=q.device)
+    kept_cnt = torch.empty(B * H * cand.num_blocks, dtype=torch.int32, device=q.device)
+    scores = None
+    if return_scores:
+        hm = 1 if score_heads > 0 else H
+        scores = torch.empty(B * hm * cand.nnz, dtype=torch.float32, device=q.device)
+    check(lib().dr_score_select(ctypes.byref(dims), ctypes.byref(cand.cfg), ctypes.byref(sel), q.data_ptr(),
+                                k.data_ptr(), cand.row_ptr.data_ptr(), cand.cols.data_ptr(), cand.nnz,
+                                kept_col.data_ptr(), kept_cnt.data_ptr(),
+                                scores.data_ptr() if scores is not None else None,
+                                workspace.data_ptr(), workspace.numel(), _stream(q.device)))
+    return Kept(kept_col, kept_cnt, scores)
+
+
+def sparse_attn(q, k, v, cand: Candidates, kept: Kept, softmax_scale: Optional[float] = None, out=None):
+    torch = _torch()
+    shape = _check_qkv(q, k, v)
+    dims = _dims(shape)
+    scale = 1.0 / math.sqrt(shape[3]) if softmax_scale is None else float(softmax_scale)
+    if out is None:
+        out = torch.empty_like(q)
+    check(lib().dr_sparse_attn(ctypes.byref(dims), ctypes.byref(cand.cfg), q.data_ptr(), k.data_ptr(),
+                               v.data_ptr(), cand.row_ptr.data_ptr(), cand.nnz, kept.kept_col.data_ptr(),
+                               kept.kept_cnt.data_ptr(), scale, out.data_ptr(), _stream(q.device)))
+    return out
+
+
+def attn(q, k, v, softmax_scale: Optional[float] = None, out=None):
+    torch = _torch()
+    shape = _check_qkv(q, k, v)
+    dims = _dims(shape)
+    scale = 1.0 / math.sqrt(shape[3]) if softmax_scale is None else float(softmax_scale)
+    if out is None:
+        out = torch.empty_like(q)
+    check(lib().dr_attn(ctypes.byref(dims), int(shape[2]), q.data_ptr(), k.data_ptr(), v.data_ptr(), scale,
+                        out.data_ptr(), _stream(q.device)))
+    return out
+
+
+def kept_from_lists(lists, row_ptr_host, batch: int, heads: int, device="cuda") -> Kept:
+    """Kept-list buffers in the library layout from host lists:
+    lists[(b, h)][a] = ascending key-block indices kept by query block a.
+    (Used to feed any externally computed mask, e.g. a reference one.)"""
+    torch = _torch()
+    row_ptr_host = np.asarray(row_ptr_host, dtype=np.int64)
+    Sb = len(row_ptr_host) - 1
+    nnz = int(row_ptr_host[-1])
+    col = np.zeros(batch * heads * nnz, dtype=np.int32)
+    cnt = np.zeros(batch * heads * Sb, dtype=np.int32)
+    for (b, h), rows in lists.items():
+        base = (b * heads + h) * nnz
+        for a, ks in enumerate(rows):
+            ks = np.asarray(ks, dtype=np.int32)
+            col[base + row_ptr_host[a]: base + row_ptr_host[a] + len(ks)] = ks
+            cnt[(b * heads + h) * Sb + a] = len(ks)
+    return Kept(torch.from_numpy(col).to(device), torch.from_numpy(cnt).to(device))

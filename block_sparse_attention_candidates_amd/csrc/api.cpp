@@ -1,0 +1,333 @@
+// C ABI of the DynamicRad hot path (include/dynrad.h): argument validation,
+// the host per-distance table, workspace layout and kernel launches.
+// Every check runs before any HIP call, so an invalid call touches no device.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "../../include/dynrad.h"
+#include "dr_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+dr_status fail(dr_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+dr_status ok() {
+  g_last_error.clear();
+  return DR_OK;
+}
+
+dr_status hip_fail(hipError_t e, const char* what) {
+  return fail(DR_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool finite(double x) { return isfinite(x) != 0; }
+
+struct Layout {
+  long long S;
+  int Sb;
+};
+
+dr_status check_radial(const dr_radial_cfg* c, Layout* out) {
+  if (!c) return fail(DR_ERR_INVALID_ARG, "radial config is NULL");
+  if (c->num_frames < 1 || c->tokens_per_frame < 1 || c->block_size < 1)
+    return fail(DR_ERR_INVALID_ARG, "num_frames, tokens_per_frame and block_size must be >= 1");
+  if (c->reserved != 0) return fail(DR_ERR_INVALID_ARG, "radial config reserved field must be 0");
+  if (!finite(c->gamma) || c->gamma <= 0.0) return fail(DR_ERR_INVALID_ARG, "gamma must be finite and > 0");
+  if (!finite(c->lambda) || c->lambda < 0.0) return fail(DR_ERR_INVALID_ARG, "lambda must be finite and >= 0");
+  if (!finite(c->theta_c) || c->theta_c < 0.0 || c->theta_c > 1.0)
+    return fail(DR_ERR_INVALID_ARG, "theta_c must be in [0, 1]");
+  if (!finite(c->theta_m) || c->theta_m < 0.0 || c->theta_m > 1.0)
+    return fail(DR_ERR_INVALID_ARG, "theta_m must be in [0, 1]");
+  if (c->block_size != 32 && c->block_size != 64)
+    return fail(DR_ERR_UNSUPPORTED, "block_size %d not built (32 or 64)", c->block_size);
+  if (c->num_frames > dr::kMaxFrames)
+    return fail(DR_ERR_UNSUPPORTED, "num_frames %d above the limit %d", c->num_frames, dr::kMaxFrames);
+  const long long S = (long long)c->num_frames * c->tokens_per_frame;
+  const long long Sb = (S + c->block_size - 1) / c->block_size;
+  if (Sb > dr::kMaxBlocks)
+    return fail(DR_ERR_UNSUPPORTED, "S_b = %lld blocks above the limit %d", Sb, dr::kMaxBlocks);
+  if (out) {
+    out->S = S;
+    out->Sb = (int)Sb;
+  }
+  return DR_OK;
+}
+
+dr_status check_dims(const dr_dims* d) {
+  if (!d) return fail(DR_ERR_INVALID_ARG, "dims is NULL");
+  if (d->batch < 1 || d->heads < 1 || d->head_dim < 1)
+    return fail(DR_ERR_INVALID_ARG, "batch, heads and head_dim must be >= 1");
+  if (d->reserved != 0) return fail(DR_ERR_INVALID_ARG, "dims reserved field must be 0");
+  if (d->head_dim != 64 && d->head_dim != 128)
+    return fail(DR_ERR_UNSUPPORTED, "head_dim %d not built (64 or 128)", d->head_dim);
+  if ((long long)d->batch * d->heads > 65535)
+    return fail(DR_ERR_UNSUPPORTED, "batch * heads above 65535");
+  return DR_OK;
+}
+
+dr_status check_select(const dr_select_cfg* s, const dr_dims* d) {
+  if (!s) return fail(DR_ERR_INVALID_ARG, "select config is NULL");
+  if (s->mode != DR_STATIC_RATIO && s->mode != DR_DYNAMIC_THRESHOLD)
+    return fail(DR_ERR_INVALID_ARG, "mode %d is neither static_ratio (0) nor dynamic_threshold (1)", s->mode);
+  if (s->score_heads < 0 || s->score_heads > d->heads)
+    return fail(DR_ERR_INVALID_ARG, "score_heads %d outside [0, heads]", s->score_heads);
+  if (s->mode == DR_STATIC_RATIO && (!finite(s->ratio) || s->ratio <= 0.0 || s->ratio > 1.0))
+    return fail(DR_ERR_INVALID_ARG, "ratio must be in (0, 1]");
+  if (s->mode == DR_DYNAMIC_THRESHOLD && (!finite(s->tau) || s->tau <= 0.0 || s->tau > 1.0))
+    return fail(DR_ERR_INVALID_ARG, "tau must be in (0, 1]");
+  return DR_OK;
+}
+
+dr_status check_nnz(long long nnz, int Sb, const dr_dims* d) {
+  if (nnz < 1 || nnz > (long long)Sb * Sb)
+    return fail(DR_ERR_INVALID_ARG, "nnz %lld outside [1, S_b^2]", nnz);
+  if ((long long)d->batch * d->heads * nnz >= (1LL << 31))
+    return fail(DR_ERR_UNSUPPORTED, "batch * heads * nnz reaches 2^31");
+  return DR_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct WsLayout {
+  size_t qbar, kbar, scores, total;
+  int Hp, Hm, g;
+};
+
+WsLayout ws_layout(const dr_dims* d, int Sb, const dr_select_cfg* s, long long nnz) {
+  WsLayout w;
+  w.g = s->score_heads > 0 ? s->score_heads : 1;
+  w.Hp = s->score_heads > 0 ? s->score_heads : d->heads;
+  w.Hm = s->score_heads > 0 ? 1 : d->heads;
+  const size_t pooled = align256((size_t)d->batch * w.Hp * Sb * d->head_dim * sizeof(float));
+  w.qbar = 0;
+  w.kbar = pooled;
+  w.scores = 2 * pooled;
+  w.total = w.scores + align256((size_t)d->batch * w.Hm * nnz * sizeof(float));
+  return w;
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t dr_num_blocks(const dr_radial_cfg* cfg) {
+  Layout L;
+  const dr_status st = check_radial(cfg, &L);
+  if (st != DR_OK) return -(int64_t)st;
+  ok();
+  return L.Sb;
+}
+
+dr_status dr_distance_table(const dr_radial_cfg* cfg, int32_t* w, int32_t* sf) {
+  dr_status st = check_radial(cfg, nullptr);
+  if (st != DR_OK) return st;
+  if (!w || !sf) return fail(DR_ERR_INVALID_ARG, "w and sf must be non-NULL");
+  const int L0 = dr::base_span(cfg->tokens_per_frame);
+  for (int t = 0; t < cfg->num_frames; ++t) {
+    int ww, ss;
+    dr::table_entry(t, cfg->tokens_per_frame, cfg->block_size, L0, cfg->gamma, cfg->lambda, &ww, &ss);
+    w[t] = ww;
+    sf[t] = ss;
+  }
+  return ok();
+}
+
+dr_status dr_build_candidates(const dr_radial_cfg* cfg, int32_t* row_ptr, int32_t* cols, int64_t cap,
+                              int64_t* nnz, hipStream_t stream) {
+  Layout L;
+  dr_status st = check_radial(cfg, &L);
+  if (st != DR_OK) return st;
+  if (!row_ptr || !cols) return fail(DR_ERR_INVALID_ARG, "row_ptr and cols must be non-NULL");
+  if (cap < 1) return fail(DR_ERR_INVALID_ARG, "cap must be >= 1");
+  dr::CandParams p;
+  p.Nf = cfg->num_frames;
+  p.Nt = cfg->tokens_per_frame;
+  p.Bs = cfg->block_size;
+  p.S = (int)L.S;
+  p.Sb = L.Sb;
+  p.L0 = dr::base_span(p.Nt);
+  p.gamma = cfg->gamma;
+  p.lambda = cfg->lambda;
+  p.theta_c = cfg->theta_c;
+  p.theta_m = cfg->theta_m;
+  hipError_t e = dr::launch_candidates(p, row_ptr, cols, cap, stream);
+  if (e != hipSuccess) return hip_fail(e, "candidate kernels");
+  if (nnz) {
+    int32_t total = 0;
+    e = hipMemcpyAsync(&total, row_ptr + L.Sb, sizeof(int32_t), hipMemcpyDeviceToHost, stream);
+    if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(nnz)");
+    e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+    *nnz = total;
+    if (total > cap)
+      return fail(DR_ERR_CAPACITY, "candidate count %d exceeds cap %lld", total, (long long)cap);
+  }
+  return ok();
+}
+
+dr_status dr_score_select_workspace(const dr_dims* dims, const dr_radial_cfg* cfg, const dr_select_cfg* sel,
+                                    int64_t nnz, size_t* bytes) {
+  Layout L;
+  dr_status st = check_radial(cfg, &L);
+  if (st != DR_OK) return st;
+  if ((st = check_dims(dims)) != DR_OK) return st;
+  if ((st = check_select(sel, dims)) != DR_OK) return st;
+  if ((st = check_nnz(nnz, L.Sb, dims)) != DR_OK) return st;
+  if (!bytes) return fail(DR_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = ws_layout(dims, L.Sb, sel, nnz).total;
+  return ok();
+}
+
+dr_status dr_score_select(const dr_dims* dims, const dr_radial_cfg* cfg, const dr_select_cfg* sel,
+                          const void* q, const void* k, const int32_t* row_ptr, const int32_t* cols,
+                          int64_t nnz, int32_t* kept_col, int32_t* kept_cnt, float* scores_out, void* ws,
+                          size_t ws_bytes, hipStream_t stream) {
+  Layout L;
+  dr_status st = check_radial(cfg, &L);
+  if (st != DR_OK) return st;
+  if ((st = check_dims(dims)) != DR_OK) return st;
+  if ((st = check_select(sel, dims)) != DR_OK) return st;
+  if ((st = check_nnz(nnz, L.Sb, dims)) != DR_OK) return st;
+  if (!q || !k || !row_ptr || !cols || !kept_col || !kept_cnt || !ws)
+    return fail(DR_ERR_INVALID_ARG, "q, k, row_ptr, cols, kept_col, kept_cnt and ws must be non-NULL");
+  const WsLayout w = ws_layout(dims, L.Sb, sel, nnz);
+  if (ws_bytes < w.total)
+    return fail(DR_ERR_CAPACITY, "workspace of %zu bytes below the %zu required", ws_bytes, w.total);
+  unsigned char* wsb = static_cast<unsigned char*>(ws);
+  float* qbar = reinterpret_cast<float*>(wsb + w.qbar);
+  float* kbar = reinterpret_cast<float*>(wsb + w.kbar);
+  float* scores = scores_out ? scores_out : reinterpret_cast<float*>(wsb + w.scores);
+
+  dr::PoolParams pp;
+  pp.q = static_cast<const uint16_t*>(q);
+  pp.k = static_cast<const uint16_t*>(k);
+  pp.qbar = qbar;
+  pp.kbar = kbar;
+  pp.B = dims->batch;
+  pp.H = dims->heads;
+  pp.Hp = w.Hp;
+  pp.S = (int)L.S;
+  pp.Sb = L.Sb;
+  pp.Bs = cfg->block_size;
+  pp.D = dims->head_dim;
+  hipError_t e = dr::launch_pool(pp, stream);
+  if (e != hipSuccess) return hip_fail(e, "pool kernel");
+
+  dr::ScoreParams sp;
+  sp.qbar = qbar;
+  sp.kbar = kbar;
+  sp.row_ptr = row_ptr;
+  sp.cols = cols;
+  sp.scores = scores;
+  sp.nnz = nnz;
+  sp.Sb = L.Sb;
+  sp.Hp = w.Hp;
+  sp.Hm = w.Hm;
+  sp.g = w.g;
+  sp.D = dims->head_dim;
+  sp.scale = (float)(1.0 / (sqrt((double)dims->head_dim) * (double)w.g));
+  e = dr::launch_scores(sp, dims->batch, stream);
+  if (e != hipSuccess) return hip_fail(e, "score kernel");
+
+  dr::SelectParams xp;
+  xp.scores = scores;
+  xp.row_ptr = row_ptr;
+  xp.cols = cols;
+  xp.kept_col = kept_col;
+  xp.kept_cnt = kept_cnt;
+  xp.nnz = nnz;
+  xp.Sb = L.Sb;
+  xp.H = dims->heads;
+  xp.Hm = w.Hm;
+  xp.mode = sel->mode;
+  xp.ratio = sel->ratio;
+  xp.tau = sel->tau;
+  xp.max_row = L.Sb;
+  e = dr::launch_select(xp, dims->batch, stream);
+  if (e != hipSuccess) return hip_fail(e, "select kernel");
+  return ok();
+}
+
+static dr_status attn_common(const dr_dims* dims, long long S, const void* q, const void* k, const void* v,
+                             float scale, void* out, dr::AttnParams* p) {
+  if (!q || !k || !v || !out) return fail(DR_ERR_INVALID_ARG, "q, k, v and out must be non-NULL");
+  if (!isfinite(scale)) return fail(DR_ERR_INVALID_ARG, "softmax_scale must be finite");
+  if (out == q || out == k || out == v) return fail(DR_ERR_INVALID_ARG, "out must not alias q, k or v");
+  if ((long long)dims->batch * dims->heads * S * dims->head_dim >= (1LL << 40))
+    return fail(DR_ERR_UNSUPPORTED, "tensor too large");
+  p->q = static_cast<const uint16_t*>(q);
+  p->k = static_cast<const uint16_t*>(k);
+  p->v = static_cast<const uint16_t*>(v);
+  p->o = static_cast<uint16_t*>(out);
+  p->S = (int)S;
+  p->BH = dims->batch * dims->heads;
+  p->n_tiles = (int)((S + 255) / 256);
+  p->scale_log2 = scale * 1.4426950408889634f;
+  return DR_OK;
+}
+
+dr_status dr_sparse_attn(const dr_dims* dims, const dr_radial_cfg* cfg, const void* q, const void* k,
+                         const void* v, const int32_t* row_ptr, int64_t nnz, const int32_t* kept_col,
+                         const int32_t* kept_cnt, float softmax_scale, void* out, hipStream_t stream) {
+  Layout L;
+  dr_status st = check_radial(cfg, &L);
+  if (st != DR_OK) return st;
+  if ((st = check_dims(dims)) != DR_OK) return st;
+  if ((st = check_nnz(nnz, L.Sb, dims)) != DR_OK) return st;
+  if (!row_ptr || !kept_col || !kept_cnt) return fail(DR_ERR_INVALID_ARG, "row_ptr, kept_col and kept_cnt must be non-NULL");
+  dr::AttnParams p;
+  if ((st = attn_common(dims, L.S, q, k, v, softmax_scale, out, &p)) != DR_OK) return st;
+  p.row_ptr = row_ptr;
+  p.kept_col = kept_col;
+  p.kept_cnt = kept_cnt;
+  p.nnz = nnz;
+  p.Sb = L.Sb;
+  const hipError_t e = dr::launch_sparse_attn(p, dims->head_dim, cfg->block_size, stream);
+  if (e != hipSuccess) return hip_fail(e, "sparse attention kernel");
+  return ok();
+}
+
+dr_status dr_attn(const dr_dims* dims, int32_t seq_len, const void* q, const void* k, const void* v,
+                  float softmax_scale, void* out, hipStream_t stream) {
+  dr_status st = check_dims(dims);
+  if (st != DR_OK) return st;
+  if (seq_len < 1) return fail(DR_ERR_INVALID_ARG, "seq_len must be >= 1");
+  dr::AttnParams p;
+  if ((st = attn_common(dims, seq_len, q, k, v, softmax_scale, out, &p)) != DR_OK) return st;
+  p.row_ptr = nullptr;
+  p.kept_col = nullptr;
+  p.kept_cnt = nullptr;
+  p.nnz = 0;
+  p.Sb = (seq_len + 63) / 64;
+  const hipError_t e = dr::launch_dense_attn(p, dims->head_dim, stream);
+  if (e != hipSuccess) return hip_fail(e, "dense attention kernel");
+  return ok();
+}
+
+const char* dr_status_string(dr_status s) {
+  switch (s) {
+    case DR_OK: return "ok";
+    case DR_ERR_INVALID_ARG: return "invalid argument";
+    case DR_ERR_UNSUPPORTED: return "unsupported configuration";
+    case DR_ERR_CAPACITY: return "insufficient capacity";
+    case DR_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+const char* dr_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

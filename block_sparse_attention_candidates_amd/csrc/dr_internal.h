@@ -1,0 +1,115 @@
+// Internal declarations shared by the C ABI (api.cpp) and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dr {
+
+constexpr int kMaxFrames = 4096;     // N_f limit (per-distance table in LDS)
+constexpr int kMaxBlocks = 16384;    // S_b limit (LDS bitmaps / selection rows)
+constexpr int kWindowCap = 1 << 30;  // saturation of w(t) and sf(t)
+constexpr double kSplitEps = 1e-6;   // epsilon of [DR] Eq. 5
+constexpr double kCountGuard = 1e-9; // ceil(r * n - guard) in the static count
+
+// Next power of two >= n ([DR] §3.1 Eq. 1, L0).
+__host__ __device__ inline int base_span(int n) {
+  int L0 = 1;
+  while (L0 < n) L0 <<= 1;
+  return L0;
+}
+
+// One entry of the per-distance table, [DR] §3.1 Eqs. 1-5.
+// t = 0: dense (w = N_t, sf = 1). t >= 1: B = floor(log2 t) + 1 (bit length),
+// span = L0 / 2^B, L = span * gamma (Eq. 2), w = N_t if t == 1 else
+// max(B_s, floor(L + 1/2)) (Eq. 3), sf = max(1, floor(B_s / (span * lambda + eps)))
+// (Eqs. 4-5). IEEE double, operations in this order, never contracted into FMAs,
+// so host and device produce identical tables.
+__host__ __device__ inline void table_entry(int t, int Nt, int Bs, int L0, double gamma,
+                                            double lambda, int* w, int* sf) {
+#pragma clang fp contract(off)
+  if (t == 0) {
+    *w = Nt;
+    *sf = 1;
+    return;
+  }
+  const int B = 32 - __builtin_clz((unsigned)t);
+  const double span = (double)L0 / (double)(1LL << B);
+  const double decay = span * gamma;
+  int ww;
+  if (t <= 1) {
+    ww = Nt;
+  } else {
+    const double r = floor(decay + 0.5);
+    ww = r >= (double)kWindowCap ? kWindowCap : (int)r;
+    if (ww < Bs) ww = Bs;
+  }
+  const double split = span * lambda;
+  const double qd = floor((double)Bs / (split + kSplitEps));
+  const int s = qd >= (double)kWindowCap ? kWindowCap : (int)qd;
+  *w = ww;
+  *sf = s < 1 ? 1 : s;
+}
+
+struct CandParams {
+  int Nf, Nt, Bs, S, Sb, L0;
+  double gamma, lambda, theta_c, theta_m;
+};
+
+struct PoolParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  float* qbar;     // [B, Hp, S_b, D]
+  float* kbar;
+  int B, H, Hp;    // Hp: heads pooled (H, or the fused-head count)
+  int S, Sb, Bs, D;
+};
+
+struct ScoreParams {
+  const float* qbar;
+  const float* kbar;
+  const int32_t* row_ptr;
+  const int32_t* cols;
+  float* scores;   // [B * Hm * nnz]
+  long long nnz;
+  int Sb, Hp, Hm, g;  // g heads summed per score (1: per-head)
+  int D;
+  float scale;     // 1 / (sqrt(D) * g)
+};
+
+struct SelectParams {
+  const float* scores;
+  const int32_t* row_ptr;
+  const int32_t* cols;
+  int32_t* kept_col;
+  int32_t* kept_cnt;
+  long long nnz;
+  int Sb, H, Hm;
+  int mode;
+  double ratio, tau;
+  int max_row;     // LDS capacity in scores (>= longest row)
+};
+
+struct AttnParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* o;
+  const int32_t* row_ptr;
+  const int32_t* kept_col;
+  const int32_t* kept_cnt;
+  long long nnz;
+  int S, Sb, BH;
+  int n_tiles;        // query-row tiles per (b, h)
+  float scale_log2;   // softmax_scale * log2(e)
+};
+
+hipError_t launch_candidates(const CandParams& p, int32_t* row_ptr, int32_t* cols, long long cap,
+                             hipStream_t stream);
+hipError_t launch_pool(const PoolParams& p, hipStream_t stream);
+hipError_t launch_scores(const ScoreParams& p, int B, hipStream_t stream);
+hipError_t launch_select(const SelectParams& p, int B, hipStream_t stream);
+hipError_t launch_sparse_attn(const AttnParams& p, int D, int Bs, hipStream_t stream);
+hipError_t launch_dense_attn(const AttnParams& p, int D, hipStream_t stream);
+
+}  // namespace dr

@@ -1,0 +1,175 @@
+/*
+ * dynrad.h -- C ABI of the DynamicRad block-sparse attention hot path for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Method: "DynamicRad: Content-Adaptive Sparse Attention for Long Video
+ * Diffusion" (arXiv 2604.20470), cited below as [DR].
+ *
+ * The path, one video-DiT self-attention layer at inference:
+ *   1. dr_build_candidates  radial block-candidate set ([DR] §3.1, Eqs. 1-7 and
+ *                           "Density control within blocks"), content-free.
+ *   2. dr_score_select      mean-pooled block scores and dual-mode selection
+ *                           ([DR] §3.2: static-ratio / dynamic-threshold).
+ *   3. dr_sparse_attn       flash-style forward attention over the kept KV
+ *                           blocks only ([DR] §3.3, Eq. 13 with eps -> 0).
+ *   dr_attn                 dense forward attention, the speedup denominator
+ *                           ([DR] App. A, Eq. 16).
+ *
+ * Conventions shared by every entry point:
+ *  - Tensors are [B, H, S, D] row-major and contiguous, bfloat16 (raw 16-bit
+ *    patterns), in device memory. S = N_f * N_t tokens, frame-major, raster
+ *    order within a frame. Blocks are B_s consecutive tokens; block a holds
+ *    tokens [a*B_s, min((a+1)*B_s, S)). S_b = ceil(S / B_s). Tokens >= S are
+ *    padding: never attended, never pooled, never written.
+ *  - All device buffers are allocated by the caller. The library allocates
+ *    nothing and keeps no state across calls except a thread-local error
+ *    message.
+ *  - Calls are asynchronous on the given HIP stream (NULL = default stream);
+ *    inputs must stay valid until the stream passes the call. Only
+ *    dr_build_candidates synchronises (to report the candidate count).
+ *  - Arguments are validated before any launch; an invalid call launches
+ *    nothing. No entry point aborts or throws. dr_last_error() describes the
+ *    most recent failure on the calling thread.
+ *  - Limits: head_dim in {64, 128}; block_size in {32, 64}; S_b <= 16384;
+ *    N_f <= 4096; batch * heads * nnz < 2^31.
+ */
+#ifndef DYNRAD_H
+#define DYNRAD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum dr_status {
+  DR_OK = 0,
+  DR_ERR_INVALID_ARG = 1, /* null pointer, non-positive size, value out of range */
+  DR_ERR_UNSUPPORTED = 2, /* valid but not built: head_dim / block_size / size limits */
+  DR_ERR_CAPACITY = 3,    /* output capacity below the required size */
+  DR_ERR_HIP = 4          /* a HIP launch or runtime call failed */
+} dr_status;
+
+/* Radial candidate configuration ([DR] §3.1; parameter vector x of §3.4 / C.4). */
+typedef struct dr_radial_cfg {
+  int32_t num_frames;       /* N_f >= 1                                              */
+  int32_t tokens_per_frame; /* N_t >= 1 (spatial tokens of one latent frame)         */
+  int32_t block_size;       /* B_s: 32 or 64                                         */
+  int32_t reserved;         /* must be 0                                             */
+  double gamma;             /* decay factor of Eq. 2, > 0                            */
+  double lambda;            /* long-range factor of Eq. 4, >= 0                      */
+  double theta_c;           /* column density threshold, in [0, 1]                   */
+  double theta_m;           /* mask (block activation) threshold, in [0, 1]          */
+} dr_radial_cfg;
+
+typedef struct dr_dims {
+  int32_t batch;    /* B >= 1                */
+  int32_t heads;    /* H >= 1                */
+  int32_t head_dim; /* D: 64 or 128          */
+  int32_t reserved; /* must be 0             */
+} dr_dims;
+
+typedef enum dr_mode {
+  DR_STATIC_RATIO = 0,     /* [DR] §3.2 "static_ratio"     */
+  DR_DYNAMIC_THRESHOLD = 1 /* [DR] §3.2 "dynamic_threshold" */
+} dr_mode;
+
+typedef struct dr_select_cfg {
+  int32_t mode;        /* dr_mode                                                        */
+  int32_t score_heads; /* 0: one mask per head; g > 0: scores averaged over heads 0..g-1
+                          and one mask shared by every head ([DR] App. B, Eq. 19)         */
+  double ratio;        /* static: keep max(1, ceil(ratio * n - 1e-9)) of n, ratio in (0,1] */
+  double tau;          /* dynamic: cumulative softmax mass to reach, tau in (0, 1]       */
+} dr_select_cfg;
+
+/* Number of blocks S_b = ceil(N_f * N_t / B_s) for a valid configuration, else
+ * a negative dr_status. Host only. */
+int64_t dr_num_blocks(const dr_radial_cfg* cfg);
+
+/* Per-distance table of [DR] §3.1 Eqs. 1-5, the table the candidate kernel uses:
+ * w[t] (window width, Eq. 3) and sf[t] (split stride, Eq. 5) for t in [0, N_f).
+ * t = 0: w = N_t, sf = 1 (dense). t >= 1: L0 = next power of two >= N_t,
+ * B(t) = floor(log2 t) + 1, L = L0 / 2^B(t) * gamma, w = N_t if t == 1 else
+ * max(B_s, floor(L + 1/2)); sf = max(1, floor(B_s / (L0 / 2^B(t) * lambda + 1e-6))).
+ * Evaluated in IEEE double, no contraction. w and sf are host arrays of
+ * num_frames int32 (windows above 2^30 saturate there; any w >= N_t - 1 admits
+ * every spatial pair). Host only. */
+dr_status dr_distance_table(const dr_radial_cfg* cfg, int32_t* w, int32_t* sf);
+
+/* Candidate block set ([DR] §3.1 Eqs. 6-7, "Density control within blocks").
+ * Token pair (q, k) with frame distance t and local indices u_q, u_k is a
+ * candidate iff t mod sf(t) == 0 and |u_q - u_k| <= w(t). For block pair
+ * (a, b): a key token of b is active iff (query tokens of a paired with it) /
+ * (query tokens of a) > theta_c; (a, b) is a candidate iff (active key tokens)
+ * / (key tokens of b) > theta_m. Padding tokens count nowhere.
+ * Output, device memory, CSR over query blocks:
+ *   row_ptr [S_b + 1] int32: row a's candidates are cols[row_ptr[a] .. row_ptr[a+1]);
+ *   cols    [cap]     int32: key-block indices, strictly ascending within a row.
+ * nnz (host pointer): if non-NULL, the call synchronises the stream and stores
+ * the candidate count; if it exceeds cap, returns DR_ERR_CAPACITY (cols holds
+ * the first cap entries; call again with cap >= *nnz). If NULL, the call is
+ * asynchronous, writes past cap are dropped and the count is row_ptr[S_b]. */
+dr_status dr_build_candidates(const dr_radial_cfg* cfg, int32_t* row_ptr, int32_t* cols,
+                              int64_t cap, int64_t* nnz, hipStream_t stream);
+
+/* Device workspace (bytes) dr_score_select needs: pooled Q and K means (float32,
+ * [B, Hs, S_b, D] each, Hs = H or score_heads) plus the score buffer (float32,
+ * [B * Hm * nnz], Hm = H or 1). Host only. */
+dr_status dr_score_select_workspace(const dr_dims* dims, const dr_radial_cfg* cfg,
+                                    const dr_select_cfg* sel, int64_t nnz, size_t* bytes);
+
+/* Block scoring and dual-mode selection ([DR] §3.2, block form).
+ *  1. Block means of Q and K over valid tokens (float32).
+ *  2. Scores on the candidate entries: s(a, c) = Qbar_a . Kbar_c / sqrt(D)
+ *     (block form of [DR] Eq. 9); with score_heads = g > 0 the mean over heads
+ *     0..g-1 ([DR] Eq. 19), and the mask is shared by every head.
+ *  3. Per query block with n candidates, order by (score desc, key index asc):
+ *     static  keeps the first k = max(1, ceil(ratio * n - 1e-9));
+ *     dynamic keeps the shortest prefix whose softmax mass (softmax of the raw
+ *     scores over the n candidates) reaches tau, at least one ([DR] §3.2
+ *     safeguard (ii)); tau >= 1 keeps all.
+ * Inputs: q, k bf16 [B, H, S, D] (device); row_ptr, cols from dr_build_candidates.
+ * Outputs (device):
+ *   kept_col [B * H * nnz] int32: the kept list of (b, h, a) starts at
+ *       (b * H + h) * nnz + row_ptr[a], ascending key-block indices;
+ *   kept_cnt [B * H * S_b] int32: its length, at (b * H + h) * S_b + a.
+ *   scores_out: NULL, or float32 [B * Hm * nnz] receiving the scores in CSR order.
+ * ws / ws_bytes: device workspace of at least dr_score_select_workspace bytes. */
+dr_status dr_score_select(const dr_dims* dims, const dr_radial_cfg* cfg, const dr_select_cfg* sel,
+                          const void* q, const void* k, const int32_t* row_ptr, const int32_t* cols,
+                          int64_t nnz, int32_t* kept_col, int32_t* kept_cnt, float* scores_out,
+                          void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Block-sparse forward attention ([DR] §3.3 Eqs. 12-13, eps -> 0): for each
+ * (b, h) and query block a, O[rows of a] = softmax(Q K^T * softmax_scale) V over
+ * the valid key tokens of the blocks in a's kept list only; online softmax in
+ * float32, bf16 products into float32 accumulators, bf16 output.
+ * Kept lists use the layout of dr_score_select (any source: a host-built mask
+ * uploaded in that layout works). Entries outside [0, S_b) are ignored and
+ * duplicates count once; a row with no kept block outputs zeros.
+ * q, k, v, out: bf16 [B, H, S, D] device; out must not alias the inputs. */
+dr_status dr_sparse_attn(const dr_dims* dims, const dr_radial_cfg* cfg, const void* q,
+                         const void* k, const void* v, const int32_t* row_ptr, int64_t nnz,
+                         const int32_t* kept_col, const int32_t* kept_cnt, float softmax_scale,
+                         void* out, hipStream_t stream);
+
+/* Dense forward attention over all seq_len keys (bidirectional), the baseline
+ * of [DR] App. A Eq. 16 / Table 5 "Dense". Same numerics and layouts as
+ * dr_sparse_attn; seq_len >= 1. */
+dr_status dr_attn(const dr_dims* dims, int32_t seq_len, const void* q, const void* k,
+                  const void* v, float softmax_scale, void* out, hipStream_t stream);
+
+/* Static description of a status code. */
+const char* dr_status_string(dr_status status);
+
+/* Detail of the last failure on the calling thread ("" if none). */
+const char* dr_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DYNRAD_H */

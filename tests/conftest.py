@@ -11,3 +11,13 @@ if ROOT not in sys.path:
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
     config.addinivalue_line("markers", "slow: CPU test that takes more than a few seconds")
+
+
+@pytest.fixture(scope="session")
+def dynrad_lib():
+    """The built C-ABI library (built once if missing)."""
+    from block_sparse_attention_candidates_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        from block_sparse_attention_candidates_amd import build
+        build.build()
+    return _lib.lib()

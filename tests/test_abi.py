@@ -1,0 +1,137 @@
+"""CPU checks of the C-ABI library (include/dynrad.h): it loads, exports every
+declared entry point, its host per-distance table equals the oracle's, and
+invalid calls are rejected by argument validation before any HIP call (no GPU
+is touched by these tests)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle import dynrad_oracle as O
+import workloads
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dynrad.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dr_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(dynrad_lib):
+    names = declared_functions()
+    assert {"dr_build_candidates", "dr_score_select", "dr_sparse_attn", "dr_attn"} <= set(names)
+    for n in names:
+        assert hasattr(dynrad_lib, n), n
+
+
+def _cfg(Nf, Nt, Bs, gamma, lam, tc=0.0, tm=0.0):
+    import block_sparse_attention_candidates_amd as dr
+    return dr.radial_cfg(Nf, Nt, Bs, gamma, lam, tc, tm)
+
+
+def test_host_table_equals_oracle(dynrad_lib):
+    import block_sparse_attention_candidates_amd as dr
+    rng = np.random.default_rng(0)
+    cases = [(21, 1560, 32, 0.7, 2.0), (21, 3600, 32, 1.0, 4.0), (33, 3600, 64, 1.0, 4.0), (4, 64, 32, 1.0, 2.0),
+             (20, 256, 32, 1.0, 0.25), (3, 128, 32, 1.265625, 1.0), (3, 256, 32, 1.0, 0.1)]
+    for _ in range(300):
+        cases.append((int(rng.integers(1, 100)), int(rng.integers(1, 5000)), int(rng.choice([32, 64])),
+                      float(rng.uniform(0.05, 4.0)), float(rng.choice([0.0, rng.uniform(0.0, 2.0)]))))
+    # round-number parameters hit exact ties of Eqs. 3 and 5
+    for g in (0.5, 0.75, 1.0, 1.25, 1.5, 2.0, 3.0):
+        for lam in (0.0625, 0.125, 0.25, 0.5, 1.0):
+            cases.append((64, 1000, 32, g, lam))
+    for Nf, Nt, Bs, g, lam in cases:
+        if Nf * Nt > 16384 * Bs:
+            continue
+        w, sf = dr.distance_table(_cfg(Nf, Nt, Bs, g, lam))
+        wo, sfo = O.distance_table(Nf, Nt, Bs, g, lam)
+        np.testing.assert_array_equal(np.minimum(w, 1 << 30), np.minimum(wo, 1 << 30), err_msg=str((Nf, Nt, Bs, g, lam)))
+        np.testing.assert_array_equal(sf, np.minimum(sfo, 1 << 30), err_msg=str((Nf, Nt, Bs, g, lam)))
+
+
+def test_num_blocks(dynrad_lib):
+    import block_sparse_attention_candidates_amd as dr
+    for name, w in workloads.WORKLOADS.items():
+        assert dr.num_blocks(_cfg(w.num_frames, w.tokens_per_frame, w.block_size, w.gamma, w.lam)) == w.num_blocks
+
+
+FAKE = ctypes.c_void_p(4096)     # never dereferenced: validation fails first
+
+
+def test_radial_validation(dynrad_lib):
+    from block_sparse_attention_candidates_amd import _lib as L
+    bad = [(_cfg(4, 64, 128, 1.0, 2.0), L.DR_ERR_UNSUPPORTED),      # B_s = 128 not built
+           (_cfg(4, 64, 0, 1.0, 2.0), L.DR_ERR_INVALID_ARG),
+           (_cfg(0, 64, 32, 1.0, 2.0), L.DR_ERR_INVALID_ARG),
+           (_cfg(4, 64, 32, 0.0, 2.0), L.DR_ERR_INVALID_ARG),         # gamma must be > 0
+           (_cfg(4, 64, 32, 1.0, -1.0), L.DR_ERR_INVALID_ARG),
+           (_cfg(4, 64, 32, 1.0, 2.0, 1.5, 0.0), L.DR_ERR_INVALID_ARG),
+           (_cfg(4, 64, 32, 1.0, 2.0, 0.0, -0.1), L.DR_ERR_INVALID_ARG),
+           (_cfg(4, 64, 32, float("nan"), 2.0), L.DR_ERR_INVALID_ARG),
+           (_cfg(5000, 64, 32, 1.0, 2.0), L.DR_ERR_UNSUPPORTED),      # N_f above 4096
+           (_cfg(100, 10000, 32, 1.0, 2.0), L.DR_ERR_UNSUPPORTED)]    # S_b above 16384
+    for cfg, want in bad:
+        assert dynrad_lib.dr_num_blocks(ctypes.byref(cfg)) == -want
+        nnz = ctypes.c_int64(-1)
+        assert dynrad_lib.dr_build_candidates(ctypes.byref(cfg), FAKE, FAKE, 10, ctypes.byref(nnz), None) == want
+        assert dynrad_lib.dr_last_error().decode() != ""
+    cfg = _cfg(4, 64, 32, 1.0, 2.0)
+    cfg.reserved = 1
+    assert dynrad_lib.dr_num_blocks(ctypes.byref(cfg)) == -L.DR_ERR_INVALID_ARG
+    good = _cfg(4, 64, 32, 1.0, 2.0)
+    assert dynrad_lib.dr_build_candidates(ctypes.byref(good), None, FAKE, 10, None, None) == L.DR_ERR_INVALID_ARG
+    assert dynrad_lib.dr_build_candidates(ctypes.byref(good), FAKE, FAKE, 0, None, None) == L.DR_ERR_INVALID_ARG
+    assert dynrad_lib.dr_build_candidates(None, FAKE, FAKE, 10, None, None) == L.DR_ERR_INVALID_ARG
+
+
+def test_select_and_attention_validation(dynrad_lib):
+    from block_sparse_attention_candidates_amd import _lib as L
+    cfg = _cfg(4, 64, 32, 1.0, 2.0)            # S = 256, S_b = 8
+    dims = L.Dims(1, 2, 64, 0)
+    sel = L.SelectCfg(L.DR_STATIC_RATIO, 0, 0.5, 0.8)
+    size = ctypes.c_size_t(0)
+    assert dynrad_lib.dr_score_select_workspace(ctypes.byref(dims), ctypes.byref(cfg), ctypes.byref(sel), 64,
+                                                ctypes.byref(size)) == L.DR_OK
+    # pooled Q and K: 2 * (1*2*8*64*4 = 4096 B) + scores 1*2*64*4 = 512 B (each rounded up to 256 B)
+    assert size.value == 4096 + 4096 + 512
+    fused = L.SelectCfg(L.DR_DYNAMIC_THRESHOLD, 1, 0.5, 0.8)
+    assert dynrad_lib.dr_score_select_workspace(ctypes.byref(dims), ctypes.byref(cfg), ctypes.byref(fused), 64,
+                                                ctypes.byref(size)) == L.DR_OK
+    assert size.value == 2048 + 2048 + 256
+
+    def ss(d=dims, s=sel, nnz=64, ws_bytes=1 << 20, q=FAKE):
+        return dynrad_lib.dr_score_select(ctypes.byref(d), ctypes.byref(cfg), ctypes.byref(s), q, FAKE, FAKE, FAKE,
+                                          nnz, FAKE, FAKE, None, FAKE, ws_bytes, None)
+    assert ss(s=L.SelectCfg(L.DR_STATIC_RATIO, 0, 0.0, 0.8)) == L.DR_ERR_INVALID_ARG     # ratio 0
+    assert ss(s=L.SelectCfg(L.DR_STATIC_RATIO, 0, 1.5, 0.8)) == L.DR_ERR_INVALID_ARG     # ratio > 1
+    assert ss(s=L.SelectCfg(L.DR_DYNAMIC_THRESHOLD, 0, 0.5, 0.0)) == L.DR_ERR_INVALID_ARG  # tau 0
+    assert ss(s=L.SelectCfg(L.DR_DYNAMIC_THRESHOLD, 0, 0.5, 1.5)) == L.DR_ERR_INVALID_ARG
+    assert ss(s=L.SelectCfg(7, 0, 0.5, 0.8)) == L.DR_ERR_INVALID_ARG
+    assert ss(s=L.SelectCfg(L.DR_STATIC_RATIO, 3, 0.5, 0.8)) == L.DR_ERR_INVALID_ARG     # score_heads > H
+    assert ss(d=L.Dims(1, 2, 96, 0)) == L.DR_ERR_UNSUPPORTED
+    assert ss(d=L.Dims(0, 2, 64, 0)) == L.DR_ERR_INVALID_ARG
+    assert ss(nnz=0) == L.DR_ERR_INVALID_ARG
+    assert ss(nnz=65) == L.DR_ERR_INVALID_ARG                                           # > S_b^2
+    assert ss(q=None) == L.DR_ERR_INVALID_ARG
+    assert ss(ws_bytes=100) == L.DR_ERR_CAPACITY
+
+    def sa(d=dims, nnz=64, out=ctypes.c_void_p(8192), scale=0.125):
+        return dynrad_lib.dr_sparse_attn(ctypes.byref(d), ctypes.byref(cfg), FAKE, ctypes.c_void_p(4096 + 64),
+                                         ctypes.c_void_p(4096 + 128), FAKE, nnz, FAKE, FAKE, scale, out, None)
+    assert sa(out=FAKE) == L.DR_ERR_INVALID_ARG            # aliases q
+    assert sa(out=None) == L.DR_ERR_INVALID_ARG
+    assert sa(d=L.Dims(1, 2, 32, 0)) == L.DR_ERR_UNSUPPORTED
+    assert sa(nnz=0) == L.DR_ERR_INVALID_ARG
+    assert sa(scale=float("inf")) == L.DR_ERR_INVALID_ARG
+    assert dynrad_lib.dr_attn(ctypes.byref(dims), 0, FAKE, FAKE, FAKE, ctypes.c_float(0.1), ctypes.c_void_p(8192),
+                              None) == L.DR_ERR_INVALID_ARG
+    assert dynrad_lib.dr_attn(ctypes.byref(L.Dims(1, 1, 80, 0)), 10, FAKE, FAKE, FAKE, ctypes.c_float(0.1),
+                              ctypes.c_void_p(8192), None) == L.DR_ERR_UNSUPPORTED
+    for s in range(5):
+        assert dynrad_lib.dr_status_string(s).decode()
