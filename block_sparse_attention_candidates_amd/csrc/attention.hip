@@ -3,82 +3,308 @@
 // baseline). [DR] = "DynamicRad: Content-Adaptive Sparse Attention for Long
 // Video Diffusion", arXiv 2604.20470.
 //
-// Work decomposition. A workgroup of 8 wavefronts owns 256 consecutive query
-// rows of one (b, h); each wavefront owns 32 rows (one 32x32 MFMA tile). In
-// sparse mode those rows are 256 / B_s query blocks; the workgroup ORs their
-// kept lists into LDS bitmaps and compacts the union of kept KV blocks, then
-// streams that union through a double-buffered LDS stage: every KV block is
-// fetched from HBM/L2 once per workgroup and used by each wavefront whose
-// query block kept it (a wave-uniform bit test). Dense mode streams every
-// 64-key block.
+// Workgroup = 8 compute wavefronts + 3 loader wavefronts, 256 query rows of
+// one (b, h). Each compute wavefront owns 32 query rows (one 32x32 MFMA tile);
+// in sparse mode those rows are 256 / B_s query blocks.
 //
-// Per wavefront and 32-key unit (CDNA4 v_mfma_f32_32x32x16_bf16):
-//   S^T = K Q^T  : A = K rows from LDS (16 B per lane), B = the wavefront's Q
-//                  fragment held in registers; lane l ends with the 16 scores of
-//                  query row l%32 for keys 8*(i/4) + 4*(l/32) + i%4.
-//   online softmax in float32 on those registers (exp2 with the scale folded
-//                  into log2(e)); the two lane halves of a row exchange their
-//                  maxima once (shuffle by 32).
-//   O^T += V^T P^T: B = the lane's own probabilities packed to bf16; A = V^T
-//                  read from LDS, where V was stored transposed with its keys
-//                  permuted to match the order in which each lane holds P.
-// KV loads are issued P steps ahead into registers (a ring unrolled at compile
-// time), written to LDS one step ahead, one barrier per step.
+// Setup (the only workgroup barriers): the kept lists of the workgroup's
+// query blocks are ORed into per-block LDS bitmaps; their union is the
+// sequence of KV blocks the workgroup streams, cut into 32-key units.
+//
+// Streaming without barriers: the loaders copy units from HBM/L2 straight into
+// an 8-slot LDS ring with direct-to-LDS loads (16 B per lane, no registers),
+// each keeping 2 units in flight, and publish a slot once its loads have
+// landed. Each compute wavefront walks only the units of the KV blocks its own
+// query block kept, announces its position, waits for the slot, computes. A
+// loader refills a slot only after every compute wavefront has moved past the
+// unit it held. Compute wavefronts therefore run out of phase with each other,
+// and the two on a SIMD overlap one's MFMA with the other's softmax. Waits are
+// bounded (a wave gives up after ~2^26 polls; the protocol never needs that).
+//
+// Per compute wavefront and 32-key unit (v_mfma_f32_32x32x16_bf16):
+//   S^T = K Q^T : A = K rows read from LDS (16 B per lane), B = the wave's Q
+//                 fragment in registers; lane l holds the 16 scores of query
+//                 row l%32 for keys 8*(i/4) + 4*(l/32) + i%4.
+//   softmax     : float32, exp2 with the scale folded into one FMA; the row max
+//                 is shared by the two lane halves with one shuffle; the
+//                 output is rescaled only when a row max grows by more than
+//                 2^8 (probabilities stay <= 256, exact after the final 1/l);
+//                 padding keys get probability 0.
+//   O^T += V^T P^T: B = the lane's own probabilities as bf16; A = V^T obtained
+//                 from row-major V in LDS with the gfx950 transposing LDS read
+//                 (ds_read_b64_tr_b16: a 16-lane group turns four 4-element
+//                 row chunks into four 4-key columns), keys taken in the order
+//                 in which each lane holds P.
+// LDS rows are XOR-swizzled in 16-byte chunks (chosen per row so that the
+// MFMA operand reads of a wave hit distinct banks); the loaders pick, per lane,
+// the global chunk that belongs at each physical position.
 #include "dr_internal.h"
 
 namespace dr {
 namespace {
 
 typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef float floatx8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef int intx4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float floatx8 __attribute__((ext_vector_type(8)));
-typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x4_v __attribute__((__vector_size__(4 * sizeof(__bf16))));
+#define DR_LDS __attribute__((address_space(3)))
 
-constexpr int kThreads = 512;
-constexpr int kRowsPerWG = 256;
+constexpr int kConsumers = 8;
+constexpr int kLoaders = 3;
+constexpr int kThreads = (kConsumers + kLoaders) * 64;
+constexpr int kRows = kConsumers * 32;       // query rows per workgroup
+constexpr int kSlots = 8;                    // ring depth, in 32-key units
+constexpr int kInflight = 2;                 // units in flight per loader
+static_assert(kSlots >= kInflight * kLoaders + 1, "ring too shallow for the loaders' pipelines");
+static_assert(kConsumers == 8, "the loaders read the 8 progress entries as two int4");
+constexpr int kUnit = 32;
+constexpr float kRescaleLog2 = 8.0f;         // rescale only past 2^8 growth
+constexpr int kSpinLimit = 1 << 26;
+constexpr int kDone = 0x3fffffff;
 
-// slot of key j (0..31) within its 32-key unit in the transposed V stage:
-// slot 16*jj + 8*h + e holds key 16*jj + 8*(e/4) + 4*h + e%4.
-__device__ __host__ constexpr int v_slot(int j) {
-  return 16 * (j / 16) + 8 * ((j % 8) / 4) + 4 * ((j % 16) / 8) + (j % 4);
+template <int D>
+struct Geo {
+  static constexpr int RB = 2 * D;               // bytes per key row
+  static constexpr int TBYTES = kUnit * RB;      // K (or V) bytes of a unit
+  static constexpr int SLOT = 2 * TBYTES;        // K then V
+  static constexpr int NLOAD = TBYTES / 1024;    // 1 KB direct loads per tensor
+  static constexpr int RING = kSlots * SLOT;
+};
+
+// 16-byte chunk swizzles (physical chunk = logical chunk ^ swz(row)).
+// K: the 16 lanes of a quarter-wave read 16 consecutive rows at one logical
+// chunk; V: a half-wave's transposing reads cover 4 rows x 64 bytes.
+template <int D>
+__device__ inline int swz_k(int key) { return D == 128 ? (key & 15) : ((key >> 1) & 7); }
+template <int D>
+__device__ inline int swz_v(int key) { return D == 128 ? 4 * (key & 3) : 4 * ((key >> 1) & 1); }
+
+__device__ inline int ld_relaxed(const int* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+__device__ inline void st_relaxed(int* p, int v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+__device__ inline void compiler_fence() { asm volatile("" ::: "memory"); }
+
+// Direct global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4):
+// lane l's bytes land at lds_wave_base + 16*l. Written as inline asm so that
+// the compiler does not treat the ring as a pending LDS write of this wave
+// (which makes it drain every load before each flag access); the loader
+// waits on these loads itself with explicit s_waitcnt vmcnt. The asm has no
+// output register and the address registers are read at issue.
+__device__ inline void dma16(const void* gptr, unsigned char* lds_wave_base) {
+  const unsigned m0 = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)lds_wave_base);
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0), "v"(gptr) : "memory", "m0");
 }
 
-template <int D, int BS>
-struct Stage {
-  static constexpr int KSTR = D + 8;                 // bf16 per K row in LDS
-  static constexpr int VSTR = BS + 8;                // bf16 per V^T row in LDS
-  static constexpr int K_ELEMS = BS * KSTR;
-  static constexpr int V_ELEMS = D * VSTR;
-  static constexpr int BUF_ELEMS = K_ELEMS + V_ELEMS;
-  static constexpr int CHUNKS = BS * D / 8;          // 16-byte chunks per tensor
-  static constexpr int CPT = CHUNKS >= kThreads ? CHUNKS / kThreads : 1;
-  static constexpr int PREFETCH = CPT == 1 ? 4 : 2;  // steps in flight
-  static constexpr size_t BYTES = 2 * (size_t)BUF_ELEMS * 2;
+// The same copy with an SGPR base and a per-lane 32-bit byte offset (saddr form).
+__device__ inline void dma16_s(const void* sbase, unsigned voff, unsigned char* lds_wave_base) {
+  const unsigned m0 = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)lds_wave_base);
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(m0), "v"(voff), "s"(sbase) : "memory", "m0");
+}
+
+// max / sum of a value over the two 32-lane halves: v_permlane32_swap(v, v)
+// yields the low half in both halves of one result and the high half in the other
+__device__ inline float max_halves(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float sum_halves(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ inline int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
+template <int N>
+__device__ inline void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+struct Shared {
+  int ready[kSlots];           // unit index held by each slot (-1: none)
+  int prog[kConsumers];        // next unit each compute wave may read
+  int n_units;
+  int pad[15 - kSlots - kConsumers > 0 ? 15 - kSlots - kConsumers : 1];
 };
 
 template <int D, int BS, bool SPARSE>
 __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
-  using St = Stage<D, BS>;
+  using G = Geo<D>;
+  constexpr int UPB = BS / kUnit;                 // units per KV block
+  constexpr int QB = kRows / BS;                  // query blocks per workgroup
+  constexpr int WPQ = BS / 32;                    // compute waves per query block
   extern __shared__ __align__(16) unsigned char smem[];
-  uint16_t* stage = reinterpret_cast<uint16_t*>(smem);
-  constexpr int NUNIT = BS / 32;
-  constexpr int QB_PER_WG = kRowsPerWG / BS;           // query blocks per workgroup
-  constexpr int WAVES_PER_QB = BS / 32;
+  unsigned char* ring = smem;
+  Shared* sh = reinterpret_cast<Shared*>(smem + G::RING);
+  unsigned int* bits = reinterpret_cast<unsigned int*>(smem + G::RING + sizeof(Shared));
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int half = lane >> 5, l32 = lane & 31;
   const int bh = blockIdx.y;
-  const int tile = blockIdx.x;
-  const int row0 = tile * kRowsPerWG;
-  const int wrow0 = row0 + wave * 32;
+  const int row0 = blockIdx.x * kRows;
   const size_t base = (size_t)bh * p.S * D;
-  const uint16_t* __restrict__ Kg = p.k + base;
-  const uint16_t* __restrict__ Vg = p.v + base;
+  const int nword = (p.Sb + 31) >> 5;
+  unsigned int* uword = bits + QB * nword;        // union of the query blocks' bitmaps
+  int* wpre = reinterpret_cast<int*>(uword + nword);  // exclusive prefix popcounts
 
-  // ---- Q fragment (B operand of S^T = K Q^T) ----
+  // ---------------- setup ----------------
+  if (tid < kSlots) sh->ready[tid] = -1;
+  if (tid < kConsumers) sh->prog[tid] = 0;
+  if constexpr (SPARSE) {
+    for (int i = tid; i < QB * nword; i += kThreads) bits[i] = 0;
+    __syncthreads();
+    if (wave < QB) {
+      const int qb = row0 / BS + wave;
+      if (qb < p.Sb) {
+        const int32_t* kl = p.kept_col + (long long)bh * p.nnz + p.row_ptr[qb];
+        const int cnt = p.kept_cnt[(long long)bh * p.Sb + qb];
+        for (int i = lane; i < cnt; i += 64) {
+          const int c = kl[i];
+          if (c >= 0 && c < p.Sb) atomicOr(&bits[wave * nword + (c >> 5)], 1u << (c & 31));
+        }
+      }
+    }
+    __syncthreads();
+    for (int wi = tid; wi < nword; wi += kThreads) {
+      unsigned int u = 0;
+      for (int s = 0; s < QB; ++s) u |= bits[s * nword + wi];
+      uword[wi] = u;
+    }
+    __syncthreads();
+    if (wave == 0) {
+      int run = 0;
+      for (int w0 = 0; w0 < nword; w0 += 64) {
+        const int wi = w0 + lane;
+        const int c = wi < nword ? __popc(uword[wi]) : 0;
+        int incl = c;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+          const int o = __shfl_up(incl, off);
+          if (lane >= off) incl += o;
+        }
+        if (wi < nword) wpre[wi] = run + incl - c;
+        run += __shfl(incl, 63);
+      }
+      if (lane == 0) sh->n_units = run * UPB;
+    }
+  } else {
+    if (tid == 0) sh->n_units = (p.S + kUnit - 1) / kUnit;
+  }
+  __syncthreads();
+  const int n_units = sh->n_units;
+
+  if (wave >= kConsumers) {
+    // ---------------- loader wavefronts ----------------
+    const int L = wave - kConsumers;
+    const uint16_t* __restrict__ Kg = p.k + base;
+    const uint16_t* __restrict__ Vg = p.v + base;
+    // cursor over the union (sparse): block of union step j
+    int cur_wi = 0, cur_step = 0;
+    unsigned int cur_bits = SPARSE ? uword[0] : 0u;
+    auto block_of_step = [&](int j) -> int {
+      if constexpr (!SPARSE) {
+        return j;
+      } else {
+        while (true) {
+          const int n = __popc(cur_bits);
+          if (j < cur_step + n) {
+            unsigned int m = cur_bits;
+            for (int t = cur_step; t < j; ++t) m &= m - 1;
+            return cur_wi * 32 + __ffs(m) - 1;
+          }
+          cur_step += n;
+          ++cur_wi;
+          cur_bits = uword[cur_wi];
+        }
+      }
+    };
+    auto publish = [&](int u) {
+      compiler_fence();
+      st_relaxed(&sh->ready[u % kSlots], u);
+    };
+    // Byte offset of this lane's 16-byte chunk within a unit's K or V tile for
+    // DMA instruction n: n * 1024 + dma_k[n % KM] (K) or + dma_v (V). The
+    // swizzles depend on the row only through row mod (4 * KM) (K) or row mod 4
+    // (V), so a few per-lane constants cover every instruction.
+    constexpr int KM = D == 128 ? 4 : 2;
+    auto lane_chunk = [&](int n, bool is_k) -> int {
+      const int off = n * 1024 + 16 * lane;
+      const int row = off / G::RB;
+      const int pc = (off % G::RB) >> 4;
+      const int lc = pc ^ (is_k ? swz_k<D>(row) : swz_v<D>(row));
+      return row * G::RB + lc * 16 - n * 1024;
+    };
+    int dma_k[KM];
+#pragma unroll
+    for (int m = 0; m < KM; ++m) dma_k[m] = lane_chunk(m, true);
+    const int dma_v = lane_chunk(0, false);
+    auto issue = [&](int u) {
+      const int j = u / UPB, q = u - j * UPB;
+      const int key0 = uniform(block_of_step(j) * BS + q * kUnit);
+      unsigned char* slot = ring + (u % kSlots) * G::SLOT;
+      if (key0 + kUnit <= p.S) {
+        const unsigned char* kb = reinterpret_cast<const unsigned char*>(Kg + (size_t)key0 * D);
+        const unsigned char* vb = reinterpret_cast<const unsigned char*>(Vg + (size_t)key0 * D);
+#pragma unroll
+        for (int n = 0; n < G::NLOAD; ++n) dma16_s(kb + n * 1024, (unsigned)dma_k[n % KM], slot + n * 1024);
+#pragma unroll
+        for (int n = 0; n < G::NLOAD; ++n) dma16_s(vb + n * 1024, (unsigned)dma_v, slot + G::TBYTES + n * 1024);
+        return;
+      }
+      // the tile running past the sequence end: rows clamped to the last token
+#pragma unroll 1
+      for (int t = 0; t < 2; ++t) {
+        const uint16_t* src = t == 0 ? Kg : Vg;
+#pragma unroll 1
+        for (int n = 0; n < G::NLOAD; ++n) {
+          const int off = n * 1024 + 16 * lane;
+          const int row = off / G::RB;
+          const int pc = (off % G::RB) >> 4;
+          const int lc = pc ^ (t == 0 ? swz_k<D>(row) : swz_v<D>(row));
+          const int key = min(key0 + row, p.S - 1);
+          const uint16_t* g = src + (size_t)key * D + lc * 8;
+          dma16(g, slot + t * G::TBYTES + n * 1024);
+        }
+      }
+    };
+    int k = 0;
+    for (int u = L; u < n_units; u += kLoaders, ++k) {
+      if (k >= kInflight) {
+        wait_vmcnt<2 * G::NLOAD * (kInflight - 1)>();
+        publish(u - kLoaders * kInflight);
+      }
+      // The slot's previous unit (u - kSlots) must be passed by every compute
+      // wave and must itself have been published: a unit that no wave needs
+      // can otherwise still be landing when the slot is refetched.
+      int spins = 0;
+      while (true) {
+        const intx4 a = *reinterpret_cast<const volatile intx4*>(&sh->prog[0]);
+        const intx4 b = *reinterpret_cast<const volatile intx4*>(&sh->prog[4]);
+        const int mn = uniform(min(min(min(a[0], a[1]), min(a[2], a[3])), min(min(b[0], b[1]), min(b[2], b[3]))));
+        const bool free_slot = mn >= u - kSlots + 1 &&
+                               (u < kSlots || uniform(ld_relaxed(&sh->ready[u % kSlots])) == u - kSlots);
+        if (free_slot || ++spins > kSpinLimit) break;
+        __builtin_amdgcn_s_sleep(1);
+      }
+      compiler_fence();
+      issue(u);
+    }
+    wait_vmcnt<0>();
+    const int first = max(L, L + kLoaders * (k - kInflight));
+    for (int u = first; u < n_units; u += kLoaders) publish(u);
+    return;
+  }
+
+  // ---------------- compute wavefronts ----------------
+  const int half = lane >> 5, l32 = lane & 31;
+  const int wrow0 = row0 + wave * 32;
   bf16x8 qf[D / 16];
   {
     const int r = wrow0 + l32;
@@ -89,191 +315,146 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
       qf[kk] = __builtin_bit_cast(bf16x8, w);
     }
   }
-
-  // ---- the KV block sequence ----
-  int n_steps;
-  const int* ulist = nullptr;
-  const unsigned int* my_bits = nullptr;
-  if constexpr (SPARSE) {
-    const int nword = (p.Sb + 31) >> 5;
-    unsigned int* bits = reinterpret_cast<unsigned int*>(smem + St::BYTES);
-    int* list = reinterpret_cast<int*>(bits + QB_PER_WG * nword);
-    __shared__ int s_cnt[kThreads / 64];
-    for (int i = tid; i < QB_PER_WG * nword; i += kThreads) bits[i] = 0;
-    __syncthreads();
-    {
-      const int slot = wave / WAVES_PER_QB;
-      const int qb = row0 / BS + slot;
-      if (wave % WAVES_PER_QB == 0 && qb < p.Sb) {
-        const int32_t* kl = p.kept_col + (long long)bh * p.nnz + p.row_ptr[qb];
-        const int cnt = p.kept_cnt[(long long)bh * p.Sb + qb];
-        for (int i = lane; i < cnt; i += 64) {
-          const int c = kl[i];
-          if (c >= 0 && c < p.Sb) atomicOr(&bits[slot * nword + (c >> 5)], 1u << (c & 31));
-        }
-      }
-    }
-    __syncthreads();
-    // compact the union in ascending order
-    int total = 0;
-    for (int w0 = 0; w0 < nword; w0 += kThreads) {
-      const int wi = w0 + tid;
-      unsigned int u = 0;
-      if (wi < nword)
-        for (int s = 0; s < QB_PER_WG; ++s) u |= bits[s * nword + wi];
-      const int c = __popc(u);
-      int incl = c;
-      for (int off = 1; off < 64; off <<= 1) {
-        const int o = __shfl_up(incl, off);
-        if (lane >= off) incl += o;
-      }
-      if (lane == 63) s_cnt[wave] = incl;
-      __syncthreads();
-      int woff = 0, wtot = 0;
-      for (int w = 0; w < kThreads / 64; ++w) {
-        woff += w < wave ? s_cnt[w] : 0;
-        wtot += s_cnt[w];
-      }
-      int pos = total + woff + incl - c;
-      while (u) {
-        const int bit = __ffs(u) - 1;
-        list[pos++] = wi * 32 + bit;
-        u &= u - 1;
-      }
-      total += wtot;
-      __syncthreads();
-    }
-    n_steps = total;
-    ulist = list;
-    my_bits = bits + (wave / WAVES_PER_QB) * nword;
-  } else {
-    n_steps = (p.S + BS - 1) / BS;
-  }
-
-  const bool wave_rows = wrow0 < p.S;
-
-  // ---- loads: ring of PREFETCH register stages ----
-  u32x4 kr[St::PREFETCH][St::CPT], vr[St::PREFETCH][St::CPT];
-  auto issue = [&](int ps, int j) {
-    const int c = SPARSE ? ulist[j] : j;
-#pragma unroll
-    for (int i = 0; i < St::CPT; ++i) {
-      const int ci = tid + i * kThreads;
-      const int key = c * BS + ci / (D / 8);
-      const int d0 = (ci % (D / 8)) * 8;
-      u32x4 kw = {0, 0, 0, 0}, vw = {0, 0, 0, 0};
-      if (ci < St::CHUNKS && key < p.S) {
-        kw = *reinterpret_cast<const u32x4*>(Kg + (size_t)key * D + d0);
-        vw = *reinterpret_cast<const u32x4*>(Vg + (size_t)key * D + d0);
-      }
-      kr[ps][i] = kw;
-      vr[ps][i] = vw;
-    }
-  };
-  auto store = [&](int ps, int buf) {
-    uint16_t* sk = stage + buf * St::BUF_ELEMS;
-    uint16_t* sv = sk + St::K_ELEMS;
-#pragma unroll
-    for (int i = 0; i < St::CPT; ++i) {
-      const int ci = tid + i * kThreads;
-      if (ci < St::CHUNKS) {
-        const int kl = ci / (D / 8);
-        const int d0 = (ci % (D / 8)) * 8;
-        *reinterpret_cast<u32x4*>(sk + kl * St::KSTR + d0) = kr[ps][i];
-        const int slot = (kl & ~31) + v_slot(kl & 31);
-        const u32x4 w = vr[ps][i];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          sv[(d0 + 2 * e) * St::VSTR + slot] = (uint16_t)(w[e] & 0xffffu);
-          sv[(d0 + 2 * e + 1) * St::VSTR + slot] = (uint16_t)(w[e] >> 16);
-        }
-      }
-    }
-  };
-
   floatx16 oacc[D / 32];
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) oacc[dt] = floatx16{};
-  float m_run = -INFINITY, l_run = 0.f;
+  const float c = p.scale_log2;
+  const bool c_pos = c >= 0.f;
+  const float c_abs = fabsf(c);
+  float m_ref = -INFINITY;   // reference row max of s * c (log2 units)
+  float l_run = 0.f;
 
-  auto compute = [&](int buf, int c) {
-    const uint16_t* sk = stage + buf * St::BUF_ELEMS;
-    const uint16_t* sv = sk + St::K_ELEMS;
+  // A = V^T operands for one 32-dim tile: lane l takes dims dt*32 + l%32 and,
+  // for MFMA step j, keys 16j + 8r + 4*half + (0..3) from transposing read r.
+  auto load_v = [&](const unsigned char* sv, int dt, bf16x8 (&va)[2]) {
+    const int kq = (lane & 15) >> 2;
+    const int dim = dt * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 #pragma unroll
-    for (int u = 0; u < NUNIT; ++u) {
-      const int key0 = c * BS + u * 32;
-      if (key0 >= p.S) break;
-      floatx16 s = {};
+    for (int j = 0; j < 2; ++j) {
+      bf16x4_v part[2];
 #pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(sk + (u * 32 + l32) * St::KSTR + kk * 16 + half * 8);
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s, 0, 0, 0);
+      for (int r = 0; r < 2; ++r) {
+        const int key = 16 * j + 8 * r + 4 * half + kq;
+        const int ch = (dim >> 3) ^ swz_v<D>(key);
+        part[r] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((DR_LDS bf16x4_v*)(sv + key * G::RB + ch * 16 + (dim & 7) * 2));
       }
-      float x[16];
-      float mloc = -INFINITY;
-      const bool ragged = key0 + 32 > p.S;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        x[i] = s[i] * p.scale_log2;
-        if (ragged && key0 + 8 * (i >> 2) + 4 * half + (i & 3) >= p.S) x[i] = -INFINITY;
-        mloc = fmaxf(mloc, x[i]);
-      }
-      mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-      const float m_new = fmaxf(m_run, mloc);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      m_run = m_new;
-      float psum = 0.f;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        x[i] = __builtin_amdgcn_exp2f(x[i] - m_new);
-        psum += x[i];
-      }
-      l_run = l_run * alpha + psum;
-#pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt) oacc[dt] *= alpha;
-      bf16x8 pb[2];
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        floatx8 f = {x[8 * j], x[8 * j + 1], x[8 * j + 2], x[8 * j + 3],
-                     x[8 * j + 4], x[8 * j + 5], x[8 * j + 6], x[8 * j + 7]};
-        pb[j] = __builtin_convertvector(f, bf16x8);
-      }
-#pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt) {
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(sv + (dt * 32 + l32) * St::VSTR + u * 32 + 16 * j + 8 * half);
-          oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[j], oacc[dt], 0, 0, 0);
-        }
-      }
+      va[j] = bf16x8{part[0][0], part[0][1], part[0][2], part[0][3], part[1][0], part[1][1], part[1][2], part[1][3]};
     }
   };
 
-  // ---- main loop ----
+  auto compute = [&](const unsigned char* slot, int key0) {
+    const unsigned char* sk = slot;
+    const unsigned char* sv = slot + G::TBYTES;
+    floatx16 s = {};
 #pragma unroll
-  for (int ps = 0; ps < St::PREFETCH; ++ps)
-    if (ps < n_steps) issue(ps, ps);
-  for (int j0 = 0; j0 < n_steps; j0 += St::PREFETCH) {
+    for (int k0 = 0; k0 < D / 16; k0 += 4) {
+      bf16x8 ka[4];
 #pragma unroll
-    for (int ps = 0; ps < St::PREFETCH; ++ps) {
-      const int j = j0 + ps;
-      if (j >= n_steps) break;
-      const int buf = j & 1;
-      store(ps, buf);
-      __syncthreads();
-      if (j + St::PREFETCH < n_steps) issue(ps, j + St::PREFETCH);
-      bool need = wave_rows;
-      int c = j;
-      if constexpr (SPARSE) {
-        c = ulist[j];
-        need = need && ((my_bits[c >> 5] >> (c & 31)) & 1u);
+      for (int kk = 0; kk < 4; ++kk) {
+        const int ch = (2 * (k0 + kk) + half) ^ swz_k<D>(l32);
+        ka[kk] = *reinterpret_cast<const bf16x8*>(sk + l32 * G::RB + ch * 16);
       }
-      if (need) compute(buf, c);
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kk], qf[k0 + kk], s, 0, 0, 0);
+    }
+    // the first V^T operands load while the softmax runs
+    bf16x8 va[2][2];
+    load_v(sv, 0, va[0]);
+    // row max of s * c over the valid keys: |c| * max(s) for c >= 0, |c| * max(-s)
+    // otherwise; padding keys (beyond S) are left out of the max and get p = 0
+    const bool ragged = key0 + kUnit > p.S;
+    float mx;
+    if (c_pos && !ragged) {
+      mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+#pragma unroll
+      for (int i = 4; i < 16; i += 4) mx = fmaxf(mx, fmaxf(fmaxf(s[i], s[i + 1]), fmaxf(s[i + 2], s[i + 3])));
+    } else {
+      // element i holds key key0 + 4*half + 8*(i/4) + i%4: valid iff below lim
+      const int lim = p.S - key0 - 4 * half;
+      mx = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const bool valid = 8 * (i >> 2) + (i & 3) < lim;
+        mx = fmaxf(mx, valid ? (c_pos ? s[i] : -s[i]) : -INFINITY);
+      }
+    }
+    mx = max_halves(mx) * c_abs;
+    if (__ballot(mx - m_ref > kRescaleLog2) != 0ull) {
+      const float m_new = fmaxf(m_ref, mx);
+      const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
+      m_ref = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) oacc[dt] *= alpha;
+    }
+    float x[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) x[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, -m_ref));
+    if (ragged) {
+      const int lim = p.S - key0 - 4 * half;
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (8 * (i >> 2) + (i & 3) >= lim) x[i] = 0.f;
+    }
+    float psum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) psum += x[i];
+    l_run += psum;
+    bf16x8 pb[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const floatx8 f = {x[8 * j], x[8 * j + 1], x[8 * j + 2], x[8 * j + 3],
+                         x[8 * j + 4], x[8 * j + 5], x[8 * j + 6], x[8 * j + 7]};
+      pb[j] = __builtin_convertvector(f, bf16x8);
+    }
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) {
+      if (dt + 1 < D / 32) load_v(sv, dt + 1, va[(dt + 1) & 1]);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[dt & 1][j], pb[j], oacc[dt], 0, 0, 0);
+    }
+  };
+
+  auto consume = [&](int u, int key0) {
+    compiler_fence();
+    st_relaxed(&sh->prog[wave], u);
+    int spins = 0;
+    while (ld_relaxed(&sh->ready[u % kSlots]) != u && ++spins <= kSpinLimit) __builtin_amdgcn_s_sleep(1);
+    compiler_fence();
+    compute(ring + (u % kSlots) * G::SLOT, key0);
+  };
+
+  if (wrow0 < p.S) {
+    if constexpr (SPARSE) {
+      const unsigned int* mine = bits + (wave / WPQ) * nword;
+      for (int wi = 0; wi < nword; ++wi) {
+        unsigned int m = mine[wi];
+        if (!m) continue;
+        const unsigned int uw = uword[wi];
+        const int wp = wpre[wi];
+        while (m) {
+          const int b = __ffs(m) - 1;
+          m &= m - 1;
+          const int j = wp + __popc(uw & ((1u << b) - 1u));
+          const int cblk = wi * 32 + b;
+#pragma unroll
+          for (int q = 0; q < UPB; ++q) {
+            const int key0 = cblk * BS + q * kUnit;
+            if (key0 >= p.S) break;
+            consume(j * UPB + q, key0);
+          }
+        }
+      }
+    } else {
+      for (int u = 0; u < n_units; ++u) consume(u, u * kUnit);
     }
   }
+  compiler_fence();
+  st_relaxed(&sh->prog[wave], kDone);
 
-  // ---- epilogue: normalise and store bf16 ----
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  // ---------------- epilogue ----------------
+  const float l_tot = sum_halves(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   const int r = wrow0 + l32;
   if (r < p.S) {
@@ -282,8 +463,8 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
     for (int dt = 0; dt < D / 32; ++dt) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        floatx4 f = {oacc[dt][4 * g] * inv, oacc[dt][4 * g + 1] * inv, oacc[dt][4 * g + 2] * inv,
-                     oacc[dt][4 * g + 3] * inv};
+        const floatx4 f = {oacc[dt][4 * g] * inv, oacc[dt][4 * g + 1] * inv, oacc[dt][4 * g + 2] * inv,
+                           oacc[dt][4 * g + 3] * inv};
         const bf16x4 hb = __builtin_convertvector(f, bf16x4);
         *reinterpret_cast<u32x2*>(orow + dt * 32 + 8 * g + 4 * half) = __builtin_bit_cast(u32x2, hb);
       }
@@ -293,11 +474,10 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
 
 template <int D, int BS, bool SPARSE>
 hipError_t launch_one(const AttnParams& p, hipStream_t stream) {
-  using St = Stage<D, BS>;
-  size_t lds = St::BYTES;
+  size_t lds = Geo<D>::RING + sizeof(Shared);
   if (SPARSE) {
     const int nword = (p.Sb + 31) / 32;
-    lds += (size_t)(kRowsPerWG / BS) * nword * 4 + (size_t)p.Sb * 4;
+    lds += (size_t)(kRows / BS) * nword * 4 + (size_t)nword * 8;
   }
   const dim3 grid((unsigned)p.n_tiles, (unsigned)p.BH);
   hipLaunchKernelGGL((attn_kernel<D, BS, SPARSE>), grid, dim3(kThreads), lds, stream, p);
@@ -315,8 +495,8 @@ hipError_t launch_sparse_attn(const AttnParams& p, int D, int Bs, hipStream_t st
 }
 
 hipError_t launch_dense_attn(const AttnParams& p, int D, hipStream_t stream) {
-  if (D == 128) return launch_one<128, 64, false>(p, stream);
-  if (D == 64) return launch_one<64, 64, false>(p, stream);
+  if (D == 128) return launch_one<128, 32, false>(p, stream);
+  if (D == 64) return launch_one<64, 32, false>(p, stream);
   return hipErrorInvalidValue;
 }
 

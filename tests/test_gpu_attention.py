@@ -130,6 +130,15 @@ def test_sparse_attention_random_masks(B, H, S, D, Bs):
     for b in range(B):
         for h in range(H):
             G.check_close(out[b, h], O.dense_attention(f64[0, b, h], f64[1, b, h], f64[2, b, h]), f"dense b{b} h{h}")
+    # any finite softmax scale: negative and zero as well
+    for scale in (-0.07, 0.0):
+        out = G.to_np(G.dr().sparse_attn(q, k, v, cand, kept, softmax_scale=scale))
+        outd = G.to_np(G.dr().attn(q, k, v, softmax_scale=scale))
+        for b in range(B):
+            for h in range(H):
+                x = [f64[i, b, h] for i in range(3)]
+                G.check_close(out[b, h], O.sparse_attention(*x, Bs, lists[(b, h)], scale=scale), f"scale {scale}")
+                G.check_close(outd[b, h], O.dense_attention(*x, scale=scale), f"dense scale {scale}")
 
 
 def test_sparse_attention_empty_rows_and_bad_entries():
