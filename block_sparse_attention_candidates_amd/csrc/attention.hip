@@ -129,8 +129,8 @@ __device__ inline void wait_vmcnt() {
 }
 
 struct Shared {
+  int prog[kConsumers];        // next unit each compute wave may read (16-byte aligned)
   int ready[kSlots];           // unit index held by each slot (-1: none)
-  int prog[kConsumers];        // next unit each compute wave may read
   int n_units;
   int pad[15 - kSlots - kConsumers > 0 ? 15 - kSlots - kConsumers : 1];
 };

@@ -36,6 +36,27 @@ __device__ void build_table(const CandParams& p, int* s_w, int* s_sf) {
 __device__ bool is_candidate(int a, int b, const CandParams& p, const int* s_w, const int* s_sf) {
   const int q0 = a * p.Bs, q1 = min(q0 + p.Bs, p.S);
   const int k0 = b * p.Bs, k1 = min(k0 + p.Bs, p.S);
+  if (p.theta_c == 0.0 && p.theta_m == 0.0) {
+    // With both thresholds at 0 the block is a candidate iff some query frame
+    // segment and some key frame segment are retained (Eq. 6) and come within
+    // w(t) of each other (Eq. 7): the interval distance
+    // max(0, v_lo - u_hi, u_lo - v_hi) decides it.
+    for (int s = q0; s < q1;) {
+      const int fq = s / p.Nt;
+      const int s_end = min(q1, (fq + 1) * p.Nt);
+      const int ulo = s - fq * p.Nt, uhi = s_end - 1 - fq * p.Nt;
+      for (int k = k0; k < k1;) {
+        const int fk = k / p.Nt;
+        const int k_end = min(k1, (fk + 1) * p.Nt);
+        const int vlo = k - fk * p.Nt, vhi = k_end - 1 - fk * p.Nt;
+        const int t = fq > fk ? fq - fk : fk - fq;
+        if (t % s_sf[t] == 0 && max(0, max(vlo - uhi, ulo - vhi)) <= s_w[t]) return true;
+        k = k_end;
+      }
+      s = s_end;
+    }
+    return false;
+  }
   const double nq = (double)(q1 - q0), nk = (double)(k1 - k0);
   int active = 0;
   for (int k = k0; k < k1; ++k) {

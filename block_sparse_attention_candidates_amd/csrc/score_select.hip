@@ -5,11 +5,11 @@
 //   pool:   one wavefront per (tensor, b, h, block): coalesced 16-byte bf16 loads
 //           of the block's valid rows, float32 sums, cross-lane reduction, mean.
 //           HBM-bound (reads Q and K once).
-//   scores: one wavefront per (b, h, 32 query blocks): walks the 32 rows'
-//           candidate lists in key-block order, and for every 32x32 tile of
-//           (query block, key block) pairs that holds a candidate computes all
-//           1024 dot products Qbar . Kbar with the fp32 MFMA (32x32x2), then
-//           scatters the candidate entries into CSR order.
+//   scores: one workgroup per (b, h, 32 query blocks): LDS bitmaps of the 32
+//           rows' candidates locate every entry's CSR position; each 32x32
+//           tile of (query block, key block) pairs holding a candidate gets
+//           all 1024 dot products Qbar . Kbar from the fp32 MFMA (32x32x2),
+//           and its candidate entries are written in place.
 //   select: one workgroup per (b, h, query block): radix select (4 passes of
 //           8 bits) over order-preserving score keys with integer histograms:
 //           counts for static-ratio, fixed-point softmax mass for
@@ -71,78 +71,121 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolParams p) {
 
 // ---------------------------------------------------------------------------
 // Candidate scores via fp32 MFMA tiles.
+// A workgroup (4 wavefronts) owns 32 consecutive query blocks (rows) of one
+// (b, h). Their candidate entries are one contiguous CSR range; the workgroup
+// turns it into per-row bitmaps over the key blocks in LDS plus, per row and
+// 32-block word, the CSR position of the word's first entry. A word with any
+// bit set in any row is an active 32x32 tile; the waves share the active
+// tiles, compute all 1024 dot products of a tile with the fp32 MFMA and write
+// the candidate entries straight to their CSR positions.
 // v_mfma_f32_32x32x2_f32: A is 32x2 (lane l: row l%32, k = l/32), B is 2x32
 // (lane l: column l%32, k = l/32), D is 32x32 (lane l: column l%32, element i:
 // row 8*(i/4) + 4*(l/32) + i%4). The reduction dimension is split so that lane
 // half h walks dims [h*D/2, (h+1)*D/2): each MFMA adds one dim from each half.
 // ---------------------------------------------------------------------------
+constexpr int kScoreThreads = 256;
+
 template <int D>
-__global__ __launch_bounds__(64) void score_kernel(ScoreParams p) {
+__global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreParams p) {
   constexpr int HD = D / 2;
-  __shared__ float tileT[32][33];
-  const int lane = threadIdx.x;
-  const int m = lane & 31, half = lane >> 5;
+  extern __shared__ unsigned int s_bits[];          // [32][nword] row bitmaps
+  __shared__ int s_ntiles;
+  const int nword = (p.Sb + 31) >> 5;
+  int* s_pos = reinterpret_cast<int*>(s_bits + 32 * nword);   // [32][nword] CSR position of each word
+  int* s_tiles = s_pos + 32 * nword;                          // active words
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int a0 = blockIdx.x * 32;
   const int bm = blockIdx.y;              // b * Hm + hm
   const int b = bm / p.Hm, hm = bm - b * p.Hm;
-  const int row = a0 + m;
-  const bool row_ok = row < p.Sb;
-  int cur = row_ok ? p.row_ptr[row] : 0;
-  const int end = row_ok ? p.row_ptr[row + 1] : 0;
   const long long out_base = (long long)bm * p.nnz;
-  // pooled head index of head j of the score: per-head mode uses head hm,
-  // fused mode sums heads 0..g-1.
-  auto pooled = [&](int j) -> size_t { return (size_t)(b * p.Hp + (p.g == 1 ? hm : j)) * p.Sb; };
 
-  float qa[HD];
-  if (p.g == 1) {
-    const float* src = p.qbar + (pooled(0) + (row_ok ? row : 0)) * D + half * HD;
-#pragma unroll
-    for (int i = 0; i < HD; i += 4) {
-      floatx4 v = row_ok ? *reinterpret_cast<const floatx4*>(src + i) : floatx4{0, 0, 0, 0};
-      qa[i] = v[0]; qa[i + 1] = v[1]; qa[i + 2] = v[2]; qa[i + 3] = v[3];
+  for (int i = tid; i < 32 * nword; i += kScoreThreads) s_bits[i] = 0;
+  __syncthreads();
+  for (int m = wave; m < 32; m += 4) {
+    const int a = a0 + m;
+    if (a >= p.Sb) continue;
+    const int e1 = p.row_ptr[a + 1];
+    for (int e = p.row_ptr[a] + lane; e < e1; e += 64) {
+      const int c = p.cols[e];
+      atomicOr(&s_bits[m * nword + (c >> 5)], 1u << (c & 31));
     }
   }
-  while (true) {
-    // next key-block tile holding a candidate of any of the 32 rows
-    int nxt = cur < end ? p.cols[cur] : 0x7fffffff;
-    for (int off = 32; off > 0; off >>= 1) nxt = min(nxt, __shfl_xor(nxt, off));
-    if (nxt == 0x7fffffff) break;
-    const int c0 = nxt & ~31;
-    const int kc = c0 + m;
+  __syncthreads();
+  for (int m = wave; m < 32; m += 4) {
+    const int a = a0 + m;
+    int run = a < p.Sb ? p.row_ptr[a] : 0;
+    for (int w0 = 0; w0 < nword; w0 += 64) {
+      const int w = w0 + lane;
+      const int cnt = w < nword ? __popc(s_bits[m * nword + w]) : 0;
+      int incl = cnt;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int o = __shfl_up(incl, off);
+        if (lane >= off) incl += o;
+      }
+      if (w < nword) s_pos[m * nword + w] = run + incl - cnt;
+      run += __shfl(incl, 63);
+    }
+  }
+  if (wave == 0) {
+    int n = 0;
+    for (int w0 = 0; w0 < nword; w0 += 64) {
+      const int w = w0 + lane;
+      unsigned int any = 0;
+      if (w < nword)
+        for (int m = 0; m < 32; ++m) any |= s_bits[m * nword + w];
+      const unsigned long long bal = __ballot(any != 0);
+      const int before = __builtin_amdgcn_mbcnt_hi((unsigned)(bal >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)bal, 0));
+      if (any) s_tiles[n + before] = w;
+      n += __popcll(bal);
+    }
+    if (lane == 0) s_ntiles = n;
+  }
+  __syncthreads();
+  const int ntiles = s_ntiles;
+
+  const int m32 = lane & 31, half = lane >> 5;
+  const int row = a0 + m32;
+  const bool row_ok = row < p.Sb;
+  // pooled head index of head j of the score: per-head mode uses head hm,
+  // fused mode sums heads 0..g-1
+  auto pooled = [&](int j) -> size_t { return (size_t)(b * p.Hp + (p.g == 1 ? hm : j)) * p.Sb; };
+  float qa[HD];
+  auto load_q = [&](int j) {
+    const float* src = p.qbar + (pooled(j) + (row_ok ? row : 0)) * D + half * HD;
+#pragma unroll
+    for (int i = 0; i < HD; i += 4) {
+      const floatx4 v = row_ok ? *reinterpret_cast<const floatx4*>(src + i) : floatx4{0, 0, 0, 0};
+      qa[i] = v[0]; qa[i + 1] = v[1]; qa[i + 2] = v[2]; qa[i + 3] = v[3];
+    }
+  };
+  if (p.g == 1) load_q(0);
+  for (int j = wave; j < ntiles; j += 4) {
+    const int t = s_tiles[j];
+    const int kc = t * 32 + m32;
     const bool kc_ok = kc < p.Sb;
     floatx16 acc = {};
-    for (int j = 0; j < p.g; ++j) {
-      if (p.g != 1) {
-        const float* src = p.qbar + (pooled(j) + (row_ok ? row : 0)) * D + half * HD;
-#pragma unroll
-        for (int i = 0; i < HD; i += 4) {
-          floatx4 v = row_ok ? *reinterpret_cast<const floatx4*>(src + i) : floatx4{0, 0, 0, 0};
-          qa[i] = v[0]; qa[i + 1] = v[1]; qa[i + 2] = v[2]; qa[i + 3] = v[3];
-        }
-      }
-      const float* ksrc = p.kbar + (pooled(j) + (kc_ok ? kc : 0)) * D + half * HD;
+    for (int hh = 0; hh < p.g; ++hh) {
+      if (p.g != 1) load_q(hh);
+      const float* ksrc = p.kbar + (pooled(hh) + (kc_ok ? kc : 0)) * D + half * HD;
 #pragma unroll
       for (int i = 0; i < HD; i += 4) {
-        floatx4 kv = kc_ok ? *reinterpret_cast<const floatx4*>(ksrc + i) : floatx4{0, 0, 0, 0};
+        const floatx4 kv = kc_ok ? *reinterpret_cast<const floatx4*>(ksrc + i) : floatx4{0, 0, 0, 0};
         acc = __builtin_amdgcn_mfma_f32_32x32x2f32(qa[i], kv[0], acc, 0, 0, 0);
         acc = __builtin_amdgcn_mfma_f32_32x32x2f32(qa[i + 1], kv[1], acc, 0, 0, 0);
         acc = __builtin_amdgcn_mfma_f32_32x32x2f32(qa[i + 2], kv[2], acc, 0, 0, 0);
         acc = __builtin_amdgcn_mfma_f32_32x32x2f32(qa[i + 3], kv[3], acc, 0, 0, 0);
       }
     }
+    // element i of this lane is (row 8*(i/4) + 4*half + i%4, key block t*32 + m32)
+    const unsigned int below = (1u << m32) - 1u;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) tileT[8 * (i >> 2) + 4 * half + (i & 3)][m] = acc[i];
-    __syncthreads();
-    // scatter this tile's candidate entries of row m (both halves walk the
-    // cursor; half 0 writes)
-    while (cur < end) {
-      const int c = p.cols[cur];
-      if (c >= c0 + 32) break;
-      if (half == 0) p.scores[out_base + cur] = tileT[m][c - c0] * p.scale;
-      ++cur;
+    for (int i = 0; i < 16; ++i) {
+      const int m = 8 * (i >> 2) + 4 * half + (i & 3);
+      const unsigned int bits = s_bits[m * nword + t];
+      if ((bits >> m32) & 1u)
+        p.scores[out_base + s_pos[m * nword + t] + __popc(bits & below)] = acc[i] * p.scale;
     }
-    __syncthreads();
   }
 }
 
@@ -338,10 +381,12 @@ hipError_t launch_pool(const PoolParams& p, hipStream_t stream) {
 
 hipError_t launch_scores(const ScoreParams& p, int B, hipStream_t stream) {
   const dim3 grid((unsigned)((p.Sb + 31) / 32), (unsigned)(B * p.Hm));
+  const int nword = (p.Sb + 31) / 32;
+  const size_t lds = (size_t)nword * (32 * 4 + 32 * 4 + 4);
   if (p.D == 128)
-    hipLaunchKernelGGL(score_kernel<128>, grid, dim3(64), 0, stream, p);
+    hipLaunchKernelGGL(score_kernel<128>, grid, dim3(kScoreThreads), lds, stream, p);
   else
-    hipLaunchKernelGGL(score_kernel<64>, grid, dim3(64), 0, stream, p);
+    hipLaunchKernelGGL(score_kernel<64>, grid, dim3(kScoreThreads), lds, stream, p);
   return hipGetLastError();
 }
 
