@@ -12,7 +12,7 @@
 // sequence of KV blocks the workgroup streams, cut into 32-key units.
 //
 // Streaming without barriers: the loaders copy units from HBM/L2 straight into
-// an 8-slot LDS ring with direct-to-LDS loads (16 B per lane, no registers),
+// an LDS ring (8 or more slots) with direct-to-LDS loads (16 B per lane, no registers),
 // each keeping 2 units in flight, and publish a slot once its loads have
 // landed. Each compute wavefront walks only the units of the KV blocks its own
 // query block kept, announces its position, waits for the slot, computes. A
@@ -58,22 +58,23 @@ constexpr int kConsumers = 8;
 constexpr int kLoaders = 3;
 constexpr int kThreads = (kConsumers + kLoaders) * 64;
 constexpr int kRows = kConsumers * 32;       // query rows per workgroup
-constexpr int kSlots = 8;                    // ring depth, in 32-key units
 constexpr int kInflight = 2;                 // units in flight per loader
-static_assert(kSlots >= kInflight * kLoaders + 1, "ring too shallow for the loaders' pipelines");
+constexpr int kMaxSlots = 16;                // ring depth limit, in 32-key units
+constexpr int kLdsBytes = 160 * 1024;        // LDS per workgroup on gfx950
 static_assert(kConsumers == 8, "the loaders read the 8 progress entries as two int4");
 constexpr int kUnit = 32;
 constexpr float kRescaleLog2 = 8.0f;         // rescale only past 2^8 growth
 constexpr int kSpinLimit = 1 << 26;
 constexpr int kDone = 0x3fffffff;
 
-template <int D>
+template <int D, int NS>
 struct Geo {
   static constexpr int RB = 2 * D;               // bytes per key row
   static constexpr int TBYTES = kUnit * RB;      // K (or V) bytes of a unit
   static constexpr int SLOT = 2 * TBYTES;        // K then V
   static constexpr int NLOAD = TBYTES / 1024;    // 1 KB direct loads per tensor
-  static constexpr int RING = kSlots * SLOT;
+  static constexpr int RING = NS * SLOT;
+  static_assert(NS >= kInflight * kLoaders + 1 && NS <= kMaxSlots, "ring depth");
 };
 
 // 16-byte chunk swizzles (physical chunk = logical chunk ^ swz(row)).
@@ -97,16 +98,18 @@ __device__ inline void compiler_fence() { asm volatile("" ::: "memory"); }
 // the compiler does not treat the ring as a pending LDS write of this wave
 // (which makes it drain every load before each flag access); the loader
 // waits on these loads itself with explicit s_waitcnt vmcnt. The asm has no
-// output register and the address registers are read at issue.
+// output register and the address registers are read at issue; one wait state
+// separates the M0 write from the load that reads it (the compiler cannot see
+// inside the asm to insert it).
 __device__ inline void dma16(const void* gptr, unsigned char* lds_wave_base) {
   const unsigned m0 = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)lds_wave_base);
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0), "v"(gptr) : "memory", "m0");
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0), "v"(gptr) : "memory", "m0");
 }
 
 // The same copy with an SGPR base and a per-lane 32-bit byte offset (saddr form).
 __device__ inline void dma16_s(const void* sbase, unsigned voff, unsigned char* lds_wave_base) {
   const unsigned m0 = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)lds_wave_base);
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(m0), "v"(voff), "s"(sbase) : "memory", "m0");
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(m0), "v"(voff), "s"(sbase) : "memory", "m0");
 }
 
 // max / sum of a value over the two 32-lane halves: v_permlane32_swap(v, v)
@@ -130,14 +133,15 @@ __device__ inline void wait_vmcnt() {
 
 struct Shared {
   int prog[kConsumers];        // next unit each compute wave may read (16-byte aligned)
-  int ready[kSlots];           // unit index held by each slot (-1: none)
+  int ready[kMaxSlots];        // unit index held by each slot (-1: none)
   int n_units;
-  int pad[15 - kSlots - kConsumers > 0 ? 15 - kSlots - kConsumers : 1];
+  int pad[3];
 };
 
-template <int D, int BS, bool SPARSE>
+template <int D, int BS, bool SPARSE, int NS>
 __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
-  using G = Geo<D>;
+  using G = Geo<D, NS>;
+  constexpr int kSlots = NS;
   constexpr int UPB = BS / kUnit;                 // units per KV block
   constexpr int QB = kRows / BS;                  // query blocks per workgroup
   constexpr int WPQ = BS / 32;                    // compute waves per query block
@@ -285,8 +289,11 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
       // can otherwise still be landing when the slot is refetched.
       int spins = 0;
       while (true) {
-        const intx4 a = *reinterpret_cast<const volatile intx4*>(&sh->prog[0]);
-        const intx4 b = *reinterpret_cast<const volatile intx4*>(&sh->prog[4]);
+        // explicit LDS loads: a generic (flat) load would also wait for this
+        // wave's copies in flight
+        const volatile DR_LDS intx4* pv = (const volatile DR_LDS intx4*)(&sh->prog[0]);
+        const intx4 a = pv[0];
+        const intx4 b = pv[1];
         const int mn = uniform(min(min(min(a[0], a[1]), min(a[2], a[3])), min(min(b[0], b[1]), min(b[2], b[3]))));
         const bool free_slot = mn >= u - kSlots + 1 &&
                                (u < kSlots || uniform(ld_relaxed(&sh->ready[u % kSlots])) == u - kSlots);
@@ -472,15 +479,28 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
   }
 }
 
-template <int D, int BS, bool SPARSE>
-hipError_t launch_one(const AttnParams& p, hipStream_t stream) {
-  size_t lds = Geo<D>::RING + sizeof(Shared);
+template <int D, int BS, bool SPARSE, int NS>
+size_t lds_bytes(const AttnParams& p) {
+  size_t lds = Geo<D, NS>::RING + sizeof(Shared);
   if (SPARSE) {
     const int nword = (p.Sb + 31) / 32;
     lds += (size_t)(kRows / BS) * nword * 4 + (size_t)nword * 8;
   }
+  return lds;
+}
+
+// Ring depth: 9 slots of 32 keys at D = 128 (16 at D = 64) when the sparse
+// bitmaps leave room for them, else 8.
+template <int D, int BS, bool SPARSE>
+hipError_t launch_one(const AttnParams& p, hipStream_t stream) {
+  constexpr int DEEP = D == 128 ? 9 : 16;
   const dim3 grid((unsigned)p.n_tiles, (unsigned)p.BH);
-  hipLaunchKernelGGL((attn_kernel<D, BS, SPARSE>), grid, dim3(kThreads), lds, stream, p);
+  const size_t deep = lds_bytes<D, BS, SPARSE, DEEP>(p);
+  const size_t base = lds_bytes<D, BS, SPARSE, 8>(p);
+  if (deep <= (size_t)kLdsBytes)
+    hipLaunchKernelGGL((attn_kernel<D, BS, SPARSE, DEEP>), grid, dim3(kThreads), deep, stream, p);
+  else
+    hipLaunchKernelGGL((attn_kernel<D, BS, SPARSE, 8>), grid, dim3(kThreads), base, stream, p);
   return hipGetLastError();
 }
 
