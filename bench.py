@@ -41,7 +41,9 @@ def parse():
     ap.add_argument("--dense-iters", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-dense", action="store_true")
-    ap.add_argument("--cpu-blocks", type=int, default=160, help="query blocks in the CPU oracle sample")
+    ap.add_argument("--cpu-blocks", type=int, default=960, help="query blocks in the CPU oracle sample")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="after timing, run one plain 1 GiB device copy (the reference for HBM byte counters)")
     return ap.parse_args()
 
 
@@ -111,8 +113,8 @@ def cpu_baseline(w, mode, ratio, tau, n_blocks):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); multi-GPU execution is not part of "
-              f"this build", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the attention path here is a "
+              f"single-GPU kernel; run it with --gpus 1", file=sys.stderr)
         sys.exit(2)
     import torch
     import block_sparse_attention_candidates_amd as dr
@@ -218,6 +220,16 @@ def main():
                      "traffic": tr["hbm_bytes_per_launch"] if tr else None,
                      "kernel": "dr_sparse_attn (attn_kernel<128,B_s,sparse>)"},
     }
+    if args.calib_copy:
+        # a plain copy kernel of known size: its FETCH_SIZE / WRITE_SIZE readings
+        # scale the attention kernel's counters to bytes
+        # (an elementwise kernel, so that the copy runs on the shader engines)
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
     if not args.no_cpu:
         print("# timing the CPU oracle sample", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(w, args.mode, ratio, tau, args.cpu_blocks)
