@@ -301,7 +301,11 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
         __builtin_amdgcn_s_sleep(1);
       }
       compiler_fence();
+      // raised wave priority while issuing: the copies of a unit leave in
+      // one burst instead of interleaving with the compute waves' issue
+      __builtin_amdgcn_s_setprio(2);
       issue(u);
+      __builtin_amdgcn_s_setprio(0);
     }
     wait_vmcnt<0>();
     const int first = max(L, L + kLoaders * (k - kInflight));

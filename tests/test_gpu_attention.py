@@ -188,3 +188,28 @@ def test_attention_special_cases_and_determinism():
     oz = G.to_np(G.dr().attn(q, k, v, softmax_scale=0.0))
     vh = G.head_f64(name, 0, 0)[2]
     np.testing.assert_allclose(oz[0, 0, :4], np.broadcast_to(vh.mean(0), (4, w.head_dim)), atol=2e-2)
+
+
+def test_sparse_attention_long_sequence():
+    """13,050 query blocks at D = 128, B_s = 32: the query-block bitmaps leave
+    no room for a 9-slot ring, so the 8-slot form of the kernel runs."""
+    import torch
+    G.log("[attn] long sequence: 116 frames x 3600 tokens, one head")
+    Nf, Nt, Bs, D = 116, 3600, 32, 128
+    S = Nf * Nt
+    rng = np.random.default_rng(11)
+    bits = workloads.bf16_bits(rng.standard_normal((3, 1, 1, S, D)).astype(np.float32))
+    q, k, v = (torch.from_numpy(bits[i]).view(torch.bfloat16).cuda() for i in range(3))
+    cand = G.dr().build_candidates(G.dr().radial_cfg(Nf, Nt, Bs, 1.0, 4.0))
+    Sb = cand.num_blocks
+    assert Sb == 13050
+    kept = G.dr().score_select(q, k, cand, mode="static", ratio=0.05)
+    out = G.to_np(G.dr().sparse_attn(q, k, v, cand, kept)[0, 0])
+    rp, _ = G.host_csr(cand)
+    lists = G.kept_lists(kept, rp, cand.nnz, Sb, 0)
+    f64 = (bits[:, 0, 0].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    blocks = G.sample_blocks(Sb, 16, seed=12)
+    rows = np.concatenate([np.arange(a * Bs, min((a + 1) * Bs, S)) for a in blocks])
+    ref = O.sparse_attention_rows(f64[0], f64[1], f64[2], Bs, lists, blocks)
+    r = G.check_close(out[rows], ref, "long sequence")
+    G.log(f"   rel-L2 {r[0]:.2e} max {r[1]:.2e}")
