@@ -8,8 +8,9 @@
 //   scores: one workgroup per (b, h, 32 query blocks): LDS bitmaps of the 32
 //           rows' candidates locate every entry's CSR position; each 32x32
 //           tile of (query block, key block) pairs holding a candidate gets
-//           all 1024 dot products Qbar . Kbar from the fp32 MFMA (32x32x2),
-//           and its candidate entries are written in place.
+//           all 1024 dot products Qbar . Kbar in float32 from three bf16 MFMA
+//           products of split operands, and its candidate entries are
+//           written in place.
 //   select: one workgroup per (b, h, query block): radix select (4 passes of
 //           8 bits) over order-preserving score keys with integer histograms:
 //           counts for static-ratio, fixed-point softmax mass for
@@ -23,6 +24,8 @@ namespace {
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef float floatx8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 __device__ inline float bf16_lo(unsigned int w) { return __uint_as_float(w << 16); }
 __device__ inline float bf16_hi(unsigned int w) { return __uint_as_float(w & 0xffff0000u); }
@@ -70,24 +73,42 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// Candidate scores via fp32 MFMA tiles.
+// Candidate scores: float32 dot products from the bf16 MFMA in three parts.
 // A workgroup (4 wavefronts) owns 32 consecutive query blocks (rows) of one
 // (b, h). Their candidate entries are one contiguous CSR range; the workgroup
 // turns it into per-row bitmaps over the key blocks in LDS plus, per row and
 // 32-block word, the CSR position of the word's first entry. A word with any
 // bit set in any row is an active 32x32 tile; the waves share the active
-// tiles, compute all 1024 dot products of a tile with the fp32 MFMA and write
-// the candidate entries straight to their CSR positions.
-// v_mfma_f32_32x32x2_f32: A is 32x2 (lane l: row l%32, k = l/32), B is 2x32
-// (lane l: column l%32, k = l/32), D is 32x32 (lane l: column l%32, element i:
-// row 8*(i/4) + 4*(l/32) + i%4). The reduction dimension is split so that lane
-// half h walks dims [h*D/2, (h+1)*D/2): each MFMA adds one dim from each half.
+// tiles, compute all 1024 dot products of a tile and write the candidate
+// entries straight to their CSR positions.
+// Each float32 operand is split as x = hi + lo (bf16 each, exact up to
+// 2^-17 |x|) and q.k is accumulated in float32 as ql.kh + qh.kl + qh.kh with
+// v_mfma_f32_32x32x16_bf16 (the dropped ql.kl and the split remainders are
+// below 2^-16 |q||k| per product): a third of the issue cycles of the float32
+// MFMA for the same result to ~1e-6 at these score magnitudes.
+// Operand layout (32x32x16): A lane l holds row l%32, dims 16*kk + 8*(l/32)
+// + (0..7); B likewise for column l%32; D element i of lane l is (row
+// 8*(i/4) + 4*(l/32) + i%4, column l%32).
 // ---------------------------------------------------------------------------
 constexpr int kScoreThreads = 256;
 
+// x = hi + lo + r with hi = bf16(x), lo = bf16(x - hi) (both round to nearest
+// even; x - hi is exact in float32) and |r| <= 2^-17 |x|.
+__device__ inline void split(const floatx8& x, bf16x8& hi, bf16x8& lo) {
+  hi = __builtin_convertvector(x, bf16x8);
+  const floatx8 back = __builtin_convertvector(hi, floatx8);
+  lo = __builtin_convertvector(x - back, bf16x8);
+}
+
+__device__ inline floatx8 load8(const float* src) {
+  const floatx4 a = *reinterpret_cast<const floatx4*>(src);
+  const floatx4 b = *reinterpret_cast<const floatx4*>(src + 4);
+  return floatx8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+
 template <int D>
 __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreParams p) {
-  constexpr int HD = D / 2;
+  constexpr int KS = D / 16;   // 16-dim steps of v_mfma_f32_32x32x16_bf16
   extern __shared__ unsigned int s_bits[];          // [32][nword] row bitmaps
   __shared__ int s_ntiles;
   const int nword = (p.Sb + 31) >> 5;
@@ -150,13 +171,15 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreParams p) {
   // pooled head index of head j of the score: per-head mode uses head hm,
   // fused mode sums heads 0..g-1
   auto pooled = [&](int j) -> size_t { return (size_t)(b * p.Hp + (p.g == 1 ? hm : j)) * p.Sb; };
-  float qa[HD];
+  // this lane's 8 dims of 16-dim step kk: 16*kk + 8*half + (0..7), as hi + lo
+  bf16x8 qh[KS], ql[KS];
   auto load_q = [&](int j) {
-    const float* src = p.qbar + (pooled(j) + (row_ok ? row : 0)) * D + half * HD;
+    const float* src = p.qbar + (pooled(j) + (row_ok ? row : 0)) * D + 8 * half;
 #pragma unroll
-    for (int i = 0; i < HD; i += 4) {
-      const floatx4 v = row_ok ? *reinterpret_cast<const floatx4*>(src + i) : floatx4{0, 0, 0, 0};
-      qa[i] = v[0]; qa[i + 1] = v[1]; qa[i + 2] = v[2]; qa[i + 3] = v[3];
+    for (int kk = 0; kk < KS; ++kk) {
+      floatx8 v = {0, 0, 0, 0, 0, 0, 0, 0};
+      if (row_ok) v = load8(src + 16 * kk);
+      split(v, qh[kk], ql[kk]);
     }
   };
   if (p.g == 1) load_q(0);
@@ -167,14 +190,17 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreParams p) {
     floatx16 acc = {};
     for (int hh = 0; hh < p.g; ++hh) {
       if (p.g != 1) load_q(hh);
-      const float* ksrc = p.kbar + (pooled(hh) + (kc_ok ? kc : 0)) * D + half * HD;
+      const float* ksrc = p.kbar + (pooled(hh) + (kc_ok ? kc : 0)) * D + 8 * half;
+      floatx8 kv[KS];
 #pragma unroll
-      for (int i = 0; i < HD; i += 4) {
-        const floatx4 kv = kc_ok ? *reinterpret_cast<const floatx4*>(ksrc + i) : floatx4{0, 0, 0, 0};
-        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(qa[i], kv[0], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(qa[i + 1], kv[1], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(qa[i + 2], kv[2], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(qa[i + 3], kv[3], acc, 0, 0, 0);
+      for (int kk = 0; kk < KS; ++kk) kv[kk] = kc_ok ? load8(ksrc + 16 * kk) : floatx8{0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) {
+        bf16x8 kh, kl;
+        split(kv[kk], kh, kl);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ql[kk], kh, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qh[kk], kl, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qh[kk], kh, acc, 0, 0, 0);
       }
     }
     // element i of this lane is (row 8*(i/4) + 4*half + i%4, key block t*32 + m32)
