@@ -31,6 +31,12 @@ Stages:
                           tokens and eps -> 0 (masked keys get exactly zero weight)
 9. masked_attention_dense the same Eq. 13 written over a full token mask (tiny
                           shapes), and dense_attention (no mask, [DR] App. A Eq. 16)
+10. token_selection / token_select
+                          the paper's token-level dynamic-threshold mode ([DR] §3.2
+                          Eqs. 9-11 with safeguard (ii), Algorithm 1): fused-head
+                          logits per candidate token pair, z-normalised per frame
+                          pair, decay-state thresholds, top-pair fallback, then the
+                          same (theta_c, theta_m) aggregation to blocks as step 3
 
 Readings where the pages leave a step open are stated at each function.
 """
@@ -43,6 +49,7 @@ from typing import List, Sequence, Tuple
 import numpy as np
 
 EPS_SPLIT = 1e-6      # the epsilon of Eq. 5 (value not given on the pages)
+EPS_NORM = 1e-6       # the epsilon of Eq. 10 (value not given on the pages)
 COUNT_GUARD = 1e-9    # guard in ceil(r * n - guard) against representation error
 
 __all__ = [
@@ -371,3 +378,214 @@ def masked_attention_dense(q, k, v, block_size: int, block_mask: np.ndarray, sca
     with np.errstate(divide="ignore"):
         A = A + np.log(tok)
     return _softmax_rows(A) @ v
+
+
+# ---------------------------------------------------------------------------
+# 10. Token-level dynamic-threshold selection ([DR] §3.2 "Dynamic-threshold
+#     mode", Eqs. 9-11, "Global thresholding with safeguards"; Algorithm 1).
+#     Small shapes only: every token pair's score is materialised.
+# ---------------------------------------------------------------------------
+def decay_length(t: int, tokens_per_frame: int, gamma: float) -> float:
+    """Eq. 2: L(t) = L0 / 2^B(t) * gamma, for t >= 1 (same operation order as
+    distance_table)."""
+    return float(_base_span(tokens_per_frame)) / float(2 ** _group_index(t)) * gamma
+
+
+def _fused(x_heads):
+    return [np.asarray(x, dtype=np.float64) for x in x_heads]
+
+
+def token_scores_block(q_heads, k_heads, rows: slice, cols: slice, scale: float) -> np.ndarray:
+    """Eq. 9 on a sub-matrix: s(u, v) = (1 / H_f) sum_h Q_u^(h) . K_v^(h) * scale
+    for query tokens `rows` and key tokens `cols` (scale = 1 / sqrt(d_k))."""
+    acc = None
+    for qh, kh in zip(q_heads, k_heads):
+        part = (qh[rows] @ kh[cols].T) * scale
+        acc = part if acc is None else acc + part
+    return acc / float(len(q_heads))
+
+
+def token_frame_stats(q_heads, k_heads, num_frames: int, tokens_per_frame: int, block_size: int,
+                      gamma: float, lam: float, tau_near: float, tau_far: float,
+                      eps: float = EPS_NORM, scale: float = None) -> dict:
+    """Per frame pair (i, j) with t = |i - j| > 1 that is retained (Eq. 6):
+    (mu, sigma, tau, fallback) where mu and sigma are the mean and standard
+    deviation of s over P(i, j) (Eqs. 7, 9, 10), tau = tau_near if L(t) >= B_s
+    else tau_far (Eq. 11), and fallback = (u, v) of the highest-scoring pair if
+    no pair reaches tau, else None (safeguard (ii)).
+    Readings: sigma is the population standard deviation (divide by |P|);
+    eps = 1e-6; a tie for the highest score goes to the first pair in (u, v)
+    order."""
+    q_heads, k_heads = _fused(q_heads), _fused(k_heads)
+    scale = 1.0 / math.sqrt(q_heads[0].shape[1]) if scale is None else scale
+    w, sf = distance_table(num_frames, tokens_per_frame, block_size, gamma, lam)
+    Nt = tokens_per_frame
+    u = np.arange(Nt)
+    stats = {}
+    for i in range(num_frames):
+        for j in range(num_frames):
+            t = abs(i - j)
+            if t <= 1 or t % sf[t] != 0:
+                continue
+            P = np.abs(u[:, None] - u[None, :]) <= w[t]
+            sv = token_scores_block(q_heads, k_heads, slice(i * Nt, (i + 1) * Nt), slice(j * Nt, (j + 1) * Nt), scale)
+            vals = sv[P]
+            mu = vals.mean()
+            sigma = math.sqrt(((vals - mu) ** 2).mean())
+            tau = tau_near if decay_length(t, Nt, gamma) >= block_size else tau_far
+            z = (sv - mu) / (sigma + eps)
+            fallback = None
+            if not (P & (z >= tau)).any():
+                masked = np.where(P, sv, -np.inf)
+                fallback = tuple(int(x) for x in np.unravel_index(int(np.argmax(masked)), masked.shape))
+            stats[(i, j)] = (mu, sigma, tau, fallback)
+    return stats
+
+
+def token_selected_rows(q_heads, k_heads, rows: slice, num_frames: int, tokens_per_frame: int,
+                        block_size: int, gamma: float, lam: float, stats: dict,
+                        eps: float = EPS_NORM, scale: float = None) -> np.ndarray:
+    """Selected token pairs [len(rows), S] for the query tokens `rows`
+    (Algorithm 1): for each frame pair, t mod sf(t) != 0 -> none (Eq. 6);
+    t <= 1 -> all of P(i, j) (tau = -inf, Eq. 11; t = 0 is dense attention);
+    otherwise the pairs of P(i, j) with (s - mu) / (sigma + eps) >= tau, or,
+    if no pair of the frame pair reaches tau, its highest-scoring pair."""
+    q_heads, k_heads = _fused(q_heads), _fused(k_heads)
+    scale = 1.0 / math.sqrt(q_heads[0].shape[1]) if scale is None else scale
+    w, sf = distance_table(num_frames, tokens_per_frame, block_size, gamma, lam)
+    Nt = tokens_per_frame
+    S = num_frames * Nt
+    sel = np.zeros((rows.stop - rows.start, S), dtype=bool)
+    qtok = np.arange(rows.start, rows.stop)
+    fq, uq = token_frame_and_index(qtok, Nt)
+    ukey = np.arange(Nt)
+    for i in np.unique(fq):
+        r = np.nonzero(fq == i)[0]
+        for j in range(num_frames):
+            t = abs(int(i) - j)
+            if t % sf[t] != 0:
+                continue
+            P = np.abs(uq[r][:, None] - ukey[None, :]) <= w[t]
+            cols = slice(j * Nt, (j + 1) * Nt)
+            if t <= 1:
+                sel[r, cols] = P
+                continue
+            mu, sigma, tau, fallback = stats[(int(i), j)]
+            if fallback is None:
+                sv = token_scores_block(q_heads, k_heads, slice(rows.start + r[0], rows.start + r[-1] + 1), cols, scale)
+                sel[r, cols] = P & ((sv - mu) / (sigma + eps) >= tau)
+            else:
+                fu, fv = fallback
+                hit = np.nonzero(uq[r] == fu)[0]
+                if len(hit):
+                    sel[r[hit[0]], j * Nt + fv] = True
+    return sel
+
+
+def aggregate_block_rows(sel_rows: np.ndarray, row_start: int, block_size: int, S: int,
+                         theta_c: float = 0.0, theta_m: float = 0.0) -> List[np.ndarray]:
+    """Kept key blocks of the query blocks covered by sel_rows (which starts at
+    the first token of a block) under the density control of [DR] §3.1 (the
+    rule of step 3): a key token of block b is active for query block a iff the
+    fraction of a's valid query tokens paired with it exceeds theta_c; the block
+    pair is kept iff the fraction of b's valid key tokens that are active exceeds
+    theta_m. Reading: the selected pairs of all frame pairs a block pair spans
+    are merged first (Algorithm 1 merges into M_b)."""
+    S_b = -(-S // block_size)
+    out = []
+    n_rows = sel_rows.shape[0]
+    for r0 in range(0, n_rows, block_size):
+        blk = sel_rows[r0:min(r0 + block_size, n_rows)]
+        nq = blk.shape[0]
+        cnt = blk.sum(axis=0)
+        active = (cnt.astype(np.float64) / float(nq)) > theta_c
+        kept = []
+        for b in range(S_b):
+            lo, hi = b * block_size, min((b + 1) * block_size, S)
+            if (active[lo:hi].sum() / float(hi - lo)) > theta_m:
+                kept.append(b)
+        out.append(np.asarray(kept, dtype=np.int64))
+    return out
+
+
+def token_select_rows(q_heads, k_heads, blocks, num_frames: int, tokens_per_frame: int, block_size: int,
+                      gamma: float, lam: float, tau_near: float, tau_far: float, theta_c: float = 0.0,
+                      theta_m: float = 0.0, eps: float = EPS_NORM, scale: float = None, stats: dict = None):
+    """Kept key blocks (ascending) of the given query blocks under the
+    token-level dynamic-threshold mode; one mask serves every head."""
+    S = num_frames * tokens_per_frame
+    if stats is None:
+        stats = token_frame_stats(q_heads, k_heads, num_frames, tokens_per_frame, block_size, gamma, lam,
+                                  tau_near, tau_far, eps, scale)
+    out = []
+    for a in blocks:
+        rows = slice(a * block_size, min((a + 1) * block_size, S))
+        sel = token_selected_rows(q_heads, k_heads, rows, num_frames, tokens_per_frame, block_size, gamma, lam,
+                                  stats, eps, scale)
+        out.append(aggregate_block_rows(sel, rows.start, block_size, S, theta_c, theta_m)[0])
+    return out
+
+
+def token_select(q_heads, k_heads, num_frames: int, tokens_per_frame: int, block_size: int,
+                 gamma: float, lam: float, tau_near: float, tau_far: float, theta_c: float = 0.0,
+                 theta_m: float = 0.0, eps: float = EPS_NORM, scale: float = None) -> List[np.ndarray]:
+    """Kept key blocks of every query block (ascending)."""
+    S_b = -(-(num_frames * tokens_per_frame) // block_size)
+    return token_select_rows(q_heads, k_heads, range(S_b), num_frames, tokens_per_frame, block_size, gamma, lam,
+                             tau_near, tau_far, theta_c, theta_m, eps, scale)
+
+
+def token_select_decisive(q_heads, k_heads, blocks, num_frames: int, tokens_per_frame: int, block_size: int,
+                          gamma: float, lam: float, tau_near: float, tau_far: float, margin: float,
+                          eps: float = EPS_NORM, scale: float = None, stats: dict = None) -> List[np.ndarray]:
+    """For each given query block, a bool per key block: True where no
+    token-level decision of the block pair can flip under a perturbation of
+    every z below `margin` and of every score below `margin` * sigma. Unsure
+    are pairs of P (t > 1) within `margin` of their threshold, and every pair of
+    a frame pair whose fallback is in doubt (its highest z within `margin` of
+    tau, or a runner-up score within `margin` * sigma of the highest)."""
+    q_heads, k_heads = _fused(q_heads), _fused(k_heads)
+    scale = 1.0 / math.sqrt(q_heads[0].shape[1]) if scale is None else scale
+    if stats is None:
+        stats = token_frame_stats(q_heads, k_heads, num_frames, tokens_per_frame, block_size, gamma, lam,
+                                  tau_near, tau_far, eps, scale)
+    w, sf = distance_table(num_frames, tokens_per_frame, block_size, gamma, lam)
+    Nt = tokens_per_frame
+    S = num_frames * Nt
+    S_b = -(-S // block_size)
+    ukey = np.arange(Nt)
+    doubtful = {}
+    for (i, j), (mu, sigma, tau, fb) in stats.items():
+        t = abs(i - j)
+        P = np.abs(ukey[:, None] - ukey[None, :]) <= w[t]
+        sv = token_scores_block(q_heads, k_heads, slice(i * Nt, (i + 1) * Nt), slice(j * Nt, (j + 1) * Nt), scale)
+        top = np.sort(sv[P])[::-1]
+        zmax = (top[0] - mu) / (sigma + eps)
+        doubtful[(i, j)] = abs(zmax - tau) <= margin or (
+            zmax < tau and len(top) > 1 and top[0] - top[1] <= margin * (sigma + eps))
+    out = []
+    for a in blocks:
+        rows = slice(a * block_size, min((a + 1) * block_size, S))
+        qtok = np.arange(rows.start, rows.stop)
+        fq, uq = token_frame_and_index(qtok, Nt)
+        unsure = np.zeros((len(qtok), S), dtype=bool)
+        for i in np.unique(fq):
+            r = np.nonzero(fq == i)[0]
+            for j in range(num_frames):
+                st = stats.get((int(i), j))
+                if st is None:
+                    continue
+                mu, sigma, tau, fb = st
+                t = abs(int(i) - j)
+                P = np.abs(uq[r][:, None] - ukey[None, :]) <= w[t]
+                cols = slice(j * Nt, (j + 1) * Nt)
+                if doubtful[(int(i), j)]:
+                    unsure[r, cols] = P
+                    continue
+                sv = token_scores_block(q_heads, k_heads, slice(rows.start + r[0], rows.start + r[-1] + 1), cols, scale)
+                unsure[r, cols] = P & (np.abs((sv - mu) / (sigma + eps) - tau) <= margin)
+        dec = np.ones(S_b, dtype=bool)
+        for b in range(S_b):
+            dec[b] = not unsure[:, b * block_size:min((b + 1) * block_size, S)].any()
+        out.append(dec)
+    return out
