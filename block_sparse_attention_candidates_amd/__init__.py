@@ -142,6 +142,31 @@ def score_select(q, k, cand: Candidates, mode: str = "static", ratio: float = 1.
     return Kept(kept_col, kept_cnt, scores)
 
 
+def token_select(q, k, cand: Candidates, tau_near: float, tau_far: float, fused_heads: int = 2,
+                 eps: float = 1e-6, workspace=None) -> Kept:
+    """The paper's token-level dynamic-threshold selection (dr_token_select):
+    one mask per batch element from heads 0..fused_heads-1, written for every head."""
+    torch = _torch()
+    shape = _check_qkv(q, k)
+    if shape[2] != cand.cfg.num_frames * cand.cfg.tokens_per_frame:
+        raise ValueError("sequence length does not match the candidate configuration")
+    dims = _dims(shape)
+    tok = _L.TokenCfg(int(fused_heads), 0, float(tau_near), float(tau_far), float(eps))
+    B, H = int(shape[0]), int(shape[1])
+    ws_bytes = ctypes.c_size_t(0)
+    check(lib().dr_token_select_workspace(ctypes.byref(dims), ctypes.byref(cand.cfg), ctypes.byref(tok),
+                                          cand.nnz, ctypes.byref(ws_bytes)))
+    if workspace is None or workspace.numel() < ws_bytes.value:
+        workspace = torch.empty(ws_bytes.value, dtype=torch.uint8, device=q.device)
+    kept_col = torch.empty(B * H * cand.nnz, dtype=torch.int32, device=q.device)
+    kept_cnt = torch.empty(B * H * cand.num_blocks, dtype=torch.int32, device=q.device)
+    check(lib().dr_token_select(ctypes.byref(dims), ctypes.byref(cand.cfg), ctypes.byref(tok), q.data_ptr(),
+                                k.data_ptr(), cand.row_ptr.data_ptr(), cand.cols.data_ptr(), cand.nnz,
+                                kept_col.data_ptr(), kept_cnt.data_ptr(), workspace.data_ptr(), workspace.numel(),
+                                _stream(q.device)))
+    return Kept(kept_col, kept_cnt)
+
+
 def sparse_attn(q, k, v, cand: Candidates, kept: Kept, softmax_scale: Optional[float] = None, out=None):
     torch = _torch()
     shape = _check_qkv(q, k, v)

@@ -32,6 +32,11 @@ class SelectCfg(ctypes.Structure):
                 ("ratio", ctypes.c_double), ("tau", ctypes.c_double)]
 
 
+class TokenCfg(ctypes.Structure):
+    _fields_ = [("fused_heads", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("tau_near", ctypes.c_double), ("tau_far", ctypes.c_double), ("eps", ctypes.c_double)]
+
+
 class DynradError(RuntimeError):
     def __init__(self, status: int, detail: str):
         super().__init__(f"dynrad status {status}: {detail}")
@@ -60,6 +65,9 @@ def lib() -> ctypes.CDLL:
         "dr_score_select": (c_int32, [P(Dims), P(RadialCfg), P(SelectCfg), c_void_p, c_void_p, c_void_p,
                                       c_void_p, c_int64, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
                                       c_void_p]),
+        "dr_token_select_workspace": (c_int32, [P(Dims), P(RadialCfg), P(TokenCfg), c_int64, P(c_size_t)]),
+        "dr_token_select": (c_int32, [P(Dims), P(RadialCfg), P(TokenCfg), c_void_p, c_void_p, c_void_p, c_void_p,
+                                      c_int64, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
         "dr_sparse_attn": (c_int32, [P(Dims), P(RadialCfg), c_void_p, c_void_p, c_void_p, c_void_p, c_int64,
                                      c_void_p, c_void_p, c_float, c_void_p, c_void_p]),
         "dr_attn": (c_int32, [P(Dims), c_int32, c_void_p, c_void_p, c_void_p, c_float, c_void_p, c_void_p]),

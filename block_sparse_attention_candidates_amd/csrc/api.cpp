@@ -119,6 +119,53 @@ WsLayout ws_layout(const dr_dims* d, int Sb, const dr_select_cfg* s, long long n
   return w;
 }
 
+struct TokWs {
+  size_t part, thr, fmax, fn, served, flags, total;
+  int n_wg, FR;
+};
+
+TokWs tok_ws(const dr_dims* d, const dr_radial_cfg* c, int Sb, long long S, long long nnz) {
+  TokWs w;
+  const int Nf = c->num_frames;
+  w.n_wg = (int)((S + 255) / 256);
+  w.FR = 255 / c->tokens_per_frame + 2;
+  const size_t fpairs = (size_t)d->batch * Nf * Nf;
+  size_t off = 0;
+  w.part = off;
+  off = align256(off + (size_t)d->batch * w.n_wg * w.FR * Nf * sizeof(dr::TokStat));
+  w.thr = off;
+  off = align256(off + fpairs * sizeof(float));
+  w.fmax = off;
+  off = align256(off + fpairs * sizeof(unsigned long long));
+  w.fn = off;
+  off = align256(off + fpairs * sizeof(double));
+  w.served = off;
+  off = align256(off + fpairs * sizeof(int));
+  w.flags = off;
+  off = align256(off + (size_t)d->batch * nnz);
+  w.total = off;
+  (void)Sb;
+  return w;
+}
+
+dr_status check_token(const dr_token_cfg* t, const dr_dims* d, const dr_radial_cfg* c, int Sb) {
+  if (!t) return fail(DR_ERR_INVALID_ARG, "token config is NULL");
+  if (t->reserved != 0) return fail(DR_ERR_INVALID_ARG, "token config reserved field must be 0");
+  if (t->fused_heads < 1 || t->fused_heads > d->heads)
+    return fail(DR_ERR_INVALID_ARG, "fused_heads %d outside [1, heads]", t->fused_heads);
+  if (t->fused_heads > 2) return fail(DR_ERR_UNSUPPORTED, "fused_heads %d not built (1 or 2)", t->fused_heads);
+  if (isnan(t->tau_near) || isnan(t->tau_far)) return fail(DR_ERR_INVALID_ARG, "tau_near / tau_far is NaN");
+  if (!finite(t->eps) || t->eps <= 0.0) return fail(DR_ERR_INVALID_ARG, "eps must be finite and > 0");
+  if (c->tokens_per_frame < 32 || c->tokens_per_frame > 65535)
+    return fail(DR_ERR_UNSUPPORTED, "token-level selection needs tokens_per_frame in [32, 65535]");
+  if (c->num_frames > dr::kMaxTokenFrames)
+    return fail(DR_ERR_UNSUPPORTED, "token-level selection needs num_frames <= %d", dr::kMaxTokenFrames);
+  const size_t lds = dr::token_lds_bytes(d->head_dim, c->block_size, t->fused_heads, Sb, c->num_frames,
+                                         255 / c->tokens_per_frame + 2);
+  if (lds > 160 * 1024) return fail(DR_ERR_UNSUPPORTED, "token-level selection needs %zu bytes of LDS", lds);
+  return DR_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -277,6 +324,71 @@ static dr_status attn_common(const dr_dims* dims, long long S, const void* q, co
   p->n_tiles = (int)((S + 255) / 256);
   p->scale_log2 = scale * 1.4426950408889634f;
   return DR_OK;
+}
+
+dr_status dr_token_select_workspace(const dr_dims* dims, const dr_radial_cfg* cfg, const dr_token_cfg* tok,
+                                    int64_t nnz, size_t* bytes) {
+  Layout L;
+  dr_status st = check_radial(cfg, &L);
+  if (st != DR_OK) return st;
+  if ((st = check_dims(dims)) != DR_OK) return st;
+  if ((st = check_token(tok, dims, cfg, L.Sb)) != DR_OK) return st;
+  if ((st = check_nnz(nnz, L.Sb, dims)) != DR_OK) return st;
+  if (!bytes) return fail(DR_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = tok_ws(dims, cfg, L.Sb, L.S, nnz).total;
+  return ok();
+}
+
+dr_status dr_token_select(const dr_dims* dims, const dr_radial_cfg* cfg, const dr_token_cfg* tok, const void* q,
+                          const void* k, const int32_t* row_ptr, const int32_t* cols, int64_t nnz,
+                          int32_t* kept_col, int32_t* kept_cnt, void* ws, size_t ws_bytes, hipStream_t stream) {
+  Layout L;
+  dr_status st = check_radial(cfg, &L);
+  if (st != DR_OK) return st;
+  if ((st = check_dims(dims)) != DR_OK) return st;
+  if ((st = check_token(tok, dims, cfg, L.Sb)) != DR_OK) return st;
+  if ((st = check_nnz(nnz, L.Sb, dims)) != DR_OK) return st;
+  if (!q || !k || !row_ptr || !cols || !kept_col || !kept_cnt || !ws)
+    return fail(DR_ERR_INVALID_ARG, "q, k, row_ptr, cols, kept_col, kept_cnt and ws must be non-NULL");
+  const TokWs w = tok_ws(dims, cfg, L.Sb, L.S, nnz);
+  if (ws_bytes < w.total)
+    return fail(DR_ERR_CAPACITY, "workspace of %zu bytes below the %zu required", ws_bytes, w.total);
+  unsigned char* wsb = static_cast<unsigned char*>(ws);
+  dr::TokParams p;
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.row_ptr = row_ptr;
+  p.cols = cols;
+  p.kept_col = kept_col;
+  p.kept_cnt = kept_cnt;
+  p.nnz = nnz;
+  p.H = dims->heads;
+  p.S = (int)L.S;
+  p.Sb = L.Sb;
+  p.Nf = cfg->num_frames;
+  p.Nt = cfg->tokens_per_frame;
+  p.Bs = cfg->block_size;
+  p.L0 = dr::base_span(p.Nt);
+  p.n_wg = w.n_wg;
+  p.FR = w.FR;
+  p.gamma = cfg->gamma;
+  p.lambda = cfg->lambda;
+  p.theta_c = cfg->theta_c;
+  p.theta_m = cfg->theta_m;
+  p.tau_near = tok->tau_near;
+  p.tau_far = tok->tau_far;
+  p.eps = tok->eps;
+  p.scale = (float)(1.0 / (sqrt((double)dims->head_dim) * (double)tok->fused_heads));
+  p.part = reinterpret_cast<dr::TokStat*>(wsb + w.part);
+  p.thr = reinterpret_cast<float*>(wsb + w.thr);
+  p.fmax = reinterpret_cast<unsigned long long*>(wsb + w.fmax);
+  p.fn = reinterpret_cast<double*>(wsb + w.fn);
+  p.served = reinterpret_cast<int*>(wsb + w.served);
+  p.flags = wsb + w.flags;
+  const hipError_t e = dr::launch_token_select(p, dims->batch, dims->head_dim, cfg->block_size, tok->fused_heads,
+                                               stream);
+  if (e != hipSuccess) return hip_fail(e, "token selection kernels");
+  return ok();
 }
 
 dr_status dr_sparse_attn(const dr_dims* dims, const dr_radial_cfg* cfg, const void* q, const void* k,

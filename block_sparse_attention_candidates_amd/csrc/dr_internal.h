@@ -104,6 +104,41 @@ struct AttnParams {
   float scale_log2;   // softmax_scale * log2(e)
 };
 
+// Token-level dynamic-threshold selection ([DR] §3.2 Eqs. 9-11).
+constexpr int kMaxTokenFrames = 64;  // N_f limit of the token-level mode (LDS statistics)
+
+// Statistics of a set of scores: count, mean, sum of squared deviations, and
+// the highest score packed with its position ((order key << 32) | ~position).
+struct TokStat {
+  double n, mean, m2;
+  unsigned long long mx;
+};
+
+struct TokParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const int32_t* row_ptr;
+  const int32_t* cols;
+  int32_t* kept_col;
+  int32_t* kept_cnt;
+  long long nnz;
+  int H, S, Sb, Nf, Nt, Bs, L0;
+  int n_wg;            // workgroups per batch element (256 query tokens each)
+  int FR;              // query frames a workgroup can span
+  double gamma, lambda, theta_c, theta_m, tau_near, tau_far, eps;
+  float scale;         // 1 / (sqrt(d_k) * H_f)
+  // workspace
+  TokStat* part;       // [B][n_wg][FR][Nf] workgroup partials
+  float* thr;          // [B][Nf][Nf] threshold in score units (+inf: no t > 1 pair)
+  unsigned long long* fmax;  // [B][Nf][Nf] highest score and position
+  double* fn;          // [B][Nf][Nf] size of P(i, j) for t > 1 (0: none)
+  int* served;         // [B][Nf][Nf] 1 if some t > 1 pair is selected
+  unsigned char* flags;  // [B][nnz] block decision per candidate entry
+};
+
+size_t token_lds_bytes(int D, int Bs, int Hf, int Sb, int Nf, int FR);
+hipError_t launch_token_select(const TokParams& p, int B, int D, int Bs, int Hf, hipStream_t stream);
+
 hipError_t launch_candidates(const CandParams& p, int32_t* row_ptr, int32_t* cols, long long cap,
                              hipStream_t stream);
 hipError_t launch_pool(const PoolParams& p, hipStream_t stream);

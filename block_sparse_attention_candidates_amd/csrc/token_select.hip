@@ -1,0 +1,806 @@
+// Token-level dynamic-threshold selection on gfx950 ([DR] §3.2
+// "Dynamic-threshold mode", Eqs. 9-11, "Global thresholding with safeguards",
+// Algorithm 1; aggregation by "Density control within blocks", §3.1).
+// [DR] = "DynamicRad: Content-Adaptive Sparse Attention for Long Video
+// Diffusion", arXiv 2604.20470.
+//
+// One mask per batch element, shared by every head. Four launches:
+//   stats:    a workgroup of 8 wavefronts owns 256 query tokens (8 / 4 query
+//             blocks); it walks the union of their candidate key blocks in
+//             ascending order, staging each key block of the H_f fused heads in
+//             LDS (double-buffered, XOR-swizzled rows), and every wave whose
+//             query block has the key block as a candidate computes its 32x32
+//             token tiles of s = (1/H_f) sum_h Q^h K^h^T / sqrt(d_k) (Eq. 9) with
+//             v_mfma_f32_32x32x16_bf16. Token pairs of P(i, j) with t > 1 feed
+//             per-frame-pair statistics (count, mean, M2 merged with Chan's
+//             formula in float64, and the highest score with its position);
+//             each wave keeps its own LDS accumulators, merged in a fixed order
+//             into one partial per workgroup: no floating-point atomics.
+//   reduce:   per frame pair, the workgroup partials merged in workgroup order:
+//             mu, sigma (population), tau(t) by decay state (Eq. 11), and the
+//             threshold in score units thr = mu + tau * (sigma + eps) (Eq. 10
+//             rearranged), rounded up to float so that s >= thr in float32 is
+//             exactly (double) s >= mu + tau * (sigma + eps).
+//   mark:     the same walk and tiles; a pair is selected iff it is a
+//             candidate pair (Eqs. 6-7) and t <= 1 (tau = -inf) or s >= thr.
+//             Per block pair, key tokens are active iff their selected share
+//             of the query tokens exceeds theta_c, and the block pair is kept
+//             iff the active share of the key tokens exceeds theta_m; one flag
+//             per candidate entry. A frame pair with a selected t > 1 pair is
+//             marked as served.
+//   fallback: for each unserved frame pair (safeguard (ii)), the block pair
+//             holding its highest-scoring pair is re-decided with that pair
+//             added, by the same tile and selection code.
+//   compact:  one wavefront per (b, query block): flags -> ascending kept list,
+//             written for every head.
+#include "dr_internal.h"
+
+namespace dr {
+namespace {
+
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kWaves = 8;
+constexpr int kThreads = kWaves * 64;
+constexpr int kRows = kWaves * 32;      // query tokens per workgroup
+
+__device__ inline int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// order-preserving unsigned key of a float
+__device__ inline unsigned int fkey(float s) {
+  unsigned int u = __float_as_uint(s);
+  if (u == 0x80000000u) u = 0;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ inline unsigned long long pack_max(float s, unsigned int loc) {
+  return ((unsigned long long)fkey(s) << 32) | (unsigned long long)(0xffffffffu - loc);
+}
+
+// XOR swizzle of 16-byte chunks within a staged key row (same layout argument
+// as the attention kernel: 16 lanes read 16 rows at one logical chunk)
+template <int D>
+__device__ inline int swz(int key) { return D == 128 ? (key & 15) : ((key >> 1) & 7); }
+
+using Stat = TokStat;
+
+// Chan et al.'s pairwise update: merge (nb, mb, m2b) into a.
+__device__ inline void merge(Stat& a, double nb, double mb, double m2b, unsigned long long mxb) {
+  if (mxb > a.mx) a.mx = mxb;
+  if (nb == 0.0) return;
+  if (a.n == 0.0) {
+    a.n = nb;
+    a.mean = mb;
+    a.m2 = m2b;
+    return;
+  }
+  const double n = a.n + nb;
+  const double d = mb - a.mean;
+  a.mean += d * (nb / n);
+  a.m2 += m2b + d * d * (a.n * nb / n);
+  a.n = n;
+}
+
+__device__ inline double wave_sum(double v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+  return v;
+}
+__device__ inline unsigned long long wave_max(unsigned long long v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    const unsigned long long o = __shfl_xor(v, off);
+    v = o > v ? o : v;
+  }
+  return v;
+}
+
+template <int D, int BS, int HF>
+struct Geo {
+  static constexpr int RB = 2 * D;                  // bytes per staged key row
+  static constexpr int KBUF = HF * BS * RB;         // one key block, all fused heads
+  static constexpr int QB = kRows / BS;             // query blocks per workgroup
+  static constexpr int WPQ = BS / 32;               // waves per query block
+};
+
+// Fused-head logits of one 32x32 token tile: A = this wave's Q rows (registers),
+// B = 32 staged keys (key sub-block ksub of the staged block). Lane l gets key
+// column l%32 and query rows 8*(i/4) + 4*(l/32) + i%4.
+template <int D, int BS, int HF>
+__device__ inline floatx16 tile_scores(const bf16x8 (&qf)[HF][D / 16], const unsigned char* kbuf, int ksub,
+                                       int lane) {
+  using G = Geo<D, BS, HF>;
+  floatx16 acc = {};
+  const int key = 32 * ksub + (lane & 31), half = lane >> 5;
+#pragma unroll
+  for (int h = 0; h < HF; ++h) {
+    const unsigned char* row = kbuf + (h * BS + key) * G::RB;
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      const int ch = (2 * kk + half) ^ swz<D>(key);
+      const bf16x8 kb = *reinterpret_cast<const bf16x8*>(row + ch * 16);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[h][kk], kb, acc, 0, 0, 0);
+    }
+  }
+  return acc;
+}
+
+// The Q fragments of 32 query rows starting at token q0 (rows >= S are zero).
+template <int D, int HF>
+__device__ inline void load_q(const TokParams& p, int b, int q0, int lane, bf16x8 (&qf)[HF][D / 16]) {
+  const int r = q0 + (lane & 31), half = lane >> 5;
+#pragma unroll
+  for (int h = 0; h < HF; ++h) {
+    const uint16_t* src = p.q + ((size_t)(b * p.H + h) * p.S + (size_t)(r < p.S ? r : 0)) * D;
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      u32x4 w = {0, 0, 0, 0};
+      if (r < p.S) w = *reinterpret_cast<const u32x4*>(src + 16 * kk + 8 * half);
+      qf[h][kk] = __builtin_bit_cast(bf16x8, w);
+    }
+  }
+}
+
+// Stage key block kb of batch b (all fused heads) into an LDS buffer; keys >= S
+// are zero. Cooperative over the workgroup: returns the 16-byte chunks this
+// thread carries so that the loads can be issued ahead of the stores.
+template <int D, int BS, int HF>
+struct Stager {
+  using G = Geo<D, BS, HF>;
+  static constexpr int CHUNKS = HF * BS * (D / 8);
+  static constexpr int PER = (CHUNKS + kThreads - 1) / kThreads;
+  u32x4 v[PER];
+  __device__ inline void load(const TokParams& p, int b, int kb, int tid) {
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int c = tid + j * kThreads;
+      v[j] = u32x4{0, 0, 0, 0};
+      if (c < CHUNKS && kb >= 0) {
+        const int h = c / (BS * (D / 8));
+        const int rem = c - h * (BS * (D / 8));
+        const int key = rem / (D / 8), ch = rem - key * (D / 8);
+        const int tok = kb * BS + key;
+        if (tok < p.S)
+          v[j] = *reinterpret_cast<const u32x4*>(p.k + ((size_t)(b * p.H + h) * p.S + tok) * D + ch * 8);
+      }
+    }
+  }
+  __device__ inline void store(unsigned char* buf, int tid) const {
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int c = tid + j * kThreads;
+      if (c < CHUNKS) {
+        const int h = c / (BS * (D / 8));
+        const int rem = c - h * (BS * (D / 8));
+        const int key = rem / (D / 8), ch = rem - key * (D / 8);
+        *reinterpret_cast<u32x4*>(buf + (h * BS + key) * G::RB + ((ch ^ swz<D>(key)) << 4)) = v[j];
+      }
+    }
+  }
+};
+
+// Per-lane view of one tile's token pairs: the lane's key token and, for its
+// 16 query rows, which of the (at most two) query frames each row lies in.
+struct TileFrames {
+  int f0;        // frame of the wave's first query row
+  int u0;        // its spatial index
+  int fk, uk;    // this lane's key token frame and spatial index
+  bool kvalid;
+};
+
+__device__ inline TileFrames tile_frames(const TokParams& p, int q0, int ktok) {
+  TileFrames f;
+  f.f0 = q0 / p.Nt;
+  f.u0 = q0 - f.f0 * p.Nt;
+  f.kvalid = ktok < p.S;
+  f.fk = ktok / p.Nt;
+  f.uk = ktok - f.fk * p.Nt;
+  return f;
+}
+
+// Row i of the lane: query token q0 + r, r = 8*(i/4) + 4*half + i%4.
+__device__ inline int row_of(int i, int half) { return 8 * (i >> 2) + 4 * half + (i & 3); }
+
+// Selection bits (one per element i) of a tile under the thresholds of the
+// frame pairs involved; inP bits mark the candidate pairs of P with t > 1.
+// thr0 / thr1: thresholds (score units) for query frame f0 / f0 + 1 against
+// the lane's key frame. w/sf: per-distance table in LDS.
+__device__ inline void select_bits(const TokParams& p, const floatx16& acc, const TileFrames& f, int q0, int half,
+                                   const int* s_w, const int* s_sf, float thr0, float thr1, unsigned& sel,
+                                   unsigned& inP2) {
+  sel = 0;
+  inP2 = 0;
+  if (!f.kvalid) return;
+  const int t0 = f.f0 > f.fk ? f.f0 - f.fk : f.fk - f.f0;
+  const int t1 = f.f0 + 1 > f.fk ? f.f0 + 1 - f.fk : f.fk - f.f0 - 1;
+  const bool ret0 = t0 < p.Nf && (t0 % s_sf[t0]) == 0;
+  const bool ret1 = t1 < p.Nf && (t1 % s_sf[t1]) == 0;
+  const int w0 = t0 < p.Nf ? s_w[t0] : 0, w1 = t1 < p.Nf ? s_w[t1] : 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int r = row_of(i, half);
+    if (q0 + r >= p.S) continue;
+    int u = f.u0 + r;
+    const bool second = u >= p.Nt;
+    if (second) u -= p.Nt;
+    const int t = second ? t1 : t0;
+    const bool ret = second ? ret1 : ret0;
+    const int w = second ? w1 : w0;
+    const int du = u > f.uk ? u - f.uk : f.uk - u;
+    if (!ret || du > w) continue;
+    if (t <= 1) {
+      sel |= 1u << i;
+    } else {
+      inP2 |= 1u << i;
+      if (acc[i] * p.scale >= (second ? thr1 : thr0)) sel |= 1u << i;
+    }
+  }
+}
+
+struct WalkState {
+  int cur_wi, cur_step;
+  unsigned int cur_bits;
+};
+
+// Union step j -> key block (j increasing across calls).
+__device__ inline int block_of_step(const unsigned int* uword, WalkState& s, int j) {
+  while (true) {
+    const int n = __popc(s.cur_bits);
+    if (j < s.cur_step + n) {
+      unsigned int m = s.cur_bits;
+      for (int t = s.cur_step; t < j; ++t) m &= m - 1;
+      return s.cur_wi * 32 + __ffs(m) - 1;
+    }
+    s.cur_step += n;
+    ++s.cur_wi;
+    s.cur_bits = uword[s.cur_wi];
+  }
+}
+
+// LDS layout shared by the stats and mark kernels: key staging (2 buffers),
+// per-query-block candidate bitmaps and their CSR word prefixes, the union
+// bitmap, and the per-distance table; then kernel-specific areas.
+template <int D, int BS, int HF>
+struct Lds {
+  using G = Geo<D, BS, HF>;
+  int nword;
+  unsigned char* kbuf[2];
+  unsigned int* bits;   // [QB][nword]
+  int* pre;             // [QB][nword]
+  unsigned int* uword;  // [nword]
+  int* s_w;             // [Nf]
+  int* s_sf;            // [Nf]
+  unsigned char* rest;  // 16-byte aligned
+  __host__ __device__ static size_t align16(size_t x) { return (x + 15) & ~(size_t)15; }
+  __device__ Lds(unsigned char* smem, int Sb, int Nf) {
+    nword = (Sb + 31) >> 5;
+    kbuf[0] = smem;
+    kbuf[1] = smem + G::KBUF;
+    bits = reinterpret_cast<unsigned int*>(smem + 2 * G::KBUF);
+    pre = reinterpret_cast<int*>(bits + G::QB * nword);
+    uword = reinterpret_cast<unsigned int*>(pre + G::QB * nword);
+    s_w = reinterpret_cast<int*>(uword + nword);
+    s_sf = s_w + Nf;
+    const size_t used = (size_t)(reinterpret_cast<unsigned char*>(s_sf + Nf) - smem);
+    rest = smem + align16(used);
+  }
+  __host__ __device__ static size_t bytes(int Sb, int Nf) {
+    const size_t nw = (size_t)(Sb + 31) / 32;
+    const size_t used = 2 * (size_t)G::KBUF + (size_t)G::QB * nw * 8 + nw * 4 + (size_t)Nf * 8;
+    return (used + 15) & ~(size_t)15;
+  }
+};
+
+// Setup shared by the stats and mark kernels: the per-distance table, the
+// candidate bitmaps of the workgroup's query blocks with their CSR word
+// prefixes, and the union bitmap. Returns the number of union steps.
+template <int D, int BS, int HF>
+__device__ int setup(const TokParams& p, Lds<D, BS, HF>& L, int a0, int* s_nsteps) {
+  using G = Geo<D, BS, HF>;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int t = tid; t < p.Nf; t += kThreads) {
+    int w, sf;
+    table_entry(t, p.Nt, BS, p.L0, p.gamma, p.lambda, &w, &sf);
+    L.s_w[t] = w < p.Nt ? w : p.Nt;
+    L.s_sf[t] = sf;
+  }
+  for (int i = tid; i < G::QB * L.nword; i += kThreads) L.bits[i] = 0;
+  __syncthreads();
+  for (int qb = wave; qb < G::QB; qb += kWaves) {
+    const int a = a0 + qb;
+    if (a >= p.Sb) continue;
+    const int e1 = p.row_ptr[a + 1];
+    for (int e = p.row_ptr[a] + lane; e < e1; e += 64) {
+      const int c = p.cols[e];
+      atomicOr(&L.bits[qb * L.nword + (c >> 5)], 1u << (c & 31));
+    }
+  }
+  __syncthreads();
+  for (int wi = tid; wi < L.nword; wi += kThreads) {
+    unsigned int u = 0;
+    for (int s = 0; s < G::QB; ++s) u |= L.bits[s * L.nword + wi];
+    L.uword[wi] = u;
+  }
+  // per query block: exclusive popcount prefix over its words (CSR positions)
+  for (int qb = wave; qb < G::QB; qb += kWaves) {
+    int run = 0;
+    for (int w0 = 0; w0 < L.nword; w0 += 64) {
+      const int wi = w0 + lane;
+      const int c = wi < L.nword ? __popc(L.bits[qb * L.nword + wi]) : 0;
+      int incl = c;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int o = __shfl_up(incl, off);
+        if (lane >= off) incl += o;
+      }
+      if (wi < L.nword) L.pre[qb * L.nword + wi] = run + incl - c;
+      run += __shfl(incl, 63);
+    }
+  }
+  __syncthreads();
+  if (wave == 0) {
+    int tot = 0;
+    for (int w0 = 0; w0 < L.nword; w0 += 64) {
+      const int wi = w0 + lane;
+      int c = wi < L.nword ? __popc(L.uword[wi]) : 0;
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) c += __shfl_xor(c, off);
+      tot += c;
+    }
+    if (lane == 0) *s_nsteps = tot;
+  }
+  __syncthreads();
+  return *s_nsteps;
+}
+
+// ---------------------------------------------------------------------------
+// Pass 1: per-frame-pair statistics of the t > 1 candidate pairs.
+// ---------------------------------------------------------------------------
+template <int D, int BS, int HF>
+__global__ __launch_bounds__(kThreads) void stats_kernel(TokParams p) {
+  using G = Geo<D, BS, HF>;
+  extern __shared__ __align__(16) unsigned char smem[];
+  __shared__ int s_nsteps;
+  Lds<D, BS, HF> L(smem, p.Sb, p.Nf);
+  Stat* acc_l = reinterpret_cast<Stat*>(L.rest);     // [kWaves][2][Nf]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5;
+  const int wg = blockIdx.x, b = blockIdx.y;
+  const int a0 = wg * G::QB;
+  for (int i = tid; i < kWaves * 2 * p.Nf; i += kThreads) acc_l[i] = Stat{0.0, 0.0, 0.0, 0ull};
+  const int nsteps = setup<D, BS, HF>(p, L, a0, &s_nsteps);
+
+  const int qb = wave / G::WPQ, sub = wave - qb * G::WPQ;
+  const int a = a0 + qb;
+  const int q0 = a * BS + 32 * sub;
+  const bool active_wave = a < p.Sb && q0 < p.S;
+  bf16x8 qf[HF][D / 16];
+  if (active_wave) load_q<D, HF>(p, b, q0, lane, qf);
+  const int f0w = q0 / p.Nt;
+  Stat* mine = acc_l + wave * 2 * p.Nf;
+
+  WalkState ws{0, 0, L.uword[0]};
+  Stager<D, BS, HF> st;
+  if (nsteps > 0) {
+    st.load(p, b, block_of_step(L.uword, ws, 0), tid);
+    st.store(L.kbuf[0], tid);
+  }
+  __syncthreads();
+  for (int j = 0; j < nsteps; ++j) {
+    const int kb = uniform(block_of_step(L.uword, ws, j));
+    int kb_next = -1;
+    if (j + 1 < nsteps) {
+      WalkState w2 = ws;
+      kb_next = uniform(block_of_step(L.uword, w2, j + 1));
+    }
+    st.load(p, b, kb_next, tid);
+    const unsigned char* kbuf = L.kbuf[j & 1];
+    const bool need = active_wave && ((L.bits[qb * L.nword + (kb >> 5)] >> (kb & 31)) & 1u);
+    if (need) {
+#pragma unroll
+      for (int ksub = 0; ksub < BS / 32; ++ksub) {
+        const int ktok0 = kb * BS + 32 * ksub;
+        if (ktok0 >= p.S) break;
+        const floatx16 acc = tile_scores<D, BS, HF>(qf, kbuf, ksub, lane);
+        const TileFrames f = tile_frames(p, q0, ktok0 + (lane & 31));
+        // t > 1 candidate pairs of P, split by (query frame f0w + fo, key frame fk0 + ko)
+        const int fk0 = ktok0 / p.Nt;
+        const int t0 = f.f0 > f.fk ? f.f0 - f.fk : f.fk - f.f0;
+        const int t1 = f.f0 + 1 > f.fk ? f.f0 + 1 - f.fk : f.fk - f.f0 - 1;
+        const bool ok0 = f.kvalid && t0 > 1 && t0 < p.Nf && (t0 % L.s_sf[t0]) == 0;
+        const bool ok1 = f.kvalid && t1 > 1 && t1 < p.Nf && (t1 % L.s_sf[t1]) == 0;
+        const int w0 = t0 < p.Nf ? L.s_w[t0] : 0, w1 = t1 < p.Nf ? L.s_w[t1] : 0;
+        float sv[16];
+        unsigned slot_bits[2] = {0u, 0u};   // element bits in P, per query frame
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          sv[i] = acc[i] * p.scale;
+          const int r = row_of(i, half);
+          if (q0 + r >= p.S) continue;
+          int u = f.u0 + r;
+          const bool second = u >= p.Nt;
+          if (second) u -= p.Nt;
+          const int du = u > f.uk ? u - f.uk : f.uk - u;
+          if (second ? (ok1 && du <= w1) : (ok0 && du <= w0)) slot_bits[second ? 1 : 0] |= 1u << i;
+        }
+        const int ko = f.fk - fk0;   // 0 or 1 (32 keys span at most two frames)
+#pragma unroll
+        for (int fo = 0; fo < 2; ++fo) {
+#pragma unroll
+          for (int kslot = 0; kslot < 2; ++kslot) {
+            const unsigned bitsm = ko == kslot ? slot_bits[fo] : 0u;
+            if (__ballot(bitsm != 0u) == 0ull) continue;
+            double n = (double)__popc(bitsm), s = 0.0;
+            unsigned long long mx = 0ull;
+            const int fq = f.f0 + fo;
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+              if ((bitsm >> i) & 1u) {
+                s += (double)sv[i];
+                int u = f.u0 + row_of(i, half) - fo * p.Nt;
+                const unsigned long long key = pack_max(sv[i], (unsigned)(u * p.Nt + f.uk));
+                mx = key > mx ? key : mx;
+              }
+            const double ntot = wave_sum(n);
+            const double mean = wave_sum(s) / ntot;
+            double m2 = 0.0;
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+              if ((bitsm >> i) & 1u) {
+                const double d = (double)sv[i] - mean;
+                m2 += d * d;
+              }
+            m2 = wave_sum(m2);
+            mx = wave_max(mx);
+            if (lane == 0) merge(mine[(fq - f0w) * p.Nf + fk0 + kslot], ntot, mean, m2, mx);
+          }
+        }
+      }
+    }
+    st.store(L.kbuf[(j + 1) & 1], tid);
+    __syncthreads();
+  }
+  // merge the waves in order into the workgroup partial: [FR][Nf] per workgroup
+  const int f_lo = (a0 * BS) / p.Nt;
+  for (int i = tid; i < p.FR * p.Nf; i += kThreads) {
+    const int fr = i / p.Nf, fk = i - fr * p.Nf;
+    Stat t{0.0, 0.0, 0.0, 0ull};
+    for (int w = 0; w < kWaves; ++w) {
+      const int qbw = w / G::WPQ, subw = w - qbw * G::WPQ;
+      const int q0w = (a0 + qbw) * BS + 32 * subw;
+      if (a0 + qbw >= p.Sb || q0w >= p.S) continue;
+      const int fo = f_lo + fr - q0w / p.Nt;
+      if (fo < 0 || fo > 1) continue;
+      const Stat& m = acc_l[(w * 2 + fo) * p.Nf + fk];
+      merge(t, m.n, m.mean, m.m2, m.mx);
+    }
+    Stat* out = p.part + ((size_t)(b * p.n_wg + wg) * p.FR + fr) * p.Nf + fk;
+    *out = t;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Pass 2: per frame pair, merge the workgroup partials (in order) and derive
+// the threshold in score units.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void reduce_kernel(TokParams p) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  const int b = blockIdx.y;
+  if (i >= p.Nf * p.Nf) return;
+  const int fq = i / p.Nf, fk = i - fq * p.Nf;
+  Stat t{0.0, 0.0, 0.0, 0ull};
+  const int w_lo = (int)(((long long)fq * p.Nt) / kRows);
+  const int w_hi = (int)(((long long)(fq + 1) * p.Nt - 1) / kRows);
+  for (int w = w_lo; w <= w_hi && w < p.n_wg; ++w) {
+    const int f_lo = (int)(((long long)w * kRows) / p.Nt);
+    const int fr = fq - f_lo;
+    if (fr < 0 || fr >= p.FR) continue;
+    const Stat& m = p.part[((size_t)(b * p.n_wg + w) * p.FR + fr) * p.Nf + fk];
+    merge(t, m.n, m.mean, m.m2, m.mx);
+  }
+  float thr = INFINITY;
+  if (t.n > 0.0) {
+#pragma clang fp contract(off)
+    const int dt = fq > fk ? fq - fk : fk - fq;
+    const int B = 32 - __builtin_clz((unsigned)dt);
+    const double decay = (double)p.L0 / (double)(1LL << B) * p.gamma;   // Eq. 2
+    const double tau = decay >= (double)p.Bs ? p.tau_near : p.tau_far;  // Eq. 11
+    const double sigma = sqrt(t.m2 / t.n);
+    const double bound = t.mean + tau * (sigma + p.eps);
+    // smallest float >= bound (float32 s >= it  <=>  (double) s >= bound)
+    float f = (float)bound;
+    if ((double)f < bound) f = nextafterf(f, INFINITY);
+    thr = f;
+  }
+  const size_t o = (size_t)b * p.Nf * p.Nf + i;
+  p.thr[o] = thr;
+  p.fmax[o] = t.mx;
+  p.fn[o] = t.n;
+  p.served[o] = 0;
+}
+
+// Decision of one block pair from per-key-token selected counts.
+__device__ inline bool block_kept(const TokParams& p, const int* cnt, int nq, int nk) {
+  int act = 0;
+  for (int c = 0; c < nk; ++c) act += ((double)cnt[c] / (double)nq) > p.theta_c ? 1 : 0;
+  return ((double)act / (double)nk) > p.theta_m;
+}
+
+// ---------------------------------------------------------------------------
+// Pass 3: selection, aggregation to block pairs, one flag per candidate entry.
+// ---------------------------------------------------------------------------
+template <int D, int BS, int HF>
+__global__ __launch_bounds__(kThreads) void mark_kernel(TokParams p) {
+  using G = Geo<D, BS, HF>;
+  extern __shared__ __align__(16) unsigned char smem[];
+  __shared__ int s_nsteps;
+  Lds<D, BS, HF> L(smem, p.Sb, p.Nf);
+  int* colcnt = reinterpret_cast<int*>(L.rest);              // [2][QB][BS]
+  float* thr_l = reinterpret_cast<float*>(colcnt + 2 * G::QB * BS);   // [FR][Nf]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5;
+  const int wg = blockIdx.x, b = blockIdx.y;
+  const int a0 = wg * G::QB;
+  const int f_lo = (a0 * BS) / p.Nt;
+  for (int i = tid; i < 2 * G::QB * BS; i += kThreads) colcnt[i] = 0;
+  for (int i = tid; i < p.FR * p.Nf; i += kThreads) {
+    const int fr = i / p.Nf, fk = i - fr * p.Nf;
+    const int fq = f_lo + fr;
+    thr_l[i] = fq < p.Nf ? p.thr[(size_t)b * p.Nf * p.Nf + (size_t)fq * p.Nf + fk] : INFINITY;
+  }
+  const int nsteps = setup<D, BS, HF>(p, L, a0, &s_nsteps);
+
+  const int qb = wave / G::WPQ, sub = wave - qb * G::WPQ;
+  const int a = a0 + qb;
+  const int q0 = a * BS + 32 * sub;
+  const bool active_wave = a < p.Sb && q0 < p.S;
+  bf16x8 qf[HF][D / 16];
+  if (active_wave) load_q<D, HF>(p, b, q0, lane, qf);
+
+  WalkState ws{0, 0, L.uword[0]};
+  Stager<D, BS, HF> st;
+  if (nsteps > 0) {
+    st.load(p, b, block_of_step(L.uword, ws, 0), tid);
+    st.store(L.kbuf[0], tid);
+  }
+  __syncthreads();
+  int kb_prev = -1;
+  for (int j = 0; j <= nsteps; ++j) {
+    // decide step j - 1 (its counts are complete after the barrier)
+    if (kb_prev >= 0 && sub == 0 && a < p.Sb && lane == 0) {
+      int* cnt = colcnt + ((j - 1) & 1) * G::QB * BS + qb * BS;
+      if ((L.bits[qb * L.nword + (kb_prev >> 5)] >> (kb_prev & 31)) & 1u) {
+        const int nq = min(BS, p.S - a * BS), nk = min(BS, p.S - kb_prev * BS);
+        const bool keep = block_kept(p, cnt, nq, nk);
+        const int wi = kb_prev >> 5;
+        const long long e = p.row_ptr[a] + L.pre[qb * L.nword + wi] +
+                            __popc(L.bits[qb * L.nword + wi] & ((1u << (kb_prev & 31)) - 1u));
+        p.flags[(long long)b * p.nnz + e] = keep ? 1 : 0;
+      }
+      for (int c = 0; c < BS; ++c) cnt[c] = 0;
+    }
+    if (j == nsteps) break;
+    const int kb = uniform(block_of_step(L.uword, ws, j));
+    int kb_next = -1;
+    if (j + 1 < nsteps) {
+      WalkState w2 = ws;
+      kb_next = uniform(block_of_step(L.uword, w2, j + 1));
+    }
+    st.load(p, b, kb_next, tid);
+    const unsigned char* kbuf = L.kbuf[j & 1];
+    const bool need = active_wave && ((L.bits[qb * L.nword + (kb >> 5)] >> (kb & 31)) & 1u);
+    if (need) {
+      int* cnt = colcnt + (j & 1) * G::QB * BS + qb * BS;
+#pragma unroll
+      for (int ksub = 0; ksub < BS / 32; ++ksub) {
+        const int ktok0 = kb * BS + 32 * ksub;
+        if (ktok0 >= p.S) break;
+        const floatx16 acc = tile_scores<D, BS, HF>(qf, kbuf, ksub, lane);
+        const TileFrames f = tile_frames(p, q0, ktok0 + (lane & 31));
+        const float thr0 = f.kvalid ? thr_l[(f.f0 - f_lo) * p.Nf + f.fk] : INFINITY;
+        const float thr1 = (f.kvalid && f.f0 + 1 - f_lo < p.FR) ? thr_l[(f.f0 + 1 - f_lo) * p.Nf + f.fk] : INFINITY;
+        unsigned sel, inP2;
+        select_bits(p, acc, f, q0, half, L.s_w, L.s_sf, thr0, thr1, sel, inP2);
+        // frame pairs with a selected t > 1 pair are served
+        const unsigned s2 = sel & inP2;
+        if (s2) {
+          for (int i = 0; i < 16; ++i)
+            if ((s2 >> i) & 1u) {
+              int u = f.u0 + row_of(i, half);
+              const int fq = f.f0 + (u >= p.Nt ? 1 : 0);
+              p.served[(size_t)b * p.Nf * p.Nf + (size_t)fq * p.Nf + f.fk] = 1;
+            }
+        }
+        // selected count of this lane's key column over the wave's 32 rows
+        int c = __popc(sel);
+        c += __shfl_xor(c, 32);
+        if (half == 0) atomicAdd(&cnt[32 * ksub + lane], c);
+      }
+    }
+    st.store(L.kbuf[(j + 1) & 1], tid);
+    kb_prev = kb;
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Pass 4: safeguard (ii). One wavefront per frame pair (i, j) of batch b.
+// ---------------------------------------------------------------------------
+template <int D, int BS, int HF>
+__global__ __launch_bounds__(64) void fallback_kernel(TokParams p) {
+  using G = Geo<D, BS, HF>;
+  __shared__ __align__(16) unsigned char kbuf[G::KBUF];
+  __shared__ int s_w[kMaxTokenFrames], s_sf[kMaxTokenFrames];
+  __shared__ int cnt[BS];
+  const int lane = threadIdx.x, half = lane >> 5;
+  const int fp = blockIdx.x, b = blockIdx.y;
+  const int fq = fp / p.Nf, fk = fp - fq * p.Nf;
+  const size_t base = (size_t)b * p.Nf * p.Nf;
+  auto unserved = [&](int i, int j) -> bool {
+    if (i < 0 || j < 0 || i >= p.Nf || j >= p.Nf) return false;
+    const size_t o = base + (size_t)i * p.Nf + j;
+    return p.fn[o] > 0.0 && p.served[o] == 0;
+  };
+  if (!unserved(fq, fk)) return;
+  // the highest-scoring pair of P(fq, fk)
+  auto pair_of = [&](int i, int j, int* qt, int* kt) {
+    const unsigned int loc = 0xffffffffu - (unsigned int)(p.fmax[base + (size_t)i * p.Nf + j] & 0xffffffffull);
+    *qt = i * p.Nt + (int)(loc / (unsigned)p.Nt);
+    *kt = j * p.Nt + (int)(loc % (unsigned)p.Nt);
+  };
+  int qt, kt;
+  pair_of(fq, fk, &qt, &kt);
+  const int a = qt / BS, kbk = kt / BS;
+  // every unserved frame pair whose fallback pair lies in block pair (a, kbk);
+  // the lowest-numbered one decides for all of them
+  const int fa0 = (a * BS) / p.Nt, fa1 = (min(p.S, (a + 1) * BS) - 1) / p.Nt;
+  const int fb0 = (kbk * BS) / p.Nt, fb1 = (min(p.S, (kbk + 1) * BS) - 1) / p.Nt;
+  int extra_q[4], extra_k[4], n_extra = 0;
+  for (int i = fa0; i <= fa1; ++i)
+    for (int j = fb0; j <= fb1; ++j) {
+      if (!unserved(i, j)) continue;
+      int q2, k2;
+      pair_of(i, j, &q2, &k2);
+      if (q2 / BS != a || k2 / BS != kbk) continue;
+      if (i * p.Nf + j < fp) return;   // a lower-numbered frame pair decides this block pair
+      extra_q[n_extra] = q2;
+      extra_k[n_extra] = k2;
+      ++n_extra;
+    }
+  // the candidate entry of (a, kbk), if any (the aggregate of the selection
+  // never exceeds that of P, so a non-candidate block pair stays dropped)
+  int lo = p.row_ptr[a], hi = p.row_ptr[a + 1];
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (p.cols[mid] < kbk) lo = mid + 1; else hi = mid;
+  }
+  if (lo >= p.row_ptr[a + 1] || p.cols[lo] != kbk) return;
+  for (int t = lane; t < p.Nf; t += 64) {
+    int w, sf;
+    table_entry(t, p.Nt, BS, p.L0, p.gamma, p.lambda, &w, &sf);
+    s_w[t] = w < p.Nt ? w : p.Nt;
+    s_sf[t] = sf;
+  }
+  for (int c = lane; c < BS; c += 64) cnt[c] = 0;
+  // stage key block kbk (one wavefront: loop over the chunks)
+  for (int c = lane; c < HF * BS * (D / 8); c += 64) {
+    const int h = c / (BS * (D / 8));
+    const int rem = c - h * (BS * (D / 8));
+    const int key = rem / (D / 8), ch = rem - key * (D / 8);
+    const int tok = kbk * BS + key;
+    u32x4 v = {0, 0, 0, 0};
+    if (tok < p.S) v = *reinterpret_cast<const u32x4*>(p.k + ((size_t)(b * p.H + h) * p.S + tok) * D + ch * 8);
+    *reinterpret_cast<u32x4*>(kbuf + (h * BS + key) * G::RB + ((ch ^ swz<D>(key)) << 4)) = v;
+  }
+  __syncthreads();
+  for (int sub = 0; sub < BS / 32; ++sub) {
+    const int q0 = a * BS + 32 * sub;
+    if (q0 >= p.S) break;
+    bf16x8 qf[HF][D / 16];
+    load_q<D, HF>(p, b, q0, lane, qf);
+    for (int ksub = 0; ksub < BS / 32; ++ksub) {
+      const int ktok0 = kbk * BS + 32 * ksub;
+      if (ktok0 >= p.S) break;
+      const floatx16 acc = tile_scores<D, BS, HF>(qf, kbuf, ksub, lane);
+      const TileFrames f = tile_frames(p, q0, ktok0 + (lane & 31));
+      const float thr0 = f.kvalid ? p.thr[base + (size_t)f.f0 * p.Nf + f.fk] : INFINITY;
+      const float thr1 = (f.kvalid && f.f0 + 1 < p.Nf) ? p.thr[base + (size_t)(f.f0 + 1) * p.Nf + f.fk] : INFINITY;
+      unsigned sel, inP2;
+      select_bits(p, acc, f, q0, half, s_w, s_sf, thr0, thr1, sel, inP2);
+      const int ktok = ktok0 + (lane & 31);
+      for (int e = 0; e < n_extra; ++e)
+        if (extra_k[e] == ktok)
+          for (int i = 0; i < 16; ++i)
+            if (q0 + row_of(i, half) == extra_q[e]) sel |= 1u << i;
+      int c = __popc(sel);
+      c += __shfl_xor(c, 32);
+      if (half == 0) cnt[32 * ksub + lane] += c;
+      __syncthreads();
+    }
+  }
+  if (lane == 0) {
+    const int nq = min(BS, p.S - a * BS), nk = min(BS, p.S - kbk * BS);
+    p.flags[(long long)b * p.nnz + lo] = block_kept(p, cnt, nq, nk) ? 1 : 0;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Pass 5: ordered compaction of the flags into kept lists of every head.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void compact_kernel(TokParams p) {
+  const int lane = threadIdx.x & 63;
+  const int a = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int b = blockIdx.y;
+  if (a >= p.Sb) return;
+  const int r0 = p.row_ptr[a], n = p.row_ptr[a + 1] - r0;
+  const unsigned char* fl = p.flags + (long long)b * p.nnz + r0;
+  int kept = 0;
+  for (int i0 = 0; i0 < n; i0 += 64) {
+    const int i = i0 + lane;
+    const bool keep = i < n && fl[i] != 0;
+    const unsigned long long m = __ballot(keep);
+    const int before = __builtin_amdgcn_mbcnt_hi((unsigned)(m >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)m, 0));
+    if (keep) {
+      const int col = p.cols[r0 + i];
+      for (int h = 0; h < p.H; ++h) p.kept_col[(long long)(b * p.H + h) * p.nnz + r0 + kept + before] = col;
+    }
+    kept += __popcll(m);
+  }
+  if (lane == 0)
+    for (int h = 0; h < p.H; ++h) p.kept_cnt[(long long)(b * p.H + h) * p.Sb + a] = kept;
+}
+
+template <int D, int BS, int HF>
+hipError_t launch_all(const TokParams& p, int B, hipStream_t stream) {
+  using G = Geo<D, BS, HF>;
+  const size_t base = Lds<D, BS, HF>::bytes(p.Sb, p.Nf);
+  const size_t lds_stats = base + (size_t)kWaves * 2 * p.Nf * sizeof(Stat);
+  const size_t lds_mark = base + (size_t)2 * G::QB * BS * 4 + (size_t)p.FR * p.Nf * 4;
+  (void)sizeof(G);
+  const dim3 grid((unsigned)p.n_wg, (unsigned)B);
+  hipLaunchKernelGGL((stats_kernel<D, BS, HF>), grid, dim3(kThreads), lds_stats, stream, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(reduce_kernel, dim3((unsigned)((p.Nf * p.Nf + 255) / 256), (unsigned)B), dim3(256), 0, stream,
+                     p);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL((mark_kernel<D, BS, HF>), grid, dim3(kThreads), lds_mark, stream, p);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL((fallback_kernel<D, BS, HF>), dim3((unsigned)(p.Nf * p.Nf), (unsigned)B), dim3(64), 0, stream,
+                     p);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(compact_kernel, dim3((unsigned)((p.Sb + 3) / 4), (unsigned)B), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+template <int D, int BS, int HF>
+size_t lds_need(int Sb, int Nf, int FR) {
+  using G = Geo<D, BS, HF>;
+  const size_t base = Lds<D, BS, HF>::bytes(Sb, Nf);
+  const size_t stats = base + (size_t)kWaves * 2 * Nf * sizeof(Stat);
+  const size_t mark = base + (size_t)2 * G::QB * BS * 4 + (size_t)FR * Nf * 4;
+  return stats > mark ? stats : mark;
+}
+
+size_t token_lds_bytes(int D, int Bs, int Hf, int Sb, int Nf, int FR) {
+  if (D == 128 && Bs == 32) return Hf == 1 ? lds_need<128, 32, 1>(Sb, Nf, FR) : lds_need<128, 32, 2>(Sb, Nf, FR);
+  if (D == 128 && Bs == 64) return Hf == 1 ? lds_need<128, 64, 1>(Sb, Nf, FR) : lds_need<128, 64, 2>(Sb, Nf, FR);
+  if (D == 64 && Bs == 32) return Hf == 1 ? lds_need<64, 32, 1>(Sb, Nf, FR) : lds_need<64, 32, 2>(Sb, Nf, FR);
+  return Hf == 1 ? lds_need<64, 64, 1>(Sb, Nf, FR) : lds_need<64, 64, 2>(Sb, Nf, FR);
+}
+
+hipError_t launch_token_select(const TokParams& p, int B, int D, int Bs, int Hf, hipStream_t stream) {
+  if (D == 128 && Bs == 32 && Hf == 1) return launch_all<128, 32, 1>(p, B, stream);
+  if (D == 128 && Bs == 32 && Hf == 2) return launch_all<128, 32, 2>(p, B, stream);
+  if (D == 128 && Bs == 64 && Hf == 1) return launch_all<128, 64, 1>(p, B, stream);
+  if (D == 128 && Bs == 64 && Hf == 2) return launch_all<128, 64, 2>(p, B, stream);
+  if (D == 64 && Bs == 32 && Hf == 1) return launch_all<64, 32, 1>(p, B, stream);
+  if (D == 64 && Bs == 32 && Hf == 2) return launch_all<64, 32, 2>(p, B, stream);
+  if (D == 64 && Bs == 64 && Hf == 1) return launch_all<64, 64, 1>(p, B, stream);
+  if (D == 64 && Bs == 64 && Hf == 2) return launch_all<64, 64, 2>(p, B, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace dr

@@ -10,6 +10,8 @@
  *                           "Density control within blocks"), content-free.
  *   2. dr_score_select      mean-pooled block scores and dual-mode selection
  *                           ([DR] §3.2: static-ratio / dynamic-threshold).
+ *      dr_token_select      the paper's token-level dynamic-threshold selector
+ *                           ([DR] §3.2 Eqs. 9-11, Algorithm 1).
  *   3. dr_sparse_attn       flash-style forward attention over the kept KV
  *                           blocks only ([DR] §3.3, Eq. 13 with eps -> 0).
  *   dr_attn                 dense forward attention, the speedup denominator
@@ -142,6 +144,47 @@ dr_status dr_score_select(const dr_dims* dims, const dr_radial_cfg* cfg, const d
                           const void* q, const void* k, const int32_t* row_ptr, const int32_t* cols,
                           int64_t nnz, int32_t* kept_col, int32_t* kept_cnt, float* scores_out,
                           void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Token-level dynamic-threshold selection: the selector of [DR] §3.2
+ * "Dynamic-threshold mode" (Eqs. 9-11, "Global thresholding with safeguards",
+ * Algorithm 1), aggregated to blocks by the density control of §3.1.
+ * For every frame pair (i, j), t = |i - j|:
+ *   - t mod sf(t) != 0: no pair (Eq. 6);
+ *   - t <= 1: every pair of P(i, j) is selected (tau = -inf, Eq. 11; t = 0 is
+ *     dense attention);
+ *   - otherwise s(u, v) = (1/H_f) sum_{h < H_f} Q_u^h . K_v^h / sqrt(d_k) (Eq. 9)
+ *     on P(i, j) = {|u - v| <= w(t)} (Eq. 7); z = (s - mu_ij) / (sigma_ij + eps)
+ *     with mu, sigma the mean and population standard deviation of s over
+ *     P(i, j) (Eq. 10); a pair is selected iff z >= tau(t), tau = tau_near if
+ *     L(t) = L0 / 2^B(t) * gamma >= B_s, else tau_far (Eq. 11); if no pair of
+ *     P(i, j) is selected, its highest-scoring pair is (safeguard (ii); ties:
+ *     the first in (u, v) order).
+ * Block pair (a, b) is kept iff, over all frame pairs it spans, the share of
+ * b's key tokens whose selected share of a's query tokens exceeds theta_c
+ * itself exceeds theta_m (cfg->theta_c, cfg->theta_m). The heads 0..H_f-1 of
+ * each batch element decide one mask, written for every head.
+ * Inputs: q, k bf16 [B, H, S, D]; row_ptr, cols from dr_build_candidates with
+ * the same cfg (the kept set is always a subset of the candidate set).
+ * Outputs: kept_col / kept_cnt in the layout of dr_score_select.
+ * Limits: tokens_per_frame in [32, 65535], num_frames <= 64, fused_heads in
+ * {1, 2} (<= heads), eps > 0, tau_near and tau_far not NaN (+-inf allowed).
+ * Deterministic: statistics are merged in a fixed order (no float atomics). */
+typedef struct dr_token_cfg {
+  int32_t fused_heads;  /* H_f: 1 or 2 ([DR] Table 4: 2)                   */
+  int32_t reserved;     /* must be 0                                        */
+  double tau_near;      /* tau_1, near_frame_thresh (Eq. 11)                */
+  double tau_far;       /* tau_2, far_frame_thresh                          */
+  double eps;           /* epsilon of Eq. 10, > 0                           */
+} dr_token_cfg;
+
+/* Device workspace (bytes) of dr_token_select. Host only. */
+dr_status dr_token_select_workspace(const dr_dims* dims, const dr_radial_cfg* cfg, const dr_token_cfg* tok,
+                                    int64_t nnz, size_t* bytes);
+
+dr_status dr_token_select(const dr_dims* dims, const dr_radial_cfg* cfg, const dr_token_cfg* tok,
+                          const void* q, const void* k, const int32_t* row_ptr, const int32_t* cols,
+                          int64_t nnz, int32_t* kept_col, int32_t* kept_cnt, void* ws, size_t ws_bytes,
+                          hipStream_t stream);
 
 /* Block-sparse forward attention ([DR] §3.3 Eqs. 12-13, eps -> 0): for each
  * (b, h) and query block a, O[rows of a] = softmax(Q K^T * softmax_scale) V over

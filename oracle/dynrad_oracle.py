@@ -407,7 +407,7 @@ def token_scores_block(q_heads, k_heads, rows: slice, cols: slice, scale: float)
 
 def token_frame_stats(q_heads, k_heads, num_frames: int, tokens_per_frame: int, block_size: int,
                       gamma: float, lam: float, tau_near: float, tau_far: float,
-                      eps: float = EPS_NORM, scale: float = None) -> dict:
+                      eps: float = EPS_NORM, scale: float = None, top2: dict = None) -> dict:
     """Per frame pair (i, j) with t = |i - j| > 1 that is retained (Eq. 6):
     (mu, sigma, tau, fallback) where mu and sigma are the mean and standard
     deviation of s over P(i, j) (Eqs. 7, 9, 10), tau = tau_near if L(t) >= B_s
@@ -415,7 +415,8 @@ def token_frame_stats(q_heads, k_heads, num_frames: int, tokens_per_frame: int, 
     no pair reaches tau, else None (safeguard (ii)).
     Readings: sigma is the population standard deviation (divide by |P|);
     eps = 1e-6; a tie for the highest score goes to the first pair in (u, v)
-    order."""
+    order. If top2 is a dict, it receives the two highest scores of each
+    frame pair (for token_select_decisive)."""
     q_heads, k_heads = _fused(q_heads), _fused(k_heads)
     scale = 1.0 / math.sqrt(q_heads[0].shape[1]) if scale is None else scale
     w, sf = distance_table(num_frames, tokens_per_frame, block_size, gamma, lam)
@@ -439,6 +440,9 @@ def token_frame_stats(q_heads, k_heads, num_frames: int, tokens_per_frame: int, 
                 masked = np.where(P, sv, -np.inf)
                 fallback = tuple(int(x) for x in np.unravel_index(int(np.argmax(masked)), masked.shape))
             stats[(i, j)] = (mu, sigma, tau, fallback)
+            if top2 is not None:
+                srt = np.partition(vals, len(vals) - 2)[-2:] if len(vals) > 1 else np.array([-np.inf, vals[0]])
+                top2[(i, j)] = (float(srt.max()), float(srt.min()))
     return stats
 
 
@@ -537,7 +541,8 @@ def token_select(q_heads, k_heads, num_frames: int, tokens_per_frame: int, block
 
 def token_select_decisive(q_heads, k_heads, blocks, num_frames: int, tokens_per_frame: int, block_size: int,
                           gamma: float, lam: float, tau_near: float, tau_far: float, margin: float,
-                          eps: float = EPS_NORM, scale: float = None, stats: dict = None) -> List[np.ndarray]:
+                          eps: float = EPS_NORM, scale: float = None, stats: dict = None,
+                          top2: dict = None) -> List[np.ndarray]:
     """For each given query block, a bool per key block: True where no
     token-level decision of the block pair can flip under a perturbation of
     every z below `margin` and of every score below `margin` * sigma. Unsure
@@ -556,13 +561,17 @@ def token_select_decisive(q_heads, k_heads, blocks, num_frames: int, tokens_per_
     ukey = np.arange(Nt)
     doubtful = {}
     for (i, j), (mu, sigma, tau, fb) in stats.items():
-        t = abs(i - j)
-        P = np.abs(ukey[:, None] - ukey[None, :]) <= w[t]
-        sv = token_scores_block(q_heads, k_heads, slice(i * Nt, (i + 1) * Nt), slice(j * Nt, (j + 1) * Nt), scale)
-        top = np.sort(sv[P])[::-1]
-        zmax = (top[0] - mu) / (sigma + eps)
-        doubtful[(i, j)] = abs(zmax - tau) <= margin or (
-            zmax < tau and len(top) > 1 and top[0] - top[1] <= margin * (sigma + eps))
+        if top2 is not None:
+            t1, t2 = top2[(i, j)]
+        else:
+            t = abs(i - j)
+            P = np.abs(ukey[:, None] - ukey[None, :]) <= w[t]
+            sv = token_scores_block(q_heads, k_heads, slice(i * Nt, (i + 1) * Nt), slice(j * Nt, (j + 1) * Nt),
+                                    scale)
+            top = np.sort(sv[P])[::-1]
+            t1, t2 = top[0], (top[1] if len(top) > 1 else -np.inf)
+        zmax = (t1 - mu) / (sigma + eps)
+        doubtful[(i, j)] = abs(zmax - tau) <= margin or (zmax < tau and t1 - t2 <= margin * (sigma + eps))
     out = []
     for a in blocks:
         rows = slice(a * block_size, min((a + 1) * block_size, S))

@@ -135,3 +135,34 @@ def test_select_and_attention_validation(dynrad_lib):
                               ctypes.c_void_p(8192), None) == L.DR_ERR_UNSUPPORTED
     for s in range(5):
         assert dynrad_lib.dr_status_string(s).decode()
+
+
+def test_token_select_validation(dynrad_lib):
+    """dr_token_select rejects out-of-range configurations before any HIP call,
+    and its workspace is the sum of its aligned parts."""
+    from block_sparse_attention_candidates_amd import _lib as L
+    FAKE = ctypes.c_void_p(4096)
+    cfg = _cfg(4, 64, 32, 1.0, 2.0)             # S = 256, S_b = 8
+    dims = L.Dims(1, 2, 64, 0)
+    tok = L.TokenCfg(2, 0, -1.5, 2.0, 1e-6)
+    size = ctypes.c_size_t(0)
+    assert dynrad_lib.dr_token_select_workspace(ctypes.byref(dims), ctypes.byref(cfg), ctypes.byref(tok), 64,
+                                                ctypes.byref(size)) == L.DR_OK
+    # partials: 1 workgroup x FR (255 // 64 + 2 = 5) x N_f 4 x 32 B = 640 -> 768; thr 64 B -> 256;
+    # maxima 128 B -> 256; counts 128 B -> 256; served 64 B -> 256; flags 64 B -> 256
+    assert size.value == 768 + 5 * 256
+
+    def ts(d=dims, c=cfg, t=tok, nnz=64, ws_bytes=1 << 20, q=FAKE):
+        return dynrad_lib.dr_token_select(ctypes.byref(d), ctypes.byref(c), ctypes.byref(t), q, FAKE, FAKE, FAKE,
+                                          nnz, FAKE, FAKE, FAKE, ws_bytes, None)
+    assert ts(t=L.TokenCfg(3, 0, -1.5, 2.0, 1e-6), d=L.Dims(1, 4, 64, 0)) == L.DR_ERR_UNSUPPORTED  # H_f = 3
+    assert ts(t=L.TokenCfg(3, 0, -1.5, 2.0, 1e-6)) == L.DR_ERR_INVALID_ARG    # H_f > heads
+    assert ts(t=L.TokenCfg(0, 0, -1.5, 2.0, 1e-6)) == L.DR_ERR_INVALID_ARG
+    assert ts(t=L.TokenCfg(2, 1, -1.5, 2.0, 1e-6)) == L.DR_ERR_INVALID_ARG    # reserved
+    assert ts(t=L.TokenCfg(2, 0, float("nan"), 2.0, 1e-6)) == L.DR_ERR_INVALID_ARG
+    assert ts(t=L.TokenCfg(2, 0, -1.5, 2.0, 0.0)) == L.DR_ERR_INVALID_ARG     # eps must be > 0
+    assert ts(c=_cfg(8, 16, 32, 1.0, 2.0)) == L.DR_ERR_UNSUPPORTED            # N_t < 32
+    assert ts(c=_cfg(65, 64, 32, 1.0, 2.0)) == L.DR_ERR_UNSUPPORTED           # N_f > 64
+    assert ts(q=None) == L.DR_ERR_INVALID_ARG
+    assert ts(ws_bytes=100) == L.DR_ERR_CAPACITY
+    assert ts(t=L.TokenCfg(2, 0, float("-inf"), float("inf"), 1e-6), ws_bytes=100) == L.DR_ERR_CAPACITY

@@ -229,3 +229,22 @@ def qkv_bits_parallel(w: Workload, heads: Optional[Sequence[int]] = None, worker
     if workers > 1 and len(jobs) > 1:
         ex.shutdown()
     return tuple(out)
+
+
+# [DR] Table 2, dynamic-threshold rows (BO-optimised presets of the paper's
+# token-level selector): decay gamma, long-range lambda, mask threshold
+# theta_m, column threshold theta_c, near / far thresholds tau_1 / tau_2.
+TOKEN_PRESETS = {
+    "low": dict(gamma=1.3, lam=0.4, theta_m=0.70, theta_c=0.45, tau_near=-1.2, tau_far=2.4),
+    "mid": dict(gamma=1.4, lam=0.7, theta_m=0.70, theta_c=0.45, tau_near=-1.5, tau_far=2.0),
+    "high": dict(gamma=1.6, lam=0.9, theta_m=0.55, theta_c=0.40, tau_near=-2.0, tau_far=2.4),
+}
+
+
+def token_workload(base: str, preset: str):
+    """A workload's tensors (same seed and field) under a Table 2 preset of
+    the token-level selector; returns (workload, (tau_near, tau_far))."""
+    pr = TOKEN_PRESETS[preset]
+    w = dataclasses.replace(get_workload(base), name=f"{base}+{preset}", gamma=pr["gamma"], lam=pr["lam"],
+                            theta_c=pr["theta_c"], theta_m=pr["theta_m"])
+    return w, (pr["tau_near"], pr["tau_far"])
