@@ -36,7 +36,11 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="wan14b_720p")
-    ap.add_argument("--mode", default="static", choices=["static", "dynamic"])
+    ap.add_argument("--mode", default="static", choices=["static", "dynamic", "token"],
+                    help="block-level static-ratio / dynamic-threshold selection, or the paper's token-level "
+                         "dynamic-threshold selector (dr_token_select) with a Table 2 preset")
+    ap.add_argument("--preset", default="mid", choices=["low", "mid", "high"],
+                    help="Table 2 dynamic preset of --mode token")
     ap.add_argument("--stage-iters", type=int, default=20)
     ap.add_argument("--dense-iters", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -88,6 +92,8 @@ def cpu_baseline(w, mode, ratio, tau, n_blocks):
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:
         cores = 1
+    if mode == "token":
+        return cpu_baseline_token(w, tau, cores)
     q, k, v = (x.astype(np.float64) for x in workloads.head_qkv(w, 0, 0))
     Sb = w.num_blocks
     blocks = np.unique(np.linspace(0, Sb - 1, n_blocks).astype(int))
@@ -110,6 +116,37 @@ def cpu_baseline(w, mode, ratio, tau, n_blocks):
                       f"(candidate rows, pooling, scores, {mode} selection, attention), float64 NumPy"}
 
 
+def cpu_baseline_token(w, taus, cores):
+    """Token-level mode: the query blocks lying in frame N_f/2, with the
+    statistics of the frame pairs they need (that frame against every key
+    frame), their selection and their attention, on heads 0-1 (H_f = 2)."""
+    import workloads
+    from oracle import dynrad_oracle as O
+    heads = [workloads.head_qkv(w, 0, h) for h in range(2)]
+    qh = [x[0].astype(np.float64) for x in heads]
+    kh = [x[1].astype(np.float64) for x in heads]
+    v0 = heads[0][2].astype(np.float64)
+    Nf, Nt, Bs = w.num_frames, w.tokens_per_frame, w.block_size
+    frames = [Nf // 2]
+    blocks = sorted({a for f in frames for a in range(f * Nt // Bs, ((f + 1) * Nt - 1) // Bs + 1)
+                     if a * Bs // Nt == f and ((a + 1) * Bs - 1) // Nt == f})
+    t0 = time.perf_counter()
+    sub = O.token_frame_stats(qh, kh, Nf, Nt, Bs, w.gamma, w.lam, taus[0], taus[1], query_frames=frames)
+    kept = O.token_select_rows(qh, kh, blocks, Nf, Nt, Bs, w.gamma, w.lam, taus[0], taus[1], w.theta_c, w.theta_m,
+                               stats=sub)
+    klist = [np.zeros(0, dtype=np.int64)] * w.num_blocks
+    for a, ks in zip(blocks, kept):
+        klist[a] = ks
+    O.sparse_attention_rows(qh[0], kh[0], v0, Bs, klist, blocks)
+    dt = time.perf_counter() - t0
+    flops = 4.0 * Bs ** 2 * w.head_dim * sum(len(x) for x in kept)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "seconds": round(dt, 3),
+            "sample": f"{w.name}: the {len(blocks)} query blocks inside frames {frames}, all stages (statistics "
+                      f"of those frames' frame pairs, token-level selection on heads 0-1, attention on head 0), "
+                      f"float64 NumPy"}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -125,6 +162,9 @@ def main():
         from block_sparse_attention_candidates_amd import build
         build.build()
     w = workloads.get_workload(args.workload)
+    taus = None
+    if args.mode == "token":
+        w, taus = workloads.token_workload(args.workload, args.preset)
     ratio = w.static_ratio if args.mode == "static" else 1.0
     tau = w.dynamic_tau if args.mode == "dynamic" else 1.0
     print(f"# generating {w.name}: B={w.batch} H={w.heads} S={w.seq_len} D={w.head_dim}", file=sys.stderr, flush=True)
@@ -133,17 +173,22 @@ def main():
     del qb, kb, vb
     cfg = dr.radial_cfg(w.num_frames, w.tokens_per_frame, w.block_size, w.gamma, w.lam, w.theta_c, w.theta_m)
     cand = dr.build_candidates(cfg)           # setup: sizes the buffers (reports nnz)
-    sel_kw = dict(mode=args.mode, ratio=ratio, tau=tau)
-    kept = dr.score_select(q, k, cand, **sel_kw)
     import ctypes
     L = _lib.lib()
+    dims = _lib.Dims(w.batch, w.heads, w.head_dim, 0)
+    wsb = ctypes.c_size_t(0)
+    if args.mode == "token":
+        kept = dr.token_select(q, k, cand, taus[0], taus[1])
+        tokc = _lib.TokenCfg(2, 0, float(taus[0]), float(taus[1]), 1e-6)
+        _lib.check(L.dr_token_select_workspace(ctypes.byref(dims), ctypes.byref(cfg), ctypes.byref(tokc), cand.nnz,
+                                               ctypes.byref(wsb)))
+    else:
+        kept = dr.score_select(q, k, cand, mode=args.mode, ratio=ratio, tau=tau)
+        selc = dr._select_cfg(args.mode, ratio, tau, 0)
+        _lib.check(L.dr_score_select_workspace(ctypes.byref(dims), ctypes.byref(cfg), ctypes.byref(selc),
+                                               cand.nnz, ctypes.byref(wsb)))
     out = torch.empty_like(q)
     # preallocated buffers for the timed step (no allocation inside it)
-    dims = _lib.Dims(w.batch, w.heads, w.head_dim, 0)
-    selc = dr._select_cfg(args.mode, ratio, tau, 0)
-    wsb = ctypes.c_size_t(0)
-    _lib.check(L.dr_score_select_workspace(ctypes.byref(dims), ctypes.byref(cfg), ctypes.byref(selc), cand.nnz,
-                                           ctypes.byref(wsb)))
     ws = torch.empty(wsb.value, dtype=torch.uint8, device="cuda")
     row_ptr = torch.empty_like(cand.row_ptr)
     cols = torch.empty_like(cand.cols)
@@ -158,6 +203,12 @@ def main():
                                          stream()))
 
     def step_select():
+        if args.mode == "token":
+            _lib.check(L.dr_token_select(ctypes.byref(dims), ctypes.byref(cfg), ctypes.byref(tokc), q.data_ptr(),
+                                         k.data_ptr(), row_ptr.data_ptr(), cols.data_ptr(), cand.nnz,
+                                         kept_col.data_ptr(), kept_cnt.data_ptr(), ws.data_ptr(), ws.numel(),
+                                         stream()))
+            return
         _lib.check(L.dr_score_select(ctypes.byref(dims), ctypes.byref(cfg), ctypes.byref(selc), q.data_ptr(),
                                      k.data_ptr(), row_ptr.data_ptr(), cols.data_ptr(), cand.nnz,
                                      kept_col.data_ptr(), kept_cnt.data_ptr(), None, ws.data_ptr(), ws.numel(),
@@ -204,7 +255,9 @@ def main():
         "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": w.name, "mode": args.mode, "ratio": ratio if args.mode == "static" else None,
-                   "tau": tau if args.mode == "dynamic" else None, "batch": w.batch, "heads": w.heads,
+                   "tau": tau if args.mode == "dynamic" else None,
+                   "tau_near_far": list(taus) if taus else None, "theta_c": w.theta_c, "theta_m": w.theta_m,
+                   "batch": w.batch, "heads": w.heads,
                    "seq_len": w.seq_len, "head_dim": w.head_dim, "block_size": w.block_size, "gamma": w.gamma,
                    "lambda": w.lam, "parallelism": "single-gpu"},
         "sparsity": round(sparsity, 4),
@@ -212,7 +265,8 @@ def main():
         "kept_blocks": kept_total,
         "speedup_vs_dense": round(ms_dense / ms_step, 3) if ms_dense else None,
         "speedup_vs_dense_attention_only": round(ms_dense / ms_attn, 3) if ms_dense else None,
-        "stage_ms": {"build_candidates": round(ms_cand, 4), "score_select": round(ms_sel, 4),
+        "stage_ms": {"build_candidates": round(ms_cand, 4),
+                     ("token_select" if args.mode == "token" else "score_select"): round(ms_sel, 4),
                      "sparse_attn": round(ms_attn, 4), "dense_attn": round(ms_dense, 3) if ms_dense else None},
         "dense_tflops": round(dense_flops / (ms_dense * 1e-3) / 1e12, 2) if ms_dense else None,
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
@@ -232,7 +286,8 @@ def main():
         del src, dst
     if not args.no_cpu:
         print("# timing the CPU oracle sample", file=sys.stderr, flush=True)
-        res["cpu_baseline"] = cpu_baseline(w, args.mode, ratio, tau, args.cpu_blocks)
+        res["cpu_baseline"] = cpu_baseline(w, args.mode, ratio, taus if args.mode == "token" else tau,
+                                           args.cpu_blocks)
     print(json.dumps(res), flush=True)
 
 

@@ -407,7 +407,8 @@ def token_scores_block(q_heads, k_heads, rows: slice, cols: slice, scale: float)
 
 def token_frame_stats(q_heads, k_heads, num_frames: int, tokens_per_frame: int, block_size: int,
                       gamma: float, lam: float, tau_near: float, tau_far: float,
-                      eps: float = EPS_NORM, scale: float = None, top2: dict = None) -> dict:
+                      eps: float = EPS_NORM, scale: float = None, top2: dict = None,
+                      query_frames=None) -> dict:
     """Per frame pair (i, j) with t = |i - j| > 1 that is retained (Eq. 6):
     (mu, sigma, tau, fallback) where mu and sigma are the mean and standard
     deviation of s over P(i, j) (Eqs. 7, 9, 10), tau = tau_near if L(t) >= B_s
@@ -416,14 +417,16 @@ def token_frame_stats(q_heads, k_heads, num_frames: int, tokens_per_frame: int, 
     Readings: sigma is the population standard deviation (divide by |P|);
     eps = 1e-6; a tie for the highest score goes to the first pair in (u, v)
     order. If top2 is a dict, it receives the two highest scores of each
-    frame pair (for token_select_decisive)."""
+    frame pair (for token_select_decisive). query_frames, if given, limits
+    the result to frame pairs (i, j) with i in it (each pair's statistics
+    depend on that pair alone)."""
     q_heads, k_heads = _fused(q_heads), _fused(k_heads)
     scale = 1.0 / math.sqrt(q_heads[0].shape[1]) if scale is None else scale
     w, sf = distance_table(num_frames, tokens_per_frame, block_size, gamma, lam)
     Nt = tokens_per_frame
     u = np.arange(Nt)
     stats = {}
-    for i in range(num_frames):
+    for i in (range(num_frames) if query_frames is None else sorted(query_frames)):
         for j in range(num_frames):
             t = abs(i - j)
             if t <= 1 or t % sf[t] != 0:
