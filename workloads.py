@@ -206,8 +206,8 @@ def qkv(w: Workload, heads: Optional[Sequence[int]] = None, batches: Optional[Se
 
 
 def _head_bits(args):
-    name, b, h = args
-    return head_qkv(WORKLOADS[name], b, h, as_bits=True)
+    w, b, h = args
+    return head_qkv(w, b, h, as_bits=True)
 
 
 def qkv_bits_parallel(w: Workload, heads: Optional[Sequence[int]] = None, workers: int = 8):
@@ -215,14 +215,14 @@ def qkv_bits_parallel(w: Workload, heads: Optional[Sequence[int]] = None, worker
     processes (same values as head_qkv)."""
     from concurrent.futures import ProcessPoolExecutor
     heads = list(range(w.heads)) if heads is None else list(heads)
-    jobs = [(w.name, b, h) for b in range(w.batch) for h in heads]
+    jobs = [(w, b, h) for b in range(w.batch) for h in heads]
     out = [np.empty((w.batch, len(heads), w.seq_len, w.head_dim), dtype=np.uint16) for _ in range(3)]
     if workers <= 1 or len(jobs) == 1:
         results = map(_head_bits, jobs)
     else:
         ex = ProcessPoolExecutor(max_workers=min(workers, len(jobs)))
         results = ex.map(_head_bits, jobs)
-    for (name, b, h), t in zip(jobs, results):
+    for (_, b, h), t in zip(jobs, results):
         j = heads.index(h)
         for o, x in zip(out, t):
             o[b, j] = x
