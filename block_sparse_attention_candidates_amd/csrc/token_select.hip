@@ -46,28 +46,28 @@ constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
 constexpr int kRows = kWaves * 32;      // query tokens per workgroup
 
-__device__ inline int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
 // order-preserving unsigned key of a float
-__device__ inline unsigned int fkey(float s) {
+__device__ __forceinline__ unsigned int fkey(float s) {
   unsigned int u = __float_as_uint(s);
   if (u == 0x80000000u) u = 0;
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-__device__ inline unsigned long long pack_max(float s, unsigned int loc) {
+__device__ __forceinline__ unsigned long long pack_max(float s, unsigned int loc) {
   return ((unsigned long long)fkey(s) << 32) | (unsigned long long)(0xffffffffu - loc);
 }
 
 // XOR swizzle of 16-byte chunks within a staged key row (same layout argument
 // as the attention kernel: 16 lanes read 16 rows at one logical chunk)
 template <int D>
-__device__ inline int swz(int key) { return D == 128 ? (key & 15) : ((key >> 1) & 7); }
+__device__ __forceinline__ int swz(int key) { return D == 128 ? (key & 15) : ((key >> 1) & 7); }
 
 using Stat = TokStat;
 
 // Chan et al.'s pairwise update: merge (nb, mb, m2b) into a.
-__device__ inline void merge(Stat& a, double nb, double mb, double m2b, unsigned long long mxb) {
+__device__ __forceinline__ void merge(Stat& a, double nb, double mb, double m2b, unsigned long long mxb) {
   if (mxb > a.mx) a.mx = mxb;
   if (nb == 0.0) return;
   if (a.n == 0.0) {
@@ -83,12 +83,12 @@ __device__ inline void merge(Stat& a, double nb, double mb, double m2b, unsigned
   a.n = n;
 }
 
-__device__ inline double wave_sum(double v) {
+__device__ __forceinline__ double wave_sum(double v) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
   return v;
 }
-__device__ inline unsigned long long wave_max(unsigned long long v) {
+__device__ __forceinline__ unsigned long long wave_max(unsigned long long v) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) {
     const unsigned long long o = __shfl_xor(v, off);
@@ -109,7 +109,7 @@ struct Geo {
 // B = 32 staged keys (key sub-block ksub of the staged block). Lane l gets key
 // column l%32 and query rows 8*(i/4) + 4*(l/32) + i%4.
 template <int D, int BS, int HF>
-__device__ inline floatx16 tile_scores(const bf16x8 (&qf)[HF][D / 16], const unsigned char* kbuf, int ksub,
+__device__ __forceinline__ floatx16 tile_scores(const bf16x8 (&qf)[HF][D / 16], const unsigned char* kbuf, int ksub,
                                        int lane) {
   using G = Geo<D, BS, HF>;
   floatx16 acc = {};
@@ -129,7 +129,7 @@ __device__ inline floatx16 tile_scores(const bf16x8 (&qf)[HF][D / 16], const uns
 
 // The Q fragments of 32 query rows starting at token q0 (rows >= S are zero).
 template <int D, int HF>
-__device__ inline void load_q(const TokParams& p, int b, int q0, int lane, bf16x8 (&qf)[HF][D / 16]) {
+__device__ __forceinline__ void load_q(const TokParams& p, int b, int q0, int lane, bf16x8 (&qf)[HF][D / 16]) {
   const int r = q0 + (lane & 31), half = lane >> 5;
 #pragma unroll
   for (int h = 0; h < HF; ++h) {
@@ -152,7 +152,7 @@ struct Stager {
   static constexpr int CHUNKS = HF * BS * (D / 8);
   static constexpr int PER = (CHUNKS + kThreads - 1) / kThreads;
   u32x4 v[PER];
-  __device__ inline void load(const TokParams& p, int b, int kb, int tid) {
+  __device__ __forceinline__ void load(const TokParams& p, int b, int kb, int tid) {
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
       const int c = tid + j * kThreads;
@@ -167,7 +167,7 @@ struct Stager {
       }
     }
   }
-  __device__ inline void store(unsigned char* buf, int tid) const {
+  __device__ __forceinline__ void store(unsigned char* buf, int tid) const {
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
       const int c = tid + j * kThreads;
@@ -190,7 +190,7 @@ struct TileFrames {
   bool kvalid;
 };
 
-__device__ inline TileFrames tile_frames(const TokParams& p, int q0, int ktok) {
+__device__ __forceinline__ TileFrames tile_frames(const TokParams& p, int q0, int ktok) {
   TileFrames f;
   f.f0 = q0 / p.Nt;
   f.u0 = q0 - f.f0 * p.Nt;
@@ -201,13 +201,41 @@ __device__ inline TileFrames tile_frames(const TokParams& p, int q0, int ktok) {
 }
 
 // Row i of the lane: query token q0 + r, r = 8*(i/4) + 4*half + i%4.
-__device__ inline int row_of(int i, int half) { return 8 * (i >> 2) + 4 * half + (i & 3); }
+__device__ __forceinline__ int row_of(int i, int half) { return 8 * (i >> 2) + 4 * half + (i & 3); }
+
+// A 32x32 tile (query tokens q0.., key tokens k0..) lying inside one query
+// frame and one key frame, away from the sequence end, has one frame distance
+// t for all its pairs; then its pairs are all or none in P(i, j) unless the
+// window edge cuts it. Computed in scalar registers.
+enum TileClass { kGeneral = 0, kNone = 1, kAllNear = 2, kAllScored = 3 };
+struct TileInfo {
+  int cls, fq, fk;
+};
+__device__ __forceinline__ TileInfo classify(const TokParams& p, int q0, int k0, const int* s_w, const int* s_sf) {
+  TileInfo ti{kGeneral, 0, 0};
+  if (q0 + 31 >= p.S || k0 + 31 >= p.S) return ti;
+  const int fq = q0 / p.Nt, fk = k0 / p.Nt;
+  if ((q0 + 31) / p.Nt != fq || (k0 + 31) / p.Nt != fk) return ti;
+  ti.fq = fq;
+  ti.fk = fk;
+  const int t = fq > fk ? fq - fk : fk - fq;
+  if (t % s_sf[t] != 0) {
+    ti.cls = kNone;
+    return ti;
+  }
+  const int uq = q0 - fq * p.Nt, uk = k0 - fk * p.Nt, w = s_w[t];
+  const int dmax = max(uq + 31 - uk, uk + 31 - uq);                  // largest |u - v| in the tile
+  const int dmin = max(0, max(uk - (uq + 31), uq - (uk + 31)));      // smallest
+  if (dmin > w) ti.cls = kNone;
+  else if (dmax <= w) ti.cls = t <= 1 ? kAllNear : kAllScored;
+  return ti;
+}
 
 // Selection bits (one per element i) of a tile under the thresholds of the
 // frame pairs involved; inP bits mark the candidate pairs of P with t > 1.
 // thr0 / thr1: thresholds (score units) for query frame f0 / f0 + 1 against
 // the lane's key frame. w/sf: per-distance table in LDS.
-__device__ inline void select_bits(const TokParams& p, const floatx16& acc, const TileFrames& f, int q0, int half,
+__device__ __forceinline__ void select_bits(const TokParams& p, const floatx16& acc, const TileFrames& f, int q0, int half,
                                    const int* s_w, const int* s_sf, float thr0, float thr1, unsigned& sel,
                                    unsigned& inP2) {
   sel = 0;
@@ -245,7 +273,7 @@ struct WalkState {
 };
 
 // Union step j -> key block (j increasing across calls).
-__device__ inline int block_of_step(const unsigned int* uword, WalkState& s, int j) {
+__device__ __forceinline__ int block_of_step(const unsigned int* uword, WalkState& s, int j) {
   while (true) {
     const int n = __popc(s.cur_bits);
     if (j < s.cur_step + n) {
@@ -297,7 +325,7 @@ struct Lds {
 // candidate bitmaps of the workgroup's query blocks with their CSR word
 // prefixes, and the union bitmap. Returns the number of union steps.
 template <int D, int BS, int HF>
-__device__ int setup(const TokParams& p, Lds<D, BS, HF>& L, int a0, int* s_nsteps) {
+__device__ __forceinline__ int setup(const TokParams& p, Lds<D, BS, HF>& L, int a0, int* s_nsteps) {
   using G = Geo<D, BS, HF>;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   for (int t = tid; t < p.Nf; t += kThreads) {
@@ -402,7 +430,34 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(TokParams p) {
       for (int ksub = 0; ksub < BS / 32; ++ksub) {
         const int ktok0 = kb * BS + 32 * ksub;
         if (ktok0 >= p.S) break;
+        const TileInfo ti = classify(p, q0, ktok0, L.s_w, L.s_sf);
+        if (ti.cls == kNone || ti.cls == kAllNear) continue;      // no t > 1 pair of P
         const floatx16 acc = tile_scores<D, BS, HF>(qf, kbuf, ksub, lane);
+        if (ti.cls == kAllScored) {
+          // all 1024 pairs in P(fq, fk): one slot, no masks
+          float s = 0.f;
+          unsigned long long mx = 0ull;
+          const int uk = ktok0 + (lane & 31) - ti.fk * p.Nt;
+          const int uq0 = q0 - ti.fq * p.Nt;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const float v = acc[i] * p.scale;
+            s += v;
+            const unsigned long long key = pack_max(v, (unsigned)((uq0 + row_of(i, half)) * p.Nt + uk));
+            mx = key > mx ? key : mx;
+          }
+          const double mean = wave_sum((double)s) / 1024.0;
+          float m2 = 0.f;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const float d = (float)((double)(acc[i] * p.scale) - mean);
+            m2 += d * d;
+          }
+          const double m2t = wave_sum((double)m2);
+          mx = wave_max(mx);
+          if (lane == 0) merge(mine[(ti.fq - f0w) * p.Nf + ti.fk], 1024.0, mean, m2t, mx);
+          continue;
+        }
         const TileFrames f = tile_frames(p, q0, ktok0 + (lane & 31));
         // t > 1 candidate pairs of P, split by (query frame f0w + fo, key frame fk0 + ko)
         const int fk0 = ktok0 / p.Nt;
@@ -521,7 +576,7 @@ __global__ __launch_bounds__(256) void reduce_kernel(TokParams p) {
 }
 
 // Decision of one block pair from per-key-token selected counts.
-__device__ inline bool block_kept(const TokParams& p, const int* cnt, int nq, int nk) {
+__device__ __forceinline__ bool block_kept(const TokParams& p, const int* cnt, int nq, int nk) {
   int act = 0;
   for (int c = 0; c < nk; ++c) act += ((double)cnt[c] / (double)nq) > p.theta_c ? 1 : 0;
   return ((double)act / (double)nk) > p.theta_m;
@@ -595,7 +650,25 @@ __global__ __launch_bounds__(kThreads) void mark_kernel(TokParams p) {
       for (int ksub = 0; ksub < BS / 32; ++ksub) {
         const int ktok0 = kb * BS + 32 * ksub;
         if (ktok0 >= p.S) break;
+        const TileInfo ti = classify(p, q0, ktok0, L.s_w, L.s_sf);
+        if (ti.cls == kNone) continue;                              // nothing selected
+        if (ti.cls == kAllNear) {                                   // everything selected
+          if (half == 0) atomicAdd(&cnt[32 * ksub + lane], 32);
+          continue;
+        }
         const floatx16 acc = tile_scores<D, BS, HF>(qf, kbuf, ksub, lane);
+        if (ti.cls == kAllScored) {
+          const float thr = thr_l[(ti.fq - f_lo) * p.Nf + ti.fk];
+          unsigned sel = 0;
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            if (acc[i] * p.scale >= thr) sel |= 1u << i;
+          if (__ballot(sel != 0u) != 0ull && lane == 0) p.served[(size_t)b * p.Nf * p.Nf + (size_t)ti.fq * p.Nf + ti.fk] = 1;
+          int c = __popc(sel);
+          c += __shfl_xor(c, 32);
+          if (half == 0) atomicAdd(&cnt[32 * ksub + lane], c);
+          continue;
+        }
         const TileFrames f = tile_frames(p, q0, ktok0 + (lane & 31));
         const float thr0 = f.kvalid ? thr_l[(f.f0 - f_lo) * p.Nf + f.fk] : INFINITY;
         const float thr1 = (f.kvalid && f.f0 + 1 - f_lo < p.FR) ? thr_l[(f.f0 + 1 - f_lo) * p.Nf + f.fk] : INFINITY;
