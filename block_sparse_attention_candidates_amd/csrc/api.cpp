@@ -132,7 +132,7 @@ TokWs tok_ws(const dr_dims* d, const dr_radial_cfg* c, int Sb, long long S, long
   const size_t fpairs = (size_t)d->batch * Nf * Nf;
   size_t off = 0;
   w.part = off;
-  off = align256(off + (size_t)d->batch * w.n_wg * w.FR * Nf * sizeof(dr::TokStat));
+  off = align256(off + (size_t)d->batch * w.n_wg * dr::kTokSplit * w.FR * Nf * sizeof(dr::TokStat));
   w.thr = off;
   off = align256(off + fpairs * sizeof(float));
   w.fmax = off;

@@ -106,6 +106,7 @@ struct AttnParams {
 
 // Token-level dynamic-threshold selection ([DR] §3.2 Eqs. 9-11).
 constexpr int kMaxTokenFrames = 64;  // N_f limit of the token-level mode (LDS statistics)
+constexpr int kTokSplit = 4;         // workgroups sharing one query group's walk of key blocks
 
 // Statistics of a set of scores: count, mean, sum of squared deviations, and
 // the highest score packed with its position ((order key << 32) | ~position).
@@ -128,7 +129,7 @@ struct TokParams {
   double gamma, lambda, theta_c, theta_m, tau_near, tau_far, eps;
   float scale;         // 1 / (sqrt(d_k) * H_f)
   // workspace
-  TokStat* part;       // [B][n_wg][FR][Nf] workgroup partials
+  TokStat* part;       // [B][n_wg][kTokSplit][FR][Nf] workgroup partials
   float* thr;          // [B][Nf][Nf] threshold in score units (+inf: no t > 1 pair)
   unsigned long long* fmax;  // [B][Nf][Nf] highest score and position
   double* fn;          // [B][Nf][Nf] size of P(i, j) for t > 1 (0: none)

@@ -267,26 +267,6 @@ __device__ __forceinline__ void select_bits(const TokParams& p, const floatx16& 
   }
 }
 
-struct WalkState {
-  int cur_wi, cur_step;
-  unsigned int cur_bits;
-};
-
-// Union step j -> key block (j increasing across calls).
-__device__ __forceinline__ int block_of_step(const unsigned int* uword, WalkState& s, int j) {
-  while (true) {
-    const int n = __popc(s.cur_bits);
-    if (j < s.cur_step + n) {
-      unsigned int m = s.cur_bits;
-      for (int t = s.cur_step; t < j; ++t) m &= m - 1;
-      return s.cur_wi * 32 + __ffs(m) - 1;
-    }
-    s.cur_step += n;
-    ++s.cur_wi;
-    s.cur_bits = uword[s.cur_wi];
-  }
-}
-
 // LDS layout shared by the stats and mark kernels: key staging (2 buffers),
 // per-query-block candidate bitmaps and their CSR word prefixes, the union
 // bitmap, and the per-distance table; then kernel-specific areas.
@@ -298,10 +278,13 @@ struct Lds {
   unsigned int* bits;   // [QB][nword]
   int* pre;             // [QB][nword]
   unsigned int* uword;  // [nword]
+  int* upre;            // [nword] exclusive prefix of the union popcounts (union step of each word)
+  int* steps;           // [Sb / kTokSplit + 2] key blocks of this workgroup's union steps
   int* s_w;             // [Nf]
   int* s_sf;            // [Nf]
   unsigned char* rest;  // 16-byte aligned
   __host__ __device__ static size_t align16(size_t x) { return (x + 15) & ~(size_t)15; }
+  __host__ __device__ static int max_steps(int Sb) { return Sb / kTokSplit + 2; }
   __device__ Lds(unsigned char* smem, int Sb, int Nf) {
     nword = (Sb + 31) >> 5;
     kbuf[0] = smem;
@@ -309,23 +292,45 @@ struct Lds {
     bits = reinterpret_cast<unsigned int*>(smem + 2 * G::KBUF);
     pre = reinterpret_cast<int*>(bits + G::QB * nword);
     uword = reinterpret_cast<unsigned int*>(pre + G::QB * nword);
-    s_w = reinterpret_cast<int*>(uword + nword);
+    upre = reinterpret_cast<int*>(uword + nword);
+    steps = upre + nword;
+    s_w = steps + max_steps(Sb);
     s_sf = s_w + Nf;
     const size_t used = (size_t)(reinterpret_cast<unsigned char*>(s_sf + Nf) - smem);
     rest = smem + align16(used);
   }
   __host__ __device__ static size_t bytes(int Sb, int Nf) {
     const size_t nw = (size_t)(Sb + 31) / 32;
-    const size_t used = 2 * (size_t)G::KBUF + (size_t)G::QB * nw * 8 + nw * 4 + (size_t)Nf * 8;
+    const size_t used = 2 * (size_t)G::KBUF + (size_t)G::QB * nw * 8 + nw * 8 + (size_t)max_steps(Sb) * 4 +
+                        (size_t)Nf * 8;
     return (used + 15) & ~(size_t)15;
   }
 };
 
+// First union step of key-range split `split` (kTokSplit workgroups share one
+// query group's walk, each taking a contiguous run of its steps).
+__device__ __forceinline__ int step_begin(int nsteps, int split) {
+  return (int)(((long long)nsteps * split) / kTokSplit);
+}
+
+// Exclusive prefix sum over a wavefront (lane order); returns the total.
+__device__ __forceinline__ int wave_scan(int c, int lane, int* excl) {
+  int incl = c;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(incl, off);
+    if (lane >= off) incl += o;
+  }
+  *excl = incl - c;
+  return __shfl(incl, 63);
+}
+
 // Setup shared by the stats and mark kernels: the per-distance table, the
 // candidate bitmaps of the workgroup's query blocks with their CSR word
-// prefixes, and the union bitmap. Returns the number of union steps.
+// prefixes, the union bitmap, and the key blocks of this split's union steps
+// in ascending order. Returns their number.
 template <int D, int BS, int HF>
-__device__ __forceinline__ int setup(const TokParams& p, Lds<D, BS, HF>& L, int a0, int* s_nsteps) {
+__device__ __forceinline__ int setup(const TokParams& p, Lds<D, BS, HF>& L, int a0, int split, int* s_nsteps) {
   using G = Geo<D, BS, HF>;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   for (int t = tid; t < p.Nf; t += kThreads) {
@@ -356,31 +361,36 @@ __device__ __forceinline__ int setup(const TokParams& p, Lds<D, BS, HF>& L, int 
     int run = 0;
     for (int w0 = 0; w0 < L.nword; w0 += 64) {
       const int wi = w0 + lane;
-      const int c = wi < L.nword ? __popc(L.bits[qb * L.nword + wi]) : 0;
-      int incl = c;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const int o = __shfl_up(incl, off);
-        if (lane >= off) incl += o;
-      }
-      if (wi < L.nword) L.pre[qb * L.nword + wi] = run + incl - c;
-      run += __shfl(incl, 63);
+      int excl;
+      const int tot = wave_scan(wi < L.nword ? __popc(L.bits[qb * L.nword + wi]) : 0, lane, &excl);
+      if (wi < L.nword) L.pre[qb * L.nword + wi] = run + excl;
+      run += tot;
     }
   }
   __syncthreads();
   if (wave == 0) {
-    int tot = 0;
+    int run = 0;
     for (int w0 = 0; w0 < L.nword; w0 += 64) {
       const int wi = w0 + lane;
-      int c = wi < L.nword ? __popc(L.uword[wi]) : 0;
-#pragma unroll
-      for (int off = 32; off > 0; off >>= 1) c += __shfl_xor(c, off);
-      tot += c;
+      int excl;
+      const int tot = wave_scan(wi < L.nword ? __popc(L.uword[wi]) : 0, lane, &excl);
+      if (wi < L.nword) L.upre[wi] = run + excl;
+      run += tot;
     }
-    if (lane == 0) *s_nsteps = tot;
+    if (lane == 0) *s_nsteps = run;
   }
   __syncthreads();
-  return *s_nsteps;
+  const int nsteps = *s_nsteps;
+  const int j0 = step_begin(nsteps, split), j1 = step_begin(nsteps, split + 1);
+  for (int wi = tid; wi < L.nword; wi += kThreads) {
+    unsigned int u = L.uword[wi];
+    int j = L.upre[wi];
+    if (j >= j1 || j + __popc(u) <= j0) continue;
+    for (; u != 0u; u &= u - 1u, ++j)
+      if (j >= j0 && j < j1) L.steps[j - j0] = wi * 32 + __ffs(u) - 1;
+  }
+  __syncthreads();
+  return j1 - j0;
 }
 
 // ---------------------------------------------------------------------------
@@ -394,10 +404,10 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(TokParams p) {
   Lds<D, BS, HF> L(smem, p.Sb, p.Nf);
   Stat* acc_l = reinterpret_cast<Stat*>(L.rest);     // [kWaves][2][Nf]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5;
-  const int wg = blockIdx.x, b = blockIdx.y;
+  const int wg = blockIdx.x / kTokSplit, split = blockIdx.x - wg * kTokSplit, b = blockIdx.y;
   const int a0 = wg * G::QB;
   for (int i = tid; i < kWaves * 2 * p.Nf; i += kThreads) acc_l[i] = Stat{0.0, 0.0, 0.0, 0ull};
-  const int nsteps = setup<D, BS, HF>(p, L, a0, &s_nsteps);
+  const int n = setup<D, BS, HF>(p, L, a0, split, &s_nsteps);
 
   const int qb = wave / G::WPQ, sub = wave - qb * G::WPQ;
   const int a = a0 + qb;
@@ -408,21 +418,65 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(TokParams p) {
   const int f0w = q0 / p.Nt;
   Stat* mine = acc_l + wave * 2 * p.Nf;
 
-  WalkState ws{0, 0, L.uword[0]};
+  // Per-lane running statistics, four sets: query frame f0w + fo (the wave's
+  // 32 rows span at most two frames) x key frame parity kp. Keys are walked in
+  // ascending order and the 32 keys of a tile span at most two adjacent frames,
+  // so the set of parity kp holds one key frame, tag[kp], at a time; it is
+  // reduced over the wave and merged into the wave's LDS statistics once the
+  // walk has passed that frame. Sums are float64 power sums of the float32
+  // scores; the highest score keeps its position for safeguard (ii).
+  double rs[4] = {0.0, 0.0, 0.0, 0.0}, rq[4] = {0.0, 0.0, 0.0, 0.0};
+  int rn[4] = {0, 0, 0, 0};
+  float rm[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+  unsigned int rl[4] = {0xffffffffu, 0xffffffffu, 0xffffffffu, 0xffffffffu};
+  int tag[2] = {-1, -1};
+  auto flush = [&](int kp) {
+    if (tag[kp] < 0) return;
+#pragma unroll
+    for (int fo = 0; fo < 2; ++fo) {
+      const int x = 2 * fo + kp;
+      int cnt = rn[x];
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) cnt += __shfl_xor(cnt, off);
+      if (cnt > 0) {
+        const double sum = wave_sum(rs[x]), sq = wave_sum(rq[x]);
+        const unsigned long long mx = wave_max(rl[x] == 0xffffffffu ? 0ull : pack_max(rm[x], rl[x]));
+        const double nn = (double)cnt, mean = sum / nn;
+        double m2 = sq - sum * mean;
+        if (m2 < 0.0) m2 = 0.0;
+        if (lane == 0) merge(mine[fo * p.Nf + tag[kp]], nn, mean, m2, mx);
+      }
+      rs[x] = rq[x] = 0.0;
+      rn[x] = 0;
+      rm[x] = -INFINITY;
+      rl[x] = 0xffffffffu;
+    }
+    tag[kp] = -1;
+  };
+  // add a lane's tile sums to set x (x may differ between lanes)
+  auto add = [&](int x, double ts, double tq, int tn, float tm, unsigned int tl) {
+#pragma unroll
+    for (int y = 0; y < 4; ++y)
+      if (y == x) {
+        rs[y] += ts;
+        rq[y] += tq;
+        rn[y] += tn;
+        if (tm > rm[y] || (tm == rm[y] && tl < rl[y])) {
+          rm[y] = tm;
+          rl[y] = tl;
+        }
+      }
+  };
+
   Stager<D, BS, HF> st;
-  if (nsteps > 0) {
-    st.load(p, b, block_of_step(L.uword, ws, 0), tid);
+  if (n > 0) {
+    st.load(p, b, L.steps[0], tid);
     st.store(L.kbuf[0], tid);
   }
   __syncthreads();
-  for (int j = 0; j < nsteps; ++j) {
-    const int kb = uniform(block_of_step(L.uword, ws, j));
-    int kb_next = -1;
-    if (j + 1 < nsteps) {
-      WalkState w2 = ws;
-      kb_next = uniform(block_of_step(L.uword, w2, j + 1));
-    }
-    st.load(p, b, kb_next, tid);
+  for (int j = 0; j < n; ++j) {
+    const int kb = uniform(L.steps[j]);
+    st.load(p, b, j + 1 < n ? uniform(L.steps[j + 1]) : -1, tid);
     const unsigned char* kbuf = L.kbuf[j & 1];
     const bool need = active_wave && ((L.bits[qb * L.nword + (kb >> 5)] >> (kb & 31)) & 1u);
     if (need) {
@@ -432,90 +486,81 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(TokParams p) {
         if (ktok0 >= p.S) break;
         const TileInfo ti = classify(p, q0, ktok0, L.s_w, L.s_sf);
         if (ti.cls == kNone || ti.cls == kAllNear) continue;      // no t > 1 pair of P
+        // retire the sets whose key frame the walk has passed
+        const int fk_first = ktok0 / p.Nt;
+#pragma unroll
+        for (int kp = 0; kp < 2; ++kp)
+          if (tag[kp] >= 0 && tag[kp] < fk_first) flush(kp);
         const floatx16 acc = tile_scores<D, BS, HF>(qf, kbuf, ksub, lane);
         if (ti.cls == kAllScored) {
-          // all 1024 pairs in P(fq, fk): one slot, no masks
-          float s = 0.f;
-          unsigned long long mx = 0ull;
-          const int uk = ktok0 + (lane & 31) - ti.fk * p.Nt;
-          const int uq0 = q0 - ti.fq * p.Nt;
+          // all 1024 pairs in P(fq, fk): one set, no masks
+          tag[ti.fk & 1] = ti.fk;
+          float v[16], m = -INFINITY;
+          double ts = 0.0, tq = 0.0;
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
-            const float v = acc[i] * p.scale;
-            s += v;
-            const unsigned long long key = pack_max(v, (unsigned)((uq0 + row_of(i, half)) * p.Nt + uk));
-            mx = key > mx ? key : mx;
+            v[i] = acc[i] * p.scale;
+            const double d = (double)v[i];
+            ts += d;
+            tq = fma(d, d, tq);
+            m = fmaxf(m, v[i]);
           }
-          const double mean = wave_sum((double)s) / 1024.0;
-          float m2 = 0.f;
+          // first of the lane's rows reaching m: rows ascend with i, and so
+          // does the position u * N_t + v
+          int first = 15;
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const float d = (float)((double)(acc[i] * p.scale) - mean);
-            m2 += d * d;
-          }
-          const double m2t = wave_sum((double)m2);
-          mx = wave_max(mx);
-          if (lane == 0) merge(mine[(ti.fq - f0w) * p.Nf + ti.fk], 1024.0, mean, m2t, mx);
+          for (int i = 15; i >= 0; --i)
+            if (v[i] == m) first = i;
+          const unsigned int loc = (unsigned)((q0 - ti.fq * p.Nt + row_of(first, half)) * p.Nt +
+                                              (ktok0 + (lane & 31) - ti.fk * p.Nt));
+          add(2 * (ti.fq - f0w) + (ti.fk & 1), ts, tq, 16, m, loc);
           continue;
         }
+        // general tile: pairs split by query frame f0 + fo and the lane's key frame
         const TileFrames f = tile_frames(p, q0, ktok0 + (lane & 31));
-        // t > 1 candidate pairs of P, split by (query frame f0w + fo, key frame fk0 + ko)
-        const int fk0 = ktok0 / p.Nt;
+        tag[fk_first & 1] = fk_first;
+        if ((min(ktok0 + 31, p.S - 1)) / p.Nt != fk_first) tag[(fk_first + 1) & 1] = fk_first + 1;
         const int t0 = f.f0 > f.fk ? f.f0 - f.fk : f.fk - f.f0;
         const int t1 = f.f0 + 1 > f.fk ? f.f0 + 1 - f.fk : f.fk - f.f0 - 1;
         const bool ok0 = f.kvalid && t0 > 1 && t0 < p.Nf && (t0 % L.s_sf[t0]) == 0;
         const bool ok1 = f.kvalid && t1 > 1 && t1 < p.Nf && (t1 % L.s_sf[t1]) == 0;
         const int w0 = t0 < p.Nf ? L.s_w[t0] : 0, w1 = t1 < p.Nf ? L.s_w[t1] : 0;
-        float sv[16];
-        unsigned slot_bits[2] = {0u, 0u};   // element bits in P, per query frame
+        double ts[2] = {0.0, 0.0}, tq[2] = {0.0, 0.0};
+        int tn[2] = {0, 0};
+        float tm[2] = {-INFINITY, -INFINITY};
+        unsigned int tl[2] = {0xffffffffu, 0xffffffffu};
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          sv[i] = acc[i] * p.scale;
           const int r = row_of(i, half);
           if (q0 + r >= p.S) continue;
           int u = f.u0 + r;
           const bool second = u >= p.Nt;
           if (second) u -= p.Nt;
           const int du = u > f.uk ? u - f.uk : f.uk - u;
-          if (second ? (ok1 && du <= w1) : (ok0 && du <= w0)) slot_bits[second ? 1 : 0] |= 1u << i;
-        }
-        const int ko = f.fk - fk0;   // 0 or 1 (32 keys span at most two frames)
-#pragma unroll
-        for (int fo = 0; fo < 2; ++fo) {
-#pragma unroll
-          for (int kslot = 0; kslot < 2; ++kslot) {
-            const unsigned bitsm = ko == kslot ? slot_bits[fo] : 0u;
-            if (__ballot(bitsm != 0u) == 0ull) continue;
-            double n = (double)__popc(bitsm), s = 0.0;
-            unsigned long long mx = 0ull;
-            const int fq = f.f0 + fo;
-#pragma unroll
-            for (int i = 0; i < 16; ++i)
-              if ((bitsm >> i) & 1u) {
-                s += (double)sv[i];
-                int u = f.u0 + row_of(i, half) - fo * p.Nt;
-                const unsigned long long key = pack_max(sv[i], (unsigned)(u * p.Nt + f.uk));
-                mx = key > mx ? key : mx;
-              }
-            const double ntot = wave_sum(n);
-            const double mean = wave_sum(s) / ntot;
-            double m2 = 0.0;
-#pragma unroll
-            for (int i = 0; i < 16; ++i)
-              if ((bitsm >> i) & 1u) {
-                const double d = (double)sv[i] - mean;
-                m2 += d * d;
-              }
-            m2 = wave_sum(m2);
-            mx = wave_max(mx);
-            if (lane == 0) merge(mine[(fq - f0w) * p.Nf + fk0 + kslot], ntot, mean, m2, mx);
+          if (!(second ? (ok1 && du <= w1) : (ok0 && du <= w0))) continue;
+          const float v = acc[i] * p.scale;
+          const double d = (double)v;
+          const int fo = second ? 1 : 0;
+          ts[fo] += d;
+          tq[fo] = fma(d, d, tq[fo]);
+          tn[fo] += 1;
+          if (v > tm[fo]) {   // rows ascend with i: the first maximum has the lowest position
+            tm[fo] = v;
+            tl[fo] = (unsigned)(u * p.Nt + f.uk);
           }
         }
+        const int kp = f.fk & 1;
+#pragma unroll
+        for (int fo = 0; fo < 2; ++fo)
+          if (tn[fo] > 0) add(2 * fo + kp, ts[fo], tq[fo], tn[fo], tm[fo], tl[fo]);
       }
     }
     st.store(L.kbuf[(j + 1) & 1], tid);
     __syncthreads();
   }
+  flush(0);
+  flush(1);
+  __syncthreads();
   // merge the waves in order into the workgroup partial: [FR][Nf] per workgroup
   const int f_lo = (a0 * BS) / p.Nt;
   for (int i = tid; i < p.FR * p.Nf; i += kThreads) {
@@ -530,7 +575,7 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(TokParams p) {
       const Stat& m = acc_l[(w * 2 + fo) * p.Nf + fk];
       merge(t, m.n, m.mean, m.m2, m.mx);
     }
-    Stat* out = p.part + ((size_t)(b * p.n_wg + wg) * p.FR + fr) * p.Nf + fk;
+    Stat* out = p.part + (((size_t)(b * p.n_wg + wg) * kTokSplit + split) * p.FR + fr) * p.Nf + fk;
     *out = t;
   }
 }
@@ -551,8 +596,10 @@ __global__ __launch_bounds__(256) void reduce_kernel(TokParams p) {
     const int f_lo = (int)(((long long)w * kRows) / p.Nt);
     const int fr = fq - f_lo;
     if (fr < 0 || fr >= p.FR) continue;
-    const Stat& m = p.part[((size_t)(b * p.n_wg + w) * p.FR + fr) * p.Nf + fk];
-    merge(t, m.n, m.mean, m.m2, m.mx);
+    for (int sp = 0; sp < kTokSplit; ++sp) {
+      const Stat& m = p.part[(((size_t)(b * p.n_wg + w) * kTokSplit + sp) * p.FR + fr) * p.Nf + fk];
+      merge(t, m.n, m.mean, m.m2, m.mx);
+    }
   }
   float thr = INFINITY;
   if (t.n > 0.0) {
@@ -582,6 +629,16 @@ __device__ __forceinline__ bool block_kept(const TokParams& p, const int* cnt, i
   return ((double)act / (double)nk) > p.theta_m;
 }
 
+// The same decision by integer thresholds: for n in 1..BS, min_c[n] is the
+// smallest count c with (double) c / n > theta_c (n + 1 if none), min_a[n]
+// likewise for theta_m. A correctly rounded quotient is monotone in c, so
+// c >= min_c[n] holds exactly when the float64 comparison does.
+__device__ __forceinline__ int min_count(int n, double theta) {
+  int c = 0;
+  while (c <= n && !((double)c / (double)n > theta)) ++c;
+  return c;
+}
+
 // ---------------------------------------------------------------------------
 // Pass 3: selection, aggregation to block pairs, one flag per candidate entry.
 // ---------------------------------------------------------------------------
@@ -590,104 +647,118 @@ __global__ __launch_bounds__(kThreads) void mark_kernel(TokParams p) {
   using G = Geo<D, BS, HF>;
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ int s_nsteps;
+  __shared__ int min_c[BS + 1], min_a[BS + 1];
   Lds<D, BS, HF> L(smem, p.Sb, p.Nf);
-  int* colcnt = reinterpret_cast<int*>(L.rest);              // [2][QB][BS]
-  float* thr_l = reinterpret_cast<float*>(colcnt + 2 * G::QB * BS);   // [FR][Nf]
+  float* thr_l = reinterpret_cast<float*>(L.rest);                    // [FR][Nf]
+  int* colcnt = reinterpret_cast<int*>(thr_l + p.FR * p.Nf);          // [2][QB][BS] when BS > 32
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5;
-  const int wg = blockIdx.x, b = blockIdx.y;
+  const int wg = blockIdx.x / kTokSplit, split = blockIdx.x - wg * kTokSplit, b = blockIdx.y;
   const int a0 = wg * G::QB;
   const int f_lo = (a0 * BS) / p.Nt;
-  for (int i = tid; i < 2 * G::QB * BS; i += kThreads) colcnt[i] = 0;
+  if (G::WPQ > 1)
+    for (int i = tid; i < 2 * G::QB * BS; i += kThreads) colcnt[i] = 0;
   for (int i = tid; i < p.FR * p.Nf; i += kThreads) {
     const int fr = i / p.Nf, fk = i - fr * p.Nf;
     const int fq = f_lo + fr;
     thr_l[i] = fq < p.Nf ? p.thr[(size_t)b * p.Nf * p.Nf + (size_t)fq * p.Nf + fk] : INFINITY;
   }
-  const int nsteps = setup<D, BS, HF>(p, L, a0, &s_nsteps);
+  for (int n = 1 + tid; n <= BS; n += kThreads) {
+    min_c[n] = min_count(n, p.theta_c);
+    min_a[n] = min_count(n, p.theta_m);
+  }
+  const int n = setup<D, BS, HF>(p, L, a0, split, &s_nsteps);
 
   const int qb = wave / G::WPQ, sub = wave - qb * G::WPQ;
   const int a = a0 + qb;
   const int q0 = a * BS + 32 * sub;
   const bool active_wave = a < p.Sb && q0 < p.S;
+  const int nq = a < p.Sb ? min(BS, p.S - a * BS) : 0;
   bf16x8 qf[HF][D / 16];
   if (active_wave) load_q<D, HF>(p, b, q0, lane, qf);
 
-  WalkState ws{0, 0, L.uword[0]};
+  // flag of candidate entry (a, kb): its CSR position from the bitmap prefix
+  auto flag_of = [&](int kb) -> unsigned char* {
+    const int wi = kb >> 5;
+    const long long e = p.row_ptr[a] + L.pre[qb * L.nword + wi] +
+                        __popc(L.bits[qb * L.nword + wi] & ((1u << (kb & 31)) - 1u));
+    return p.flags + (long long)b * p.nnz + e;
+  };
+  // selected count of key column lane % 32 of the tile (q0, ktok0) over the
+  // wave's 32 query rows (the same value in both half-waves); marks served
+  // frame pairs
+  auto tile_count = [&](const unsigned char* kbuf, int ksub, int ktok0) -> int {
+    const TileInfo ti = classify(p, q0, ktok0, L.s_w, L.s_sf);
+    if (ti.cls == kNone) return 0;
+    if (ti.cls == kAllNear) return 32;
+    const floatx16 acc = tile_scores<D, BS, HF>(qf, kbuf, ksub, lane);
+    unsigned sel = 0;
+    if (ti.cls == kAllScored) {
+      const float thr = thr_l[(ti.fq - f_lo) * p.Nf + ti.fk];
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (acc[i] * p.scale >= thr) sel |= 1u << i;
+      if (__ballot(sel != 0u) != 0ull && lane == 0) p.served[(size_t)b * p.Nf * p.Nf + (size_t)ti.fq * p.Nf + ti.fk] = 1;
+    } else {
+      const TileFrames f = tile_frames(p, q0, ktok0 + (lane & 31));
+      const float thr0 = f.kvalid ? thr_l[(f.f0 - f_lo) * p.Nf + f.fk] : INFINITY;
+      const float thr1 = (f.kvalid && f.f0 + 1 - f_lo < p.FR) ? thr_l[(f.f0 + 1 - f_lo) * p.Nf + f.fk] : INFINITY;
+      unsigned inP2;
+      select_bits(p, acc, f, q0, half, L.s_w, L.s_sf, thr0, thr1, sel, inP2);
+      // frame pairs with a selected t > 1 pair are served
+      const unsigned s2 = sel & inP2;
+      if (s2) {
+        for (int i = 0; i < 16; ++i)
+          if ((s2 >> i) & 1u) {
+            int u = f.u0 + row_of(i, half);
+            const int fq = f.f0 + (u >= p.Nt ? 1 : 0);
+            p.served[(size_t)b * p.Nf * p.Nf + (size_t)fq * p.Nf + f.fk] = 1;
+          }
+      }
+    }
+    const int c = __popc(sel);
+    return c + __shfl_xor(c, 32);
+  };
+
   Stager<D, BS, HF> st;
-  if (nsteps > 0) {
-    st.load(p, b, block_of_step(L.uword, ws, 0), tid);
+  if (n > 0) {
+    st.load(p, b, L.steps[0], tid);
     st.store(L.kbuf[0], tid);
   }
   __syncthreads();
   int kb_prev = -1;
-  for (int j = 0; j <= nsteps; ++j) {
-    // decide step j - 1 (its counts are complete after the barrier)
-    if (kb_prev >= 0 && sub == 0 && a < p.Sb && lane == 0) {
-      int* cnt = colcnt + ((j - 1) & 1) * G::QB * BS + qb * BS;
-      if ((L.bits[qb * L.nword + (kb_prev >> 5)] >> (kb_prev & 31)) & 1u) {
-        const int nq = min(BS, p.S - a * BS), nk = min(BS, p.S - kb_prev * BS);
-        const bool keep = block_kept(p, cnt, nq, nk);
-        const int wi = kb_prev >> 5;
-        const long long e = p.row_ptr[a] + L.pre[qb * L.nword + wi] +
-                            __popc(L.bits[qb * L.nword + wi] & ((1u << (kb_prev & 31)) - 1u));
-        p.flags[(long long)b * p.nnz + e] = keep ? 1 : 0;
+  for (int j = 0; j <= n; ++j) {
+    if (G::WPQ > 1) {
+      // decide step j - 1 from the counts of all its waves (complete after the barrier)
+      if (kb_prev >= 0 && sub == 0 && a < p.Sb && ((L.bits[qb * L.nword + (kb_prev >> 5)] >> (kb_prev & 31)) & 1u)) {
+        int* cnt = colcnt + ((j - 1) & 1) * G::QB * BS + qb * BS;
+        const int nk = min(BS, p.S - kb_prev * BS);
+        const int c = lane < BS ? cnt[lane] : 0;
+        const int n_act = __popcll(__ballot(lane < nk && c >= min_c[nq]));
+        if (lane == 0) *flag_of(kb_prev) = n_act >= min_a[nk] ? 1 : 0;
+        if (lane < BS) cnt[lane] = 0;
       }
-      for (int c = 0; c < BS; ++c) cnt[c] = 0;
     }
-    if (j == nsteps) break;
-    const int kb = uniform(block_of_step(L.uword, ws, j));
-    int kb_next = -1;
-    if (j + 1 < nsteps) {
-      WalkState w2 = ws;
-      kb_next = uniform(block_of_step(L.uword, w2, j + 1));
-    }
-    st.load(p, b, kb_next, tid);
+    if (j == n) break;
+    const int kb = uniform(L.steps[j]);
+    st.load(p, b, j + 1 < n ? uniform(L.steps[j + 1]) : -1, tid);
     const unsigned char* kbuf = L.kbuf[j & 1];
     const bool need = active_wave && ((L.bits[qb * L.nword + (kb >> 5)] >> (kb & 31)) & 1u);
     if (need) {
-      int* cnt = colcnt + (j & 1) * G::QB * BS + qb * BS;
+      if (G::WPQ == 1) {
+        // one wave holds the whole block pair: decide in registers
+        const int nk = min(BS, p.S - kb * BS);
+        const int c = tile_count(kbuf, 0, kb * BS);
+        const int n_act = __popcll(__ballot(lane < nk && c >= min_c[nq]));
+        if (lane == 0) *flag_of(kb) = n_act >= min_a[nk] ? 1 : 0;
+      } else {
+        int* cnt = colcnt + (j & 1) * G::QB * BS + qb * BS;
 #pragma unroll
-      for (int ksub = 0; ksub < BS / 32; ++ksub) {
-        const int ktok0 = kb * BS + 32 * ksub;
-        if (ktok0 >= p.S) break;
-        const TileInfo ti = classify(p, q0, ktok0, L.s_w, L.s_sf);
-        if (ti.cls == kNone) continue;                              // nothing selected
-        if (ti.cls == kAllNear) {                                   // everything selected
-          if (half == 0) atomicAdd(&cnt[32 * ksub + lane], 32);
-          continue;
-        }
-        const floatx16 acc = tile_scores<D, BS, HF>(qf, kbuf, ksub, lane);
-        if (ti.cls == kAllScored) {
-          const float thr = thr_l[(ti.fq - f_lo) * p.Nf + ti.fk];
-          unsigned sel = 0;
-#pragma unroll
-          for (int i = 0; i < 16; ++i)
-            if (acc[i] * p.scale >= thr) sel |= 1u << i;
-          if (__ballot(sel != 0u) != 0ull && lane == 0) p.served[(size_t)b * p.Nf * p.Nf + (size_t)ti.fq * p.Nf + ti.fk] = 1;
-          int c = __popc(sel);
-          c += __shfl_xor(c, 32);
+        for (int ksub = 0; ksub < BS / 32; ++ksub) {
+          const int ktok0 = kb * BS + 32 * ksub;
+          if (ktok0 >= p.S) break;
+          const int c = tile_count(kbuf, ksub, ktok0);
           if (half == 0) atomicAdd(&cnt[32 * ksub + lane], c);
-          continue;
         }
-        const TileFrames f = tile_frames(p, q0, ktok0 + (lane & 31));
-        const float thr0 = f.kvalid ? thr_l[(f.f0 - f_lo) * p.Nf + f.fk] : INFINITY;
-        const float thr1 = (f.kvalid && f.f0 + 1 - f_lo < p.FR) ? thr_l[(f.f0 + 1 - f_lo) * p.Nf + f.fk] : INFINITY;
-        unsigned sel, inP2;
-        select_bits(p, acc, f, q0, half, L.s_w, L.s_sf, thr0, thr1, sel, inP2);
-        // frame pairs with a selected t > 1 pair are served
-        const unsigned s2 = sel & inP2;
-        if (s2) {
-          for (int i = 0; i < 16; ++i)
-            if ((s2 >> i) & 1u) {
-              int u = f.u0 + row_of(i, half);
-              const int fq = f.f0 + (u >= p.Nt ? 1 : 0);
-              p.served[(size_t)b * p.Nf * p.Nf + (size_t)fq * p.Nf + f.fk] = 1;
-            }
-        }
-        // selected count of this lane's key column over the wave's 32 rows
-        int c = __popc(sel);
-        c += __shfl_xor(c, 32);
-        if (half == 0) atomicAdd(&cnt[32 * ksub + lane], c);
       }
     }
     st.store(L.kbuf[(j + 1) & 1], tid);
@@ -828,9 +899,8 @@ hipError_t launch_all(const TokParams& p, int B, hipStream_t stream) {
   using G = Geo<D, BS, HF>;
   const size_t base = Lds<D, BS, HF>::bytes(p.Sb, p.Nf);
   const size_t lds_stats = base + (size_t)kWaves * 2 * p.Nf * sizeof(Stat);
-  const size_t lds_mark = base + (size_t)2 * G::QB * BS * 4 + (size_t)p.FR * p.Nf * 4;
-  (void)sizeof(G);
-  const dim3 grid((unsigned)p.n_wg, (unsigned)B);
+  const size_t lds_mark = base + (size_t)p.FR * p.Nf * 4 + (G::WPQ > 1 ? (size_t)2 * G::QB * BS * 4 : 0);
+  const dim3 grid((unsigned)(p.n_wg * kTokSplit), (unsigned)B);
   hipLaunchKernelGGL((stats_kernel<D, BS, HF>), grid, dim3(kThreads), lds_stats, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -853,7 +923,9 @@ size_t lds_need(int Sb, int Nf, int FR) {
   using G = Geo<D, BS, HF>;
   const size_t base = Lds<D, BS, HF>::bytes(Sb, Nf);
   const size_t stats = base + (size_t)kWaves * 2 * Nf * sizeof(Stat);
-  const size_t mark = base + (size_t)2 * G::QB * BS * 4 + (size_t)FR * Nf * 4;
+  // (+ the static arrays of the mark kernel: the integer thresholds and the step count)
+  const size_t mark = base + (size_t)FR * Nf * 4 + (G::WPQ > 1 ? (size_t)2 * G::QB * BS * 4 : 0) +
+                      (size_t)2 * (BS + 1) * 4 + 16;
   return stats > mark ? stats : mark;
 }
 

@@ -148,9 +148,9 @@ def test_token_select_validation(dynrad_lib):
     size = ctypes.c_size_t(0)
     assert dynrad_lib.dr_token_select_workspace(ctypes.byref(dims), ctypes.byref(cfg), ctypes.byref(tok), 64,
                                                 ctypes.byref(size)) == L.DR_OK
-    # partials: 1 workgroup x FR (255 // 64 + 2 = 5) x N_f 4 x 32 B = 640 -> 768; thr 64 B -> 256;
-    # maxima 128 B -> 256; counts 128 B -> 256; served 64 B -> 256; flags 64 B -> 256
-    assert size.value == 768 + 5 * 256
+    # partials: 1 workgroup x 4 key-range splits x FR (255 // 64 + 2 = 5) x N_f 4 x 32 B = 2560;
+    # thr 64 B -> 256; maxima 128 B -> 256; counts 128 B -> 256; served 64 B -> 256; flags 64 B -> 256
+    assert size.value == 2560 + 5 * 256
 
     def ts(d=dims, c=cfg, t=tok, nnz=64, ws_bytes=1 << 20, q=FAKE):
         return dynrad_lib.dr_token_select(ctypes.byref(d), ctypes.byref(c), ctypes.byref(t), q, FAKE, FAKE, FAKE,
