@@ -39,6 +39,7 @@
 // MFMA operand reads of a wave hit distinct banks); the loaders pick, per lane,
 // the global chunk that belongs at each physical position.
 #include "dr_internal.h"
+#include "lds_dma.h"
 
 namespace dr {
 namespace {
@@ -93,25 +94,6 @@ __device__ inline void st_relaxed(int* p, int v) {
 }
 __device__ inline void compiler_fence() { asm volatile("" ::: "memory"); }
 
-// Direct global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4):
-// lane l's bytes land at lds_wave_base + 16*l. Written as inline asm so that
-// the compiler does not treat the ring as a pending LDS write of this wave
-// (which makes it drain every load before each flag access); the loader
-// waits on these loads itself with explicit s_waitcnt vmcnt. The asm has no
-// output register and the address registers are read at issue; one wait state
-// separates the M0 write from the load that reads it (the compiler cannot see
-// inside the asm to insert it).
-__device__ inline void dma16(const void* gptr, unsigned char* lds_wave_base) {
-  const unsigned m0 = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)lds_wave_base);
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0), "v"(gptr) : "memory", "m0");
-}
-
-// The same copy with an SGPR base and a per-lane 32-bit byte offset (saddr form).
-__device__ inline void dma16_s(const void* sbase, unsigned voff, unsigned char* lds_wave_base) {
-  const unsigned m0 = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)lds_wave_base);
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(m0), "v"(voff), "s"(sbase) : "memory", "m0");
-}
-
 // max / sum of a value over the two 32-lane halves: v_permlane32_swap(v, v)
 // yields the low half in both halves of one result and the high half in the other
 __device__ inline float max_halves(float v) {
@@ -123,13 +105,6 @@ __device__ inline float sum_halves(float v) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 __device__ inline int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
-
-// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
-template <int N>
-__device__ inline void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
 
 struct Shared {
   int prog[kConsumers];        // next unit each compute wave may read (16-byte aligned)

@@ -34,6 +34,7 @@
 //   compact:  one wavefront per (b, query block): flags -> ascending kept list,
 //             written for every head.
 #include "dr_internal.h"
+#include "lds_dma.h"
 
 namespace dr {
 namespace {
@@ -103,6 +104,10 @@ struct Geo {
   static constexpr int KBUF = HF * BS * RB;         // one key block, all fused heads
   static constexpr int QB = kRows / BS;             // query blocks per workgroup
   static constexpr int WPQ = BS / 32;               // waves per query block
+  // key-block ring in LDS: NB buffers, blocks prefetched NB - 1 steps ahead
+  static constexpr int NB = KBUF <= 16384 ? 5 : 3;
+  static constexpr int NI = KBUF / 1024;            // 1 KB direct-to-LDS loads per block
+  static constexpr int PERW = NI >= kWaves ? NI / kWaves : 1;   // per issuing wave
 };
 
 // Fused-head logits of one 32x32 token tile: A = this wave's Q rows (registers),
@@ -143,43 +148,34 @@ __device__ __forceinline__ void load_q(const TokParams& p, int b, int q0, int la
   }
 }
 
-// Stage key block kb of batch b (all fused heads) into an LDS buffer; keys >= S
-// are zero. Cooperative over the workgroup: returns the 16-byte chunks this
-// thread carries so that the loads can be issued ahead of the stores.
+// Stage key block kb of batch b (all fused heads) into LDS buffer buf with
+// direct-to-LDS loads: load n (64 lanes x 16 B) of the block is issued by wave
+// n % kWaves and fills bytes [1024 n, 1024 n + 1024) of the buffer, that is
+// chunk slots 64 n .. 64 n + 63 in row-major order. Slot s of key row r holds
+// the row's logical chunk s ^ swz(key), so the source address carries the
+// swizzle. Keys >= S read the last token instead (finite values that no
+// selection uses: tiles holding them take the masked path).
 template <int D, int BS, int HF>
-struct Stager {
+__device__ __forceinline__ void issue_block(const TokParams& p, int b, int kb, unsigned char* buf, int wave, int lane) {
   using G = Geo<D, BS, HF>;
-  static constexpr int CHUNKS = HF * BS * (D / 8);
-  static constexpr int PER = (CHUNKS + kThreads - 1) / kThreads;
-  u32x4 v[PER];
-  __device__ __forceinline__ void load(const TokParams& p, int b, int kb, int tid) {
-#pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      const int c = tid + j * kThreads;
-      v[j] = u32x4{0, 0, 0, 0};
-      if (c < CHUNKS && kb >= 0) {
-        const int h = c / (BS * (D / 8));
-        const int rem = c - h * (BS * (D / 8));
-        const int key = rem / (D / 8), ch = rem - key * (D / 8);
-        const int tok = kb * BS + key;
-        if (tok < p.S)
-          v[j] = *reinterpret_cast<const u32x4*>(p.k + ((size_t)(b * p.H + h) * p.S + tok) * D + ch * 8);
-      }
-    }
+  for (int n = wave; n < G::NI; n += kWaves) {
+    const int c = n * 64 + lane;
+    const int row = c / (D / 8), slot = c % (D / 8);
+    const int h = row / BS, key = row % BS;
+    const int tok = min(kb * BS + key, p.S - 1);
+    dma16(p.k + ((size_t)(b * p.H + h) * p.S + tok) * D + (size_t)(slot ^ swz<D>(key)) * 8, buf + n * 1024);
   }
-  __device__ __forceinline__ void store(unsigned char* buf, int tid) const {
-#pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      const int c = tid + j * kThreads;
-      if (c < CHUNKS) {
-        const int h = c / (BS * (D / 8));
-        const int rem = c - h * (BS * (D / 8));
-        const int key = rem / (D / 8), ch = rem - key * (D / 8);
-        *reinterpret_cast<u32x4*>(buf + (h * BS + key) * G::RB + ((ch ^ swz<D>(key)) << 4)) = v[j];
-      }
-    }
-  }
-};
+}
+
+// Wait until this wave's loads of a step have landed, `later` steps having
+// been issued after it (later <= NB - 2).
+template <int D, int BS, int HF>
+__device__ __forceinline__ void wait_block(int later, int wave) {
+  using G = Geo<D, BS, HF>;
+  if (G::NI < kWaves && wave >= G::NI) return;     // issues nothing
+  if (later >= G::NB - 2) wait_vmcnt<G::PERW * (G::NB - 2)>();
+  else wait_vmcnt<0>();
+}
 
 // Per-lane view of one tile's token pairs: the lane's key token and, for its
 // 16 query rows, which of the (at most two) query frames each row lies in.
@@ -274,7 +270,7 @@ template <int D, int BS, int HF>
 struct Lds {
   using G = Geo<D, BS, HF>;
   int nword;
-  unsigned char* kbuf[2];
+  unsigned char* ring;  // [NB][KBUF]
   unsigned int* bits;   // [QB][nword]
   int* pre;             // [QB][nword]
   unsigned int* uword;  // [nword]
@@ -284,12 +280,12 @@ struct Lds {
   int* s_sf;            // [Nf]
   unsigned char* rest;  // 16-byte aligned
   __host__ __device__ static size_t align16(size_t x) { return (x + 15) & ~(size_t)15; }
+  __device__ unsigned char* kbuf(int j) const { return ring + (j % G::NB) * G::KBUF; }
   __host__ __device__ static int max_steps(int Sb) { return Sb / kTokSplit + 2; }
   __device__ Lds(unsigned char* smem, int Sb, int Nf) {
     nword = (Sb + 31) >> 5;
-    kbuf[0] = smem;
-    kbuf[1] = smem + G::KBUF;
-    bits = reinterpret_cast<unsigned int*>(smem + 2 * G::KBUF);
+    ring = smem;
+    bits = reinterpret_cast<unsigned int*>(smem + G::NB * G::KBUF);
     pre = reinterpret_cast<int*>(bits + G::QB * nword);
     uword = reinterpret_cast<unsigned int*>(pre + G::QB * nword);
     upre = reinterpret_cast<int*>(uword + nword);
@@ -301,7 +297,7 @@ struct Lds {
   }
   __host__ __device__ static size_t bytes(int Sb, int Nf) {
     const size_t nw = (size_t)(Sb + 31) / 32;
-    const size_t used = 2 * (size_t)G::KBUF + (size_t)G::QB * nw * 8 + nw * 8 + (size_t)max_steps(Sb) * 4 +
+    const size_t used = (size_t)G::NB * G::KBUF + (size_t)G::QB * nw * 8 + nw * 8 + (size_t)max_steps(Sb) * 4 +
                         (size_t)Nf * 8;
     return (used + 15) & ~(size_t)15;
   }
@@ -415,6 +411,7 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(TokParams p) {
   const bool active_wave = a < p.Sb && q0 < p.S;
   bf16x8 qf[HF][D / 16];
   if (active_wave) load_q<D, HF>(p, b, q0, lane, qf);
+  wait_vmcnt<0>();   // Q resident before the ring's loads are counted
   const int f0w = q0 / p.Nt;
   Stat* mine = acc_l + wave * 2 * p.Nf;
 
@@ -468,16 +465,15 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(TokParams p) {
       }
   };
 
-  Stager<D, BS, HF> st;
-  if (n > 0) {
-    st.load(p, b, L.steps[0], tid);
-    st.store(L.kbuf[0], tid);
-  }
-  __syncthreads();
+  // key blocks stream through the LDS ring, NB - 1 steps ahead of use
+  constexpr int PF = G::NB - 1;
+  for (int j = 0; j < PF && j < n; ++j) issue_block<D, BS, HF>(p, b, uniform(L.steps[j]), L.kbuf(j), wave, lane);
   for (int j = 0; j < n; ++j) {
+    wait_block<D, BS, HF>(min(PF - 1, n - 1 - j), wave);
+    __syncthreads();   // step j staged by every wave; step j - 1's buffer free
+    if (j + PF < n) issue_block<D, BS, HF>(p, b, uniform(L.steps[j + PF]), L.kbuf(j + PF), wave, lane);
     const int kb = uniform(L.steps[j]);
-    st.load(p, b, j + 1 < n ? uniform(L.steps[j + 1]) : -1, tid);
-    const unsigned char* kbuf = L.kbuf[j & 1];
+    const unsigned char* kbuf = L.kbuf(j);
     const bool need = active_wave && ((L.bits[qb * L.nword + (kb >> 5)] >> (kb & 31)) & 1u);
     if (need) {
 #pragma unroll
@@ -555,8 +551,6 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(TokParams p) {
           if (tn[fo] > 0) add(2 * fo + kp, ts[fo], tq[fo], tn[fo], tm[fo], tl[fo]);
       }
     }
-    st.store(L.kbuf[(j + 1) & 1], tid);
-    __syncthreads();
   }
   flush(0);
   flush(1);
@@ -647,10 +641,13 @@ __global__ __launch_bounds__(kThreads) void mark_kernel(TokParams p) {
   using G = Geo<D, BS, HF>;
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ int s_nsteps;
-  __shared__ int min_c[BS + 1], min_a[BS + 1];
+  __shared__ int min_c[BS + 1], min_a[BS + 1], pos_lo[G::QB];
   Lds<D, BS, HF> L(smem, p.Sb, p.Nf);
-  float* thr_l = reinterpret_cast<float*>(L.rest);                    // [FR][Nf]
-  int* colcnt = reinterpret_cast<int*>(thr_l + p.FR * p.Nf);          // [2][QB][BS] when BS > 32
+  const int MS = Lds<D, BS, HF>::max_steps(p.Sb);
+  float* thr_l = reinterpret_cast<float*>(L.rest);                      // [FR][Nf]
+  int* served_l = reinterpret_cast<int*>(thr_l + p.FR * p.Nf);          // [FR][Nf]
+  int* colcnt = served_l + p.FR * p.Nf;                                 // [2][QB][BS] when BS > 32
+  unsigned char* flags_l = reinterpret_cast<unsigned char*>(colcnt + (G::WPQ > 1 ? 2 * G::QB * BS : 0));  // [QB][MS]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5;
   const int wg = blockIdx.x / kTokSplit, split = blockIdx.x - wg * kTokSplit, b = blockIdx.y;
   const int a0 = wg * G::QB;
@@ -661,12 +658,21 @@ __global__ __launch_bounds__(kThreads) void mark_kernel(TokParams p) {
     const int fr = i / p.Nf, fk = i - fr * p.Nf;
     const int fq = f_lo + fr;
     thr_l[i] = fq < p.Nf ? p.thr[(size_t)b * p.Nf * p.Nf + (size_t)fq * p.Nf + fk] : INFINITY;
+    served_l[i] = 0;
   }
   for (int n = 1 + tid; n <= BS; n += kThreads) {
     min_c[n] = min_count(n, p.theta_c);
     min_a[n] = min_count(n, p.theta_m);
   }
   const int n = setup<D, BS, HF>(p, L, a0, split, &s_nsteps);
+
+  // position of key block kb in the candidate row of query block qb2
+  auto pos_of = [&](int qb2, int kb) -> int {
+    const int wi = kb >> 5;
+    return L.pre[qb2 * L.nword + wi] + __popc(L.bits[qb2 * L.nword + wi] & ((1u << (kb & 31)) - 1u));
+  };
+  // this split's flags of row qb2 are kept in LDS from its first step on
+  if (tid < G::QB && n > 0) pos_lo[tid] = pos_of(tid, L.steps[0]);
 
   const int qb = wave / G::WPQ, sub = wave - qb * G::WPQ;
   const int a = a0 + qb;
@@ -675,14 +681,8 @@ __global__ __launch_bounds__(kThreads) void mark_kernel(TokParams p) {
   const int nq = a < p.Sb ? min(BS, p.S - a * BS) : 0;
   bf16x8 qf[HF][D / 16];
   if (active_wave) load_q<D, HF>(p, b, q0, lane, qf);
+  wait_vmcnt<0>();   // Q resident before the ring's loads are counted
 
-  // flag of candidate entry (a, kb): its CSR position from the bitmap prefix
-  auto flag_of = [&](int kb) -> unsigned char* {
-    const int wi = kb >> 5;
-    const long long e = p.row_ptr[a] + L.pre[qb * L.nword + wi] +
-                        __popc(L.bits[qb * L.nword + wi] & ((1u << (kb & 31)) - 1u));
-    return p.flags + (long long)b * p.nnz + e;
-  };
   // selected count of key column lane % 32 of the tile (q0, ktok0) over the
   // wave's 32 query rows (the same value in both half-waves); marks served
   // frame pairs
@@ -697,7 +697,7 @@ __global__ __launch_bounds__(kThreads) void mark_kernel(TokParams p) {
 #pragma unroll
       for (int i = 0; i < 16; ++i)
         if (acc[i] * p.scale >= thr) sel |= 1u << i;
-      if (__ballot(sel != 0u) != 0ull && lane == 0) p.served[(size_t)b * p.Nf * p.Nf + (size_t)ti.fq * p.Nf + ti.fk] = 1;
+      if (__ballot(sel != 0u) != 0ull && lane == 0) served_l[(ti.fq - f_lo) * p.Nf + ti.fk] = 1;
     } else {
       const TileFrames f = tile_frames(p, q0, ktok0 + (lane & 31));
       const float thr0 = f.kvalid ? thr_l[(f.f0 - f_lo) * p.Nf + f.fk] : INFINITY;
@@ -711,7 +711,7 @@ __global__ __launch_bounds__(kThreads) void mark_kernel(TokParams p) {
           if ((s2 >> i) & 1u) {
             int u = f.u0 + row_of(i, half);
             const int fq = f.f0 + (u >= p.Nt ? 1 : 0);
-            p.served[(size_t)b * p.Nf * p.Nf + (size_t)fq * p.Nf + f.fk] = 1;
+            served_l[(fq - f_lo) * p.Nf + f.fk] = 1;
           }
       }
     }
@@ -719,29 +719,28 @@ __global__ __launch_bounds__(kThreads) void mark_kernel(TokParams p) {
     return c + __shfl_xor(c, 32);
   };
 
-  Stager<D, BS, HF> st;
-  if (n > 0) {
-    st.load(p, b, L.steps[0], tid);
-    st.store(L.kbuf[0], tid);
-  }
-  __syncthreads();
+  // key blocks stream through the LDS ring, NB - 1 steps ahead of use
+  constexpr int PF = G::NB - 1;
+  for (int j = 0; j < PF && j < n; ++j) issue_block<D, BS, HF>(p, b, uniform(L.steps[j]), L.kbuf(j), wave, lane);
   int kb_prev = -1;
   for (int j = 0; j <= n; ++j) {
+    if (j < n) wait_block<D, BS, HF>(min(PF - 1, n - 1 - j), wave);
+    __syncthreads();   // step j staged by every wave; step j - 1 finished
     if (G::WPQ > 1) {
-      // decide step j - 1 from the counts of all its waves (complete after the barrier)
+      // decide step j - 1 from the counts of all its waves
       if (kb_prev >= 0 && sub == 0 && a < p.Sb && ((L.bits[qb * L.nword + (kb_prev >> 5)] >> (kb_prev & 31)) & 1u)) {
         int* cnt = colcnt + ((j - 1) & 1) * G::QB * BS + qb * BS;
         const int nk = min(BS, p.S - kb_prev * BS);
         const int c = lane < BS ? cnt[lane] : 0;
         const int n_act = __popcll(__ballot(lane < nk && c >= min_c[nq]));
-        if (lane == 0) *flag_of(kb_prev) = n_act >= min_a[nk] ? 1 : 0;
+        if (lane == 0) flags_l[qb * MS + pos_of(qb, kb_prev) - pos_lo[qb]] = n_act >= min_a[nk] ? 1 : 0;
         if (lane < BS) cnt[lane] = 0;
       }
     }
     if (j == n) break;
+    if (j + PF < n) issue_block<D, BS, HF>(p, b, uniform(L.steps[j + PF]), L.kbuf(j + PF), wave, lane);
     const int kb = uniform(L.steps[j]);
-    st.load(p, b, j + 1 < n ? uniform(L.steps[j + 1]) : -1, tid);
-    const unsigned char* kbuf = L.kbuf[j & 1];
+    const unsigned char* kbuf = L.kbuf(j);
     const bool need = active_wave && ((L.bits[qb * L.nword + (kb >> 5)] >> (kb & 31)) & 1u);
     if (need) {
       if (G::WPQ == 1) {
@@ -749,7 +748,7 @@ __global__ __launch_bounds__(kThreads) void mark_kernel(TokParams p) {
         const int nk = min(BS, p.S - kb * BS);
         const int c = tile_count(kbuf, 0, kb * BS);
         const int n_act = __popcll(__ballot(lane < nk && c >= min_c[nq]));
-        if (lane == 0) *flag_of(kb) = n_act >= min_a[nk] ? 1 : 0;
+        if (lane == 0) flags_l[qb * MS + pos_of(qb, kb) - pos_lo[qb]] = n_act >= min_a[nk] ? 1 : 0;
       } else {
         int* cnt = colcnt + (j & 1) * G::QB * BS + qb * BS;
 #pragma unroll
@@ -761,10 +760,23 @@ __global__ __launch_bounds__(kThreads) void mark_kernel(TokParams p) {
         }
       }
     }
-    st.store(L.kbuf[(j + 1) & 1], tid);
     kb_prev = kb;
-    __syncthreads();
   }
+  __syncthreads();
+  // write out this split's flags (a contiguous run of each candidate row) and
+  // the served frame pairs
+  if (n > 0 && wave < G::QB && a0 + wave < p.Sb) {
+    const int last = L.steps[n - 1];
+    const int lo = pos_lo[wave];
+    const int hi = pos_of(wave, last) + (int)((L.bits[wave * L.nword + (last >> 5)] >> (last & 31)) & 1u);
+    unsigned char* out = p.flags + (long long)b * p.nnz + p.row_ptr[a0 + wave] + lo;
+    for (int i = lane; i < hi - lo; i += 64) out[i] = flags_l[wave * MS + i];
+  }
+  for (int i = tid; i < p.FR * p.Nf; i += kThreads)
+    if (served_l[i]) {
+      const int fr = i / p.Nf, fk = i - fr * p.Nf;
+      p.served[(size_t)b * p.Nf * p.Nf + (size_t)(f_lo + fr) * p.Nf + fk] = 1;
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -899,7 +911,8 @@ hipError_t launch_all(const TokParams& p, int B, hipStream_t stream) {
   using G = Geo<D, BS, HF>;
   const size_t base = Lds<D, BS, HF>::bytes(p.Sb, p.Nf);
   const size_t lds_stats = base + (size_t)kWaves * 2 * p.Nf * sizeof(Stat);
-  const size_t lds_mark = base + (size_t)p.FR * p.Nf * 4 + (G::WPQ > 1 ? (size_t)2 * G::QB * BS * 4 : 0);
+  const size_t lds_mark = base + (size_t)p.FR * p.Nf * 8 + (G::WPQ > 1 ? (size_t)2 * G::QB * BS * 4 : 0) +
+                          (size_t)G::QB * Lds<D, BS, HF>::max_steps(p.Sb);
   const dim3 grid((unsigned)(p.n_wg * kTokSplit), (unsigned)B);
   hipLaunchKernelGGL((stats_kernel<D, BS, HF>), grid, dim3(kThreads), lds_stats, stream, p);
   hipError_t e = hipGetLastError();
@@ -924,8 +937,8 @@ size_t lds_need(int Sb, int Nf, int FR) {
   const size_t base = Lds<D, BS, HF>::bytes(Sb, Nf);
   const size_t stats = base + (size_t)kWaves * 2 * Nf * sizeof(Stat);
   // (+ the static arrays of the mark kernel: the integer thresholds and the step count)
-  const size_t mark = base + (size_t)FR * Nf * 4 + (G::WPQ > 1 ? (size_t)2 * G::QB * BS * 4 : 0) +
-                      (size_t)2 * (BS + 1) * 4 + 16;
+  const size_t mark = base + (size_t)FR * Nf * 8 + (G::WPQ > 1 ? (size_t)2 * G::QB * BS * 4 : 0) +
+                      (size_t)G::QB * Lds<D, BS, HF>::max_steps(Sb) + (size_t)(2 * (BS + 1) + G::QB) * 4 + 16;
   return stats > mark ? stats : mark;
 }
 
