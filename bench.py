@@ -13,7 +13,6 @@ kept blocks only) with the speedup over the on-GPU dense kernel, on one GPU.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import math
 import os
@@ -64,11 +63,6 @@ def event_ms(fn, iters, torch):
     return s.elapsed_time(e) / iters
 
 
-def kernel_source_digest():
-    p = os.path.join(ROOT, "block_sparse_attention_candidates_amd", "csrc", "attention.hip")
-    return hashlib.sha256(open(p, "rb").read()).hexdigest()
-
-
 def traffic_record(workload, mode):
     """HBM bytes per sparse-attention launch from committed rocprofv3 PMC
     counters, if they were taken on the current kernel source."""
@@ -76,7 +70,8 @@ def traffic_record(workload, mode):
     if not os.path.exists(p):
         return None
     rec = json.load(open(p)).get(f"{workload}/{mode}")
-    if not rec or rec.get("attention_hip_sha256") != kernel_source_digest():
+    from block_sparse_attention_candidates_amd.profsum import attention_source_digest
+    if not rec or rec.get("attention_src_sha256") != attention_source_digest():
         return None
     return rec
 

@@ -61,17 +61,29 @@ def _counter(run_dir: str, counter: str):
     return sum(attn) / len(attn), max(copy)
 
 
+# the sources the sparse-attention kernel is compiled from
+ATTENTION_SOURCES = ("attention.hip", "lds_dma.h", "dr_internal.h")
+
+
+def attention_source_digest() -> str:
+    """SHA-256 over the attention kernel's source files, in a fixed order."""
+    h = hashlib.sha256()
+    for name in ATTENTION_SOURCES:
+        with open(os.path.join(PKG, "csrc", name), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
 def traffic(fetch_dir: str, write_dir: str, workload: str, mode: str) -> dict:
     fa, fc = _counter(fetch_dir, "FETCH_SIZE")
     wa, wc = _counter(write_dir, "WRITE_SIZE")
     f_scale, w_scale = GIB / (fc * 1024.0), GIB / (wc * 1024.0)
-    src = os.path.join(PKG, "csrc", "attention.hip")
     rec = {
         "fetch_kib_per_launch": fa, "write_kib_per_launch": wa,
         "copy_fetch_kib": fc, "copy_write_kib": wc,
         "fetch_scale": f_scale, "write_scale": w_scale,
         "hbm_bytes_per_launch": fa * 1024.0 * f_scale + wa * 1024.0 * w_scale,
-        "attention_hip_sha256": hashlib.sha256(open(src, "rb").read()).hexdigest(),
+        "attention_src_sha256": attention_source_digest(),
     }
     path = os.path.join(ROOT, "profiles", "sparse_attn_traffic.json")
     db = json.load(open(path)) if os.path.exists(path) else {}
