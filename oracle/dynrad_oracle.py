@@ -37,6 +37,11 @@ Stages:
                           logits per candidate token pair, z-normalised per frame
                           pair, decay-state thresholds, top-pair fallback, then the
                           same (theta_c, theta_m) aggregation to blocks as step 3
+11. static_select         the paper's decay-state static-ratio mode ([DR] §3.2
+                          Eq. 8, Algorithm 1): per retained frame pair a uniform
+                          sample of max(1, floor(|P(i, j)| * rho)) candidate pairs
+                          drawn with a seeded counter-based generator
+                          (Philox4x32-10), then the same aggregation to blocks
 
 Readings where the pages leave a step open are stated at each function.
 """
@@ -601,3 +606,150 @@ def token_select_decisive(q_heads, k_heads, blocks, num_frames: int, tokens_per_
             dec[b] = not unsure[:, b * block_size:min((b + 1) * block_size, S)].any()
         out.append(dec)
     return out
+
+
+# ---------------------------------------------------------------------------
+# 11. Decay-state static-ratio selection ([DR] §3.2 "Static-ratio mode", Eq. 8,
+#     Algorithm 1). For each retained frame pair (i, j) (t mod sf(t) = 0):
+#     t <= 1 keeps all of P(i, j) (rho = 1; t = 0 is dense attention);
+#     t > 1 keeps k = max(1, floor(|P(i, j)| * rho)) pairs of P(i, j) drawn
+#     uniformly, rho = rho_1 if L(t) >= B_s (near) else rho_2 (far). The
+#     selected pairs are aggregated to blocks as in steps 3 and 10.
+#
+#     Reading of "uniformly sample ... using a deterministic seed" (the pages
+#     name no generator): pair (u, v) of P(i, j) gets the 32-bit word number
+#     (v mod 4) of Philox4x32-10 applied to the counter (u, floor(v / 4), i, j)
+#     under the key (seed mod 2^32, seed div 2^32); the k pairs with the
+#     smallest (word, u * N_t + v) are kept. The k smallest of independent
+#     uniform keys form a uniformly random k-subset.
+#     Reading of floor(|P| * rho): evaluated in float64 with the same 1e-9
+#     guard as the block form's count (floor(|P| * rho + 1e-9)).
+# ---------------------------------------------------------------------------
+PHILOX_M = (0xD2511F53, 0xCD9E8D57)   # round multipliers
+PHILOX_W = (0x9E3779B9, 0xBB67AE85)   # key schedule increments
+_U32 = np.uint64(0xFFFFFFFF)
+
+
+def philox4x32_10(c0, c1, c2, c3, k0: int, k1: int):
+    """Philox4x32 with 10 rounds (Salmon, Moraes, Dror and Shaw, "Parallel
+    Random Numbers: As Easy as 1, 2, 3", SC 2011), elementwise over arrays of
+    32-bit counters. One round: the products M0 * c0 and M1 * c2 (64-bit) give
+    the new counter (hi(M1 c2) ^ c1 ^ k0, lo(M1 c2), hi(M0 c0) ^ c3 ^ k1,
+    lo(M0 c0)); the key advances by (W0, W1) before every round after the first.
+    Returns the four output words as uint64 arrays holding 32-bit values."""
+    c = [np.asarray(x, dtype=np.uint64) & _U32 for x in (c0, c1, c2, c3)]
+    k = [int(k0) & 0xFFFFFFFF, int(k1) & 0xFFFFFFFF]
+    for r in range(10):
+        if r:
+            k = [(k[0] + PHILOX_W[0]) & 0xFFFFFFFF, (k[1] + PHILOX_W[1]) & 0xFFFFFFFF]
+        p0 = np.uint64(PHILOX_M[0]) * c[0]
+        p1 = np.uint64(PHILOX_M[1]) * c[2]
+        c = [(p1 >> np.uint64(32)) ^ c[1] ^ np.uint64(k[0]), p1 & _U32,
+             (p0 >> np.uint64(32)) ^ c[3] ^ np.uint64(k[1]), p0 & _U32]
+    return c
+
+
+def static_rho(t: int, tokens_per_frame: int, block_size: int, gamma: float, rho_near: float,
+               rho_far: float) -> float:
+    """Eq. 8: 1 for t <= 1, rho_1 when L(t) >= B_s, rho_2 otherwise (L(t) the
+    unclamped Eq. 2 length, as in Eq. 11)."""
+    if t <= 1:
+        return 1.0
+    return rho_near if decay_length(t, tokens_per_frame, gamma) >= block_size else rho_far
+
+
+def static_pair_count(n_pairs: int, rho: float) -> int:
+    """k = max(1, floor(|P| * rho)) in float64 (guarded, see above)."""
+    return max(1, int(math.floor(float(n_pairs) * rho + COUNT_GUARD)))
+
+
+def static_pair_keys(u, v, i: int, j: int, tokens_per_frame: int, seed: int) -> np.ndarray:
+    """Sort keys (word << 32) | (u * N_t + v) of pairs (u, v) of frame pair (i, j)."""
+    u = np.asarray(u, dtype=np.uint64)
+    v = np.asarray(v, dtype=np.uint64)
+    words = philox4x32_10(u, v // np.uint64(4), np.full(u.shape, i, np.uint64), np.full(u.shape, j, np.uint64),
+                          seed & 0xFFFFFFFF, seed >> 32)
+    lane = (v % np.uint64(4)).astype(np.int64)
+    x = np.choose(lane, words)
+    return (x << np.uint64(32)) | (u * np.uint64(tokens_per_frame) + v)
+
+
+def static_frame_thresholds(num_frames: int, tokens_per_frame: int, block_size: int, gamma: float, lam: float,
+                            rho_near: float, rho_far: float, seed: int, query_frames=None) -> dict:
+    """{(i, j): (|P|, k, largest kept sort key)} for every retained frame pair
+    with t > 1 (and query frame i in query_frames, if given)."""
+    Nt = tokens_per_frame
+    w, sf = distance_table(num_frames, Nt, block_size, gamma, lam)
+    frames = range(num_frames) if query_frames is None else query_frames
+    out = {}
+    for i in frames:
+        for j in range(num_frames):
+            t = abs(int(i) - j)
+            if t <= 1 or t % sf[t] != 0:
+                continue
+            keys = []
+            for u in range(Nt):   # P(i, j) row by row (Eq. 7)
+                v = np.arange(max(0, u - w[t]), min(Nt - 1, u + w[t]) + 1)
+                keys.append(static_pair_keys(np.full(v.shape, u), v, int(i), j, Nt, seed))
+            keys = np.concatenate(keys)
+            k = static_pair_count(len(keys), static_rho(t, Nt, block_size, gamma, rho_near, rho_far))
+            out[(int(i), j)] = (len(keys), k, int(np.sort(keys)[k - 1]))
+    return out
+
+
+def static_selected_rows(rows: slice, num_frames: int, tokens_per_frame: int, block_size: int, gamma: float,
+                         lam: float, seed: int, thresholds: dict) -> np.ndarray:
+    """Selected token pairs [len(rows), S] of the query tokens `rows`: all of
+    P(i, j) for t <= 1, the pairs whose sort key is at most the frame pair's
+    k-th smallest for t > 1, none for frame pairs that are not retained."""
+    Nt = tokens_per_frame
+    w, sf = distance_table(num_frames, Nt, block_size, gamma, lam)
+    S = num_frames * Nt
+    sel = np.zeros((rows.stop - rows.start, S), dtype=bool)
+    qtok = np.arange(rows.start, rows.stop)
+    fq, uq = token_frame_and_index(qtok, Nt)
+    ukey = np.arange(Nt)
+    for i in np.unique(fq):
+        r = np.nonzero(fq == i)[0]
+        for j in range(num_frames):
+            t = abs(int(i) - j)
+            if t % sf[t] != 0:
+                continue
+            P = np.abs(uq[r][:, None] - ukey[None, :]) <= w[t]
+            cols = slice(j * Nt, (j + 1) * Nt)
+            if t <= 1:
+                sel[r, cols] = P
+                continue
+            uu = np.repeat(uq[r], Nt)
+            vv = np.tile(ukey, len(r))
+            keys = static_pair_keys(uu, vv, int(i), j, Nt, seed).reshape(len(r), Nt)
+            sel[r, cols] = P & (keys <= np.uint64(thresholds[(int(i), j)][2]))
+    return sel
+
+
+def static_select_rows(blocks, num_frames: int, tokens_per_frame: int, block_size: int, gamma: float, lam: float,
+                       rho_near: float, rho_far: float, seed: int, theta_c: float = 0.0, theta_m: float = 0.0,
+                       thresholds: dict = None) -> List[np.ndarray]:
+    """Kept key blocks (ascending) of the given query blocks under the
+    decay-state static-ratio mode; the mask depends on no tensor content."""
+    S = num_frames * tokens_per_frame
+    if thresholds is None:
+        frames = sorted({f for a in blocks for f in range(a * block_size // tokens_per_frame,
+                                                          (min(S, (a + 1) * block_size) - 1) // tokens_per_frame + 1)})
+        thresholds = static_frame_thresholds(num_frames, tokens_per_frame, block_size, gamma, lam, rho_near,
+                                             rho_far, seed, query_frames=frames)
+    out = []
+    for a in blocks:
+        rows = slice(a * block_size, min((a + 1) * block_size, S))
+        sel = static_selected_rows(rows, num_frames, tokens_per_frame, block_size, gamma, lam, seed, thresholds)
+        out.append(aggregate_block_rows(sel, rows.start, block_size, S, theta_c, theta_m)[0])
+    return out
+
+
+def static_select(num_frames: int, tokens_per_frame: int, block_size: int, gamma: float, lam: float,
+                  rho_near: float, rho_far: float, seed: int, theta_c: float = 0.0,
+                  theta_m: float = 0.0) -> List[np.ndarray]:
+    """Kept key blocks of every query block (ascending)."""
+    S_b = -(-(num_frames * tokens_per_frame) // block_size)
+    return static_select_rows(range(S_b), num_frames, tokens_per_frame, block_size, gamma, lam, rho_near,
+                              rho_far, seed, theta_c, theta_m)

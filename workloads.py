@@ -241,6 +241,24 @@ TOKEN_PRESETS = {
 }
 
 
+# [DR] Table 2, static rows: decay gamma, long-range lambda, theta_m, theta_c,
+# near / far retention ratios rho_1 / rho_2 (Eq. 8).
+STATIC_PRESETS = {
+    "low": dict(gamma=2.0, lam=0.3, theta_m=0.75, theta_c=0.20, rho_near=0.25, rho_far=0.55),
+    "mid": dict(gamma=1.3, lam=0.7, theta_m=0.60, theta_c=0.15, rho_near=0.75, rho_far=0.55),
+    "high": dict(gamma=1.6, lam=0.8, theta_m=0.65, theta_c=0.15, rho_near=0.55, rho_far=0.50),
+}
+
+
+def static_workload(base: str, preset: str):
+    """A workload's shape under a Table 2 static preset; returns
+    (workload, (rho_near, rho_far))."""
+    pr = STATIC_PRESETS[preset]
+    w = dataclasses.replace(get_workload(base), name=f"{base}+static-{preset}", gamma=pr["gamma"], lam=pr["lam"],
+                            theta_c=pr["theta_c"], theta_m=pr["theta_m"])
+    return w, (pr["rho_near"], pr["rho_far"])
+
+
 def token_workload(base: str, preset: str):
     """A workload's tensors (same seed and field) under a Table 2 preset of
     the token-level selector; returns (workload, (tau_near, tau_far))."""
