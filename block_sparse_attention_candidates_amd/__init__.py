@@ -27,7 +27,8 @@ from . import _lib as _L
 from ._lib import Dims, DynradError, RadialCfg, SelectCfg, check, lib
 
 __all__ = ["radial_cfg", "num_blocks", "distance_table", "Candidates", "Kept", "build_candidates",
-           "score_select", "sparse_attn", "attn", "DynradError", "kept_from_lists"]
+           "score_select", "token_select", "static_select", "sparse_attn", "attn", "DynradError",
+           "kept_from_lists"]
 
 
 def radial_cfg(num_frames: int, tokens_per_frame: int, block_size: int, gamma: float, lam: float,
@@ -164,6 +165,27 @@ def token_select(q, k, cand: Candidates, tau_near: float, tau_far: float, fused_
                                 k.data_ptr(), cand.row_ptr.data_ptr(), cand.cols.data_ptr(), cand.nnz,
                                 kept_col.data_ptr(), kept_cnt.data_ptr(), workspace.data_ptr(), workspace.numel(),
                                 _stream(q.device)))
+    return Kept(kept_col, kept_cnt)
+
+
+def static_select(cand: Candidates, rho_near: float, rho_far: float, seed: int, batch: int = 1, heads: int = 1,
+                  workspace=None) -> Kept:
+    """The paper's decay-state static-ratio selection (dr_static_select): a
+    content-free mask from (rho_near, rho_far, seed), written for every one of
+    batch x heads."""
+    torch = _torch()
+    device = cand.row_ptr.device
+    dims = _L.Dims(int(batch), int(heads), 64, 0)
+    st = _L.StaticCfg(float(rho_near), float(rho_far), int(seed) & 0xFFFFFFFFFFFFFFFF)
+    ws_bytes = ctypes.c_size_t(0)
+    check(lib().dr_static_select_workspace(ctypes.byref(cand.cfg), cand.nnz, ctypes.byref(ws_bytes)))
+    if workspace is None or workspace.numel() < ws_bytes.value:
+        workspace = torch.empty(ws_bytes.value, dtype=torch.uint8, device=device)
+    kept_col = torch.empty(batch * heads * cand.nnz, dtype=torch.int32, device=device)
+    kept_cnt = torch.empty(batch * heads * cand.num_blocks, dtype=torch.int32, device=device)
+    check(lib().dr_static_select(ctypes.byref(dims), ctypes.byref(cand.cfg), ctypes.byref(st),
+                                 cand.row_ptr.data_ptr(), cand.cols.data_ptr(), cand.nnz, kept_col.data_ptr(),
+                                 kept_cnt.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream(device)))
     return Kept(kept_col, kept_cnt)
 
 

@@ -391,6 +391,95 @@ dr_status dr_token_select(const dr_dims* dims, const dr_radial_cfg* cfg, const d
   return ok();
 }
 
+namespace {
+
+struct StaticWs {
+  size_t state, hist, flags, total;
+};
+
+StaticWs static_ws(const dr_radial_cfg* c, long long nnz) {
+  StaticWs w;
+  const size_t nfp = (size_t)c->num_frames * c->num_frames;
+  size_t off = 0;
+  w.state = off;
+  off = align256(off + nfp * sizeof(dr::StaticState));
+  w.hist = off;
+  off = align256(off + nfp * dr::kStaticBins * sizeof(uint32_t));
+  w.flags = off;
+  off = align256(off + (size_t)nnz);
+  w.total = off;
+  return w;
+}
+
+dr_status check_static(const dr_static_cfg* st, const dr_radial_cfg* c) {
+  if (!st) return fail(DR_ERR_INVALID_ARG, "static config is NULL");
+  if (!(st->rho_near >= 0.0 && st->rho_near <= 1.0) || !(st->rho_far >= 0.0 && st->rho_far <= 1.0))
+    return fail(DR_ERR_INVALID_ARG, "rho_near and rho_far must lie in [0, 1]");
+  if (c->tokens_per_frame < 32 || c->tokens_per_frame > 65535)
+    return fail(DR_ERR_UNSUPPORTED, "static decay-state selection needs tokens_per_frame in [32, 65535]");
+  if (c->num_frames > dr::kMaxTokenFrames)
+    return fail(DR_ERR_UNSUPPORTED, "static decay-state selection supports num_frames <= %d", dr::kMaxTokenFrames);
+  return DR_OK;
+}
+
+}  // namespace
+
+dr_status dr_static_select_workspace(const dr_radial_cfg* cfg, int64_t nnz, size_t* bytes) {
+  Layout L;
+  dr_status st = check_radial(cfg, &L);
+  if (st != DR_OK) return st;
+  if (cfg->num_frames > dr::kMaxTokenFrames)
+    return fail(DR_ERR_UNSUPPORTED, "static decay-state selection supports num_frames <= %d", dr::kMaxTokenFrames);
+  if (nnz < 1 || nnz > (long long)L.Sb * L.Sb) return fail(DR_ERR_INVALID_ARG, "nnz %lld outside [1, S_b^2]", (long long)nnz);
+  if (!bytes) return fail(DR_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = static_ws(cfg, nnz).total;
+  return ok();
+}
+
+dr_status dr_static_select(const dr_dims* dims, const dr_radial_cfg* cfg, const dr_static_cfg* scfg,
+                           const int32_t* row_ptr, const int32_t* cols, int64_t nnz, int32_t* kept_col,
+                           int32_t* kept_cnt, void* ws, size_t ws_bytes, hipStream_t stream) {
+  Layout L;
+  dr_status st = check_radial(cfg, &L);
+  if (st != DR_OK) return st;
+  if ((st = check_dims(dims)) != DR_OK) return st;
+  if ((st = check_static(scfg, cfg)) != DR_OK) return st;
+  if ((st = check_nnz(nnz, L.Sb, dims)) != DR_OK) return st;
+  if (!row_ptr || !cols || !kept_col || !kept_cnt || !ws)
+    return fail(DR_ERR_INVALID_ARG, "row_ptr, cols, kept_col, kept_cnt and ws must be non-NULL");
+  const StaticWs w = static_ws(cfg, nnz);
+  if (ws_bytes < w.total)
+    return fail(DR_ERR_CAPACITY, "workspace of %zu bytes below the %zu required", ws_bytes, w.total);
+  unsigned char* wsb = static_cast<unsigned char*>(ws);
+  dr::StaticParams p;
+  p.row_ptr = row_ptr;
+  p.cols = cols;
+  p.nnz = nnz;
+  p.S = (int)L.S;
+  p.Sb = L.Sb;
+  p.Nf = cfg->num_frames;
+  p.Nt = cfg->tokens_per_frame;
+  p.Bs = cfg->block_size;
+  p.L0 = dr::base_span(p.Nt);
+  p.gamma = cfg->gamma;
+  p.lambda = cfg->lambda;
+  p.theta_c = cfg->theta_c;
+  p.theta_m = cfg->theta_m;
+  p.rho_near = scfg->rho_near;
+  p.rho_far = scfg->rho_far;
+  p.seed_lo = (uint32_t)(scfg->seed & 0xffffffffu);
+  p.seed_hi = (uint32_t)(scfg->seed >> 32);
+  p.state = reinterpret_cast<dr::StaticState*>(wsb + w.state);
+  p.hist = reinterpret_cast<uint32_t*>(wsb + w.hist);
+  p.flags = wsb + w.flags;
+  hipError_t e = dr::launch_static_select(p, stream);
+  if (e != hipSuccess) return hip_fail(e, "static selection kernels");
+  const dr::FlagCompact fc{row_ptr, cols, p.flags, 0, nnz, L.Sb, dims->heads, kept_col, kept_cnt};
+  e = dr::launch_flag_compact(fc, dims->batch, stream);
+  if (e != hipSuccess) return hip_fail(e, "kept-list compaction");
+  return ok();
+}
+
 dr_status dr_sparse_attn(const dr_dims* dims, const dr_radial_cfg* cfg, const void* q, const void* k,
                          const void* v, const int32_t* row_ptr, int64_t nnz, const int32_t* kept_col,
                          const int32_t* kept_cnt, float softmax_scale, void* out, hipStream_t stream) {

@@ -51,6 +51,16 @@ __host__ __device__ inline void table_entry(int t, int Nt, int Bs, int L0, doubl
   *sf = s < 1 ? 1 : s;
 }
 
+// Density-control decision by integer thresholds ([DR] §3.1 "Density control
+// within blocks"): the smallest count c in [0, n] with (double) c / n > theta
+// (n + 1 if none). A correctly rounded quotient is monotone in c, so
+// c >= min_count(n, theta) holds exactly when the float64 comparison does.
+__host__ __device__ inline int min_count(int n, double theta) {
+  int c = 0;
+  while (c <= n && !((double)c / (double)n > theta)) ++c;
+  return c;
+}
+
 struct CandParams {
   int Nf, Nt, Bs, S, Sb, L0;
   double gamma, lambda, theta_c, theta_m;
@@ -138,6 +148,50 @@ struct TokParams {
 };
 
 size_t token_lds_bytes(int D, int Bs, int Hf, int Sb, int Nf, int FR);
+
+// Ordered compaction of one flag per candidate entry into kept lists written
+// for every head: flags of batch element b at flags + b * flag_stride
+// (flag_stride 0: one mask for all batch elements).
+struct FlagCompact {
+  const int32_t* row_ptr;
+  const int32_t* cols;
+  const unsigned char* flags;
+  long long flag_stride;
+  long long nnz;
+  int Sb, H;
+  int32_t* kept_col;
+  int32_t* kept_cnt;
+};
+hipError_t launch_flag_compact(const FlagCompact& c, int B, hipStream_t stream);
+
+// Decay-state static-ratio selection ([DR] §3.2 Eq. 8): per frame pair state of
+// the sample's threshold search.
+struct StaticState {
+  uint32_t active;    // 1: t > 1 and t mod sf(t) = 0 (a sampled frame pair)
+  uint32_t w;         // window w(t), clamped to N_t
+  uint32_t n, k;      // |P(i, j)| and the number of pairs kept
+  uint32_t rank;      // rank (1-based) of the k-th key within the current group
+  uint32_t group;     // keys agreeing with the resolved prefix
+  uint32_t xpre;      // resolved bits of the threshold word
+  uint32_t ppre;      // resolved bits of the position cut (ties of the word only)
+  uint32_t pos_mode;  // 1: the word ties and positions are being resolved
+  uint32_t pcut;      // inclusive position cut among pairs whose word equals xpre
+  uint32_t pad[2];
+};
+
+struct StaticParams {
+  const int32_t* row_ptr;
+  const int32_t* cols;
+  long long nnz;
+  int S, Sb, Nf, Nt, Bs, L0;
+  double gamma, lambda, theta_c, theta_m, rho_near, rho_far;
+  uint32_t seed_lo, seed_hi;
+  StaticState* state;     // [Nf * Nf]
+  uint32_t* hist;         // [Nf * Nf][2048]
+  unsigned char* flags;   // [nnz]
+};
+constexpr int kStaticBins = 2048;
+hipError_t launch_static_select(const StaticParams& p, hipStream_t stream);
 hipError_t launch_token_select(const TokParams& p, int B, int D, int Bs, int Hf, hipStream_t stream);
 
 hipError_t launch_candidates(const CandParams& p, int32_t* row_ptr, int32_t* cols, long long cap,

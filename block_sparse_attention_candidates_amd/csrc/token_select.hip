@@ -32,7 +32,8 @@
 //             holding its highest-scoring pair is re-decided with that pair
 //             added, by the same tile and selection code.
 //   compact:  one wavefront per (b, query block): flags -> ascending kept list,
-//             written for every head.
+//             written for every head (flag_compact_kernel, shared with the
+//             static decay-state selector).
 #include "dr_internal.h"
 #include "lds_dma.h"
 
@@ -623,16 +624,6 @@ __device__ __forceinline__ bool block_kept(const TokParams& p, const int* cnt, i
   return ((double)act / (double)nk) > p.theta_m;
 }
 
-// The same decision by integer thresholds: for n in 1..BS, min_c[n] is the
-// smallest count c with (double) c / n > theta_c (n + 1 if none), min_a[n]
-// likewise for theta_m. A correctly rounded quotient is monotone in c, so
-// c >= min_c[n] holds exactly when the float64 comparison does.
-__device__ __forceinline__ int min_count(int n, double theta) {
-  int c = 0;
-  while (c <= n && !((double)c / (double)n > theta)) ++c;
-  return c;
-}
-
 // ---------------------------------------------------------------------------
 // Pass 3: selection, aggregation to block pairs, one flag per candidate entry.
 // ---------------------------------------------------------------------------
@@ -880,32 +871,8 @@ __global__ __launch_bounds__(64) void fallback_kernel(TokParams p) {
   }
 }
 
-// ---------------------------------------------------------------------------
-// Pass 5: ordered compaction of the flags into kept lists of every head.
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void compact_kernel(TokParams p) {
-  const int lane = threadIdx.x & 63;
-  const int a = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int b = blockIdx.y;
-  if (a >= p.Sb) return;
-  const int r0 = p.row_ptr[a], n = p.row_ptr[a + 1] - r0;
-  const unsigned char* fl = p.flags + (long long)b * p.nnz + r0;
-  int kept = 0;
-  for (int i0 = 0; i0 < n; i0 += 64) {
-    const int i = i0 + lane;
-    const bool keep = i < n && fl[i] != 0;
-    const unsigned long long m = __ballot(keep);
-    const int before = __builtin_amdgcn_mbcnt_hi((unsigned)(m >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)m, 0));
-    if (keep) {
-      const int col = p.cols[r0 + i];
-      for (int h = 0; h < p.H; ++h) p.kept_col[(long long)(b * p.H + h) * p.nnz + r0 + kept + before] = col;
-    }
-    kept += __popcll(m);
-  }
-  if (lane == 0)
-    for (int h = 0; h < p.H; ++h) p.kept_cnt[(long long)(b * p.H + h) * p.Sb + a] = kept;
-}
-
+// Pass 5 (ordered compaction of the flags into kept lists of every head) is
+// flag_compact_kernel below.
 template <int D, int BS, int HF>
 hipError_t launch_all(const TokParams& p, int B, hipStream_t stream) {
   using G = Geo<D, BS, HF>;
@@ -925,8 +892,8 @@ hipError_t launch_all(const TokParams& p, int B, hipStream_t stream) {
   hipLaunchKernelGGL((fallback_kernel<D, BS, HF>), dim3((unsigned)(p.Nf * p.Nf), (unsigned)B), dim3(64), 0, stream,
                      p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(compact_kernel, dim3((unsigned)((p.Sb + 3) / 4), (unsigned)B), dim3(256), 0, stream, p);
-  return hipGetLastError();
+  const FlagCompact fc{p.row_ptr, p.cols, p.flags, p.nnz, p.nnz, p.Sb, p.H, p.kept_col, p.kept_cnt};
+  return launch_flag_compact(fc, B, stream);
 }
 
 }  // namespace
@@ -947,6 +914,35 @@ size_t token_lds_bytes(int D, int Bs, int Hf, int Sb, int Nf, int FR) {
   if (D == 128 && Bs == 64) return Hf == 1 ? lds_need<128, 64, 1>(Sb, Nf, FR) : lds_need<128, 64, 2>(Sb, Nf, FR);
   if (D == 64 && Bs == 32) return Hf == 1 ? lds_need<64, 32, 1>(Sb, Nf, FR) : lds_need<64, 32, 2>(Sb, Nf, FR);
   return Hf == 1 ? lds_need<64, 64, 1>(Sb, Nf, FR) : lds_need<64, 64, 2>(Sb, Nf, FR);
+}
+
+// One wavefront per (b, query block): flags -> ascending kept list, by ballots.
+__global__ __launch_bounds__(256) void flag_compact_kernel(FlagCompact p) {
+  const int lane = threadIdx.x & 63;
+  const int a = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int b = blockIdx.y;
+  if (a >= p.Sb) return;
+  const int r0 = p.row_ptr[a], n = p.row_ptr[a + 1] - r0;
+  const unsigned char* fl = p.flags + (long long)b * p.flag_stride + r0;
+  int kept = 0;
+  for (int i0 = 0; i0 < n; i0 += 64) {
+    const int i = i0 + lane;
+    const bool keep = i < n && fl[i] != 0;
+    const unsigned long long m = __ballot(keep);
+    const int before = __builtin_amdgcn_mbcnt_hi((unsigned)(m >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)m, 0));
+    if (keep) {
+      const int col = p.cols[r0 + i];
+      for (int h = 0; h < p.H; ++h) p.kept_col[(long long)(b * p.H + h) * p.nnz + r0 + kept + before] = col;
+    }
+    kept += __popcll(m);
+  }
+  if (lane == 0)
+    for (int h = 0; h < p.H; ++h) p.kept_cnt[(long long)(b * p.H + h) * p.Sb + a] = kept;
+}
+
+hipError_t launch_flag_compact(const FlagCompact& c, int B, hipStream_t stream) {
+  hipLaunchKernelGGL(flag_compact_kernel, dim3((unsigned)((c.Sb + 3) / 4), (unsigned)B), dim3(256), 0, stream, c);
+  return hipGetLastError();
 }
 
 hipError_t launch_token_select(const TokParams& p, int B, int D, int Bs, int Hf, hipStream_t stream) {

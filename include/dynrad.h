@@ -12,6 +12,8 @@
  *                           ([DR] §3.2: static-ratio / dynamic-threshold).
  *      dr_token_select      the paper's token-level dynamic-threshold selector
  *                           ([DR] §3.2 Eqs. 9-11, Algorithm 1).
+ *      dr_static_select     the paper's decay-state static-ratio selector
+ *                           ([DR] §3.2 Eq. 8, Algorithm 1), content-free.
  *   3. dr_sparse_attn       flash-style forward attention over the kept KV
  *                           blocks only ([DR] §3.3, Eq. 13 with eps -> 0).
  *   dr_attn                 dense forward attention, the speedup denominator
@@ -185,6 +187,43 @@ dr_status dr_token_select(const dr_dims* dims, const dr_radial_cfg* cfg, const d
                           const void* q, const void* k, const int32_t* row_ptr, const int32_t* cols,
                           int64_t nnz, int32_t* kept_col, int32_t* kept_cnt, void* ws, size_t ws_bytes,
                           hipStream_t stream);
+
+/* Decay-state static-ratio selection: the selector of [DR] §3.2 "Static-ratio
+ * mode" (Eq. 8, Algorithm 1), aggregated to blocks by the density control of
+ * §3.1. It reads no tensor: the mask depends on cfg, rho and the seed only, so
+ * it is built once and reused for every layer and step.
+ * For every frame pair (i, j), t = |i - j|:
+ *   - t mod sf(t) != 0: no pair (Eq. 6);
+ *   - t <= 1: every pair of P(i, j) is selected (rho = 1; t = 0 is dense);
+ *   - otherwise k = max(1, floor(|P(i, j)| * rho + 1e-9)) (float64) pairs of
+ *     P(i, j) = {|u - v| <= w(t)} (Eq. 7), rho = rho_near if
+ *     L(t) = L0 / 2^B(t) * gamma >= B_s else rho_far (Eq. 8), drawn uniformly
+ *     with the seed: pair (u, v) gets the 32-bit output word (v mod 4) of
+ *     Philox4x32-10 (Salmon et al., "Parallel Random Numbers: As Easy as 1, 2,
+ *     3", SC 2011) at counter (u, floor(v / 4), i, j) under the key
+ *     (seed mod 2^32, seed div 2^32), and the k pairs with the smallest
+ *     (word, u * N_t + v) are selected (a uniformly random k-subset).
+ * Block pair (a, b) is kept iff, over all frame pairs it spans, the share of
+ * b's key tokens whose selected share of a's query tokens exceeds theta_c
+ * itself exceeds theta_m. The one mask is written for every (b, h) of dims
+ * (head_dim is not used; pass batch = heads = 1 for a single copy).
+ * Inputs: row_ptr, cols from dr_build_candidates with the same cfg.
+ * Outputs: kept_col / kept_cnt in the layout of dr_score_select.
+ * Limits: tokens_per_frame in [32, 65535], num_frames <= 64, rho_near and
+ * rho_far in [0, 1]. Bit-reproducible (integer work only). */
+typedef struct dr_static_cfg {
+  double rho_near;   /* rho_1, topk_ratio1: retention for t > 1, L(t) >= B_s (Eq. 8) */
+  double rho_far;    /* rho_2, topk_ratio2: retention for t > 1, L(t) <  B_s         */
+  uint64_t seed;     /* Philox key: (seed mod 2^32, seed div 2^32)                  */
+} dr_static_cfg;
+
+/* Device workspace (bytes) of dr_static_select: 48 + 8192 bytes per ordered
+ * frame pair, plus nnz bytes (each part 256-byte aligned). Host only. */
+dr_status dr_static_select_workspace(const dr_radial_cfg* cfg, int64_t nnz, size_t* bytes);
+
+dr_status dr_static_select(const dr_dims* dims, const dr_radial_cfg* cfg, const dr_static_cfg* st,
+                           const int32_t* row_ptr, const int32_t* cols, int64_t nnz, int32_t* kept_col,
+                           int32_t* kept_cnt, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Block-sparse forward attention ([DR] §3.3 Eqs. 12-13, eps -> 0): for each
  * (b, h) and query block a, O[rows of a] = softmax(Q K^T * softmax_scale) V over

@@ -674,6 +674,16 @@ def static_pair_keys(u, v, i: int, j: int, tokens_per_frame: int, seed: int) -> 
     return (x << np.uint64(32)) | (u * np.uint64(tokens_per_frame) + v)
 
 
+def static_frame_sorted_keys(i: int, j: int, tokens_per_frame: int, window: int, seed: int) -> np.ndarray:
+    """Sort keys of all pairs of P(i, j) = {|u - v| <= window} (Eq. 7), ascending."""
+    Nt = tokens_per_frame
+    keys = []
+    for u in range(Nt):
+        v = np.arange(max(0, u - window), min(Nt - 1, u + window) + 1)
+        keys.append(static_pair_keys(np.full(v.shape, u), v, int(i), int(j), Nt, seed))
+    return np.sort(np.concatenate(keys))
+
+
 def static_frame_thresholds(num_frames: int, tokens_per_frame: int, block_size: int, gamma: float, lam: float,
                             rho_near: float, rho_far: float, seed: int, query_frames=None) -> dict:
     """{(i, j): (|P|, k, largest kept sort key)} for every retained frame pair
@@ -687,13 +697,9 @@ def static_frame_thresholds(num_frames: int, tokens_per_frame: int, block_size: 
             t = abs(int(i) - j)
             if t <= 1 or t % sf[t] != 0:
                 continue
-            keys = []
-            for u in range(Nt):   # P(i, j) row by row (Eq. 7)
-                v = np.arange(max(0, u - w[t]), min(Nt - 1, u + w[t]) + 1)
-                keys.append(static_pair_keys(np.full(v.shape, u), v, int(i), j, Nt, seed))
-            keys = np.concatenate(keys)
+            keys = static_frame_sorted_keys(int(i), j, Nt, w[t], seed)
             k = static_pair_count(len(keys), static_rho(t, Nt, block_size, gamma, rho_near, rho_far))
-            out[(int(i), j)] = (len(keys), k, int(np.sort(keys)[k - 1]))
+            out[(int(i), j)] = (len(keys), k, int(keys[k - 1]))
     return out
 
 

@@ -166,3 +166,30 @@ def test_token_select_validation(dynrad_lib):
     assert ts(q=None) == L.DR_ERR_INVALID_ARG
     assert ts(ws_bytes=100) == L.DR_ERR_CAPACITY
     assert ts(t=L.TokenCfg(2, 0, float("-inf"), float("inf"), 1e-6), ws_bytes=100) == L.DR_ERR_CAPACITY
+
+
+def test_static_select_validation(dynrad_lib):
+    """dr_static_select rejects out-of-range configurations before any HIP call;
+    its workspace is 48 + 8192 bytes per ordered frame pair plus the flags."""
+    from block_sparse_attention_candidates_amd import _lib as L
+    FAKE = ctypes.c_void_p(4096)
+    cfg = _cfg(4, 64, 32, 1.0, 2.0)             # S = 256, S_b = 8, 16 frame pairs
+    dims = L.Dims(1, 2, 64, 0)
+    sc = L.StaticCfg(0.5, 0.3, 7)
+    size = ctypes.c_size_t(0)
+    assert dynrad_lib.dr_static_select_workspace(ctypes.byref(cfg), 64, ctypes.byref(size)) == L.DR_OK
+    # states 16 x 48 = 768; histograms 16 x 8192 = 131072; flags 64 -> 256
+    assert size.value == 768 + 131072 + 256
+
+    def ss(d=dims, c=cfg, s=sc, nnz=64, ws_bytes=1 << 20, rp=FAKE):
+        return dynrad_lib.dr_static_select(ctypes.byref(d), ctypes.byref(c), ctypes.byref(s) if s else None, rp,
+                                           FAKE, nnz, FAKE, FAKE, FAKE, ws_bytes, None)
+    assert ss(s=None) == L.DR_ERR_INVALID_ARG
+    assert ss(s=L.StaticCfg(1.5, 0.3, 7)) == L.DR_ERR_INVALID_ARG
+    assert ss(s=L.StaticCfg(0.5, -0.1, 7)) == L.DR_ERR_INVALID_ARG
+    assert ss(s=L.StaticCfg(float("nan"), 0.3, 7)) == L.DR_ERR_INVALID_ARG
+    assert ss(c=_cfg(8, 16, 32, 1.0, 2.0)) == L.DR_ERR_UNSUPPORTED            # N_t < 32
+    assert ss(c=_cfg(65, 64, 32, 1.0, 2.0)) == L.DR_ERR_UNSUPPORTED           # N_f > 64
+    assert ss(nnz=0) == L.DR_ERR_INVALID_ARG
+    assert ss(rp=None) == L.DR_ERR_INVALID_ARG
+    assert ss(ws_bytes=100) == L.DR_ERR_CAPACITY
