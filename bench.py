@@ -1,11 +1,16 @@
 """Benchmark of the DynamicRad block-sparse attention hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--mode static|dynamic]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--mode static|dynamic|token|decay-static] [--preset low|mid|high]
 
 One step = one pass of the whole hot path over one batch of synthetic input
 already resident in HBM: candidate build (asynchronous form), block mean
 pooling + scoring + selection, and block-sparse flash attention. The dense
 kernel is timed separately as the speedup denominator. Prints one JSON line.
+
+--mode decay-static: the paper's content-free static-ratio selector (Eq. 8);
+its mask depends on no tensor, so it is built once (timed separately as
+stage_ms.mask_build) and a step is the sparse attention over it.
 
 Metric: sparse-attention effective TFLOP/s (4 * B_s^2 * D per kept block,
 kept blocks only) with the speedup over the on-GPU dense kernel, on one GPU.
@@ -35,11 +40,13 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="wan14b_720p")
-    ap.add_argument("--mode", default="static", choices=["static", "dynamic", "token"],
-                    help="block-level static-ratio / dynamic-threshold selection, or the paper's token-level "
-                         "dynamic-threshold selector (dr_token_select) with a Table 2 preset")
+    ap.add_argument("--mode", default="static", choices=["static", "dynamic", "token", "decay-static"],
+                    help="block-level static-ratio / dynamic-threshold selection, the paper's token-level "
+                         "dynamic-threshold selector (dr_token_select) or its decay-state static-ratio "
+                         "selector (dr_static_select), the last two with a Table 2 preset")
     ap.add_argument("--preset", default="mid", choices=["low", "mid", "high"],
-                    help="Table 2 dynamic preset of --mode token")
+                    help="Table 2 preset (dynamic rows for --mode token, static rows for --mode decay-static)")
+    ap.add_argument("--seed", type=int, default=2024, help="sampling seed of --mode decay-static")
     ap.add_argument("--stage-iters", type=int, default=20)
     ap.add_argument("--dense-iters", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -89,6 +96,8 @@ def cpu_baseline(w, mode, ratio, tau, n_blocks):
         cores = 1
     if mode == "token":
         return cpu_baseline_token(w, tau, cores)
+    if mode == "decay-static":
+        return cpu_baseline_decay_static(w, tau, cores)
     q, k, v = (x.astype(np.float64) for x in workloads.head_qkv(w, 0, 0))
     Sb = w.num_blocks
     blocks = np.unique(np.linspace(0, Sb - 1, n_blocks).astype(int))
@@ -142,6 +151,36 @@ def cpu_baseline_token(w, taus, cores):
                       f"float64 NumPy"}
 
 
+def cpu_baseline_decay_static(w, rho_seed, cores, n_blocks=16):
+    """Decay-state static mode: n_blocks query blocks evenly spaced inside
+    frame N_f/2, with the sample cuts of that frame's frame pairs, their
+    selection and their attention on head 0."""
+    import workloads
+    from oracle import dynrad_oracle as O
+    rn, rf, seed = rho_seed
+    q, k, v = (x.astype(np.float64) for x in workloads.head_qkv(w, 0, 0))
+    Nf, Nt, Bs = w.num_frames, w.tokens_per_frame, w.block_size
+    f = Nf // 2
+    inside = [a for a in range(f * Nt // Bs, ((f + 1) * Nt - 1) // Bs + 1)
+              if a * Bs // Nt == f and ((a + 1) * Bs - 1) // Nt == f]
+    blocks = [inside[int(x)] for x in np.unique(np.linspace(0, len(inside) - 1, n_blocks).astype(int))]
+    t0 = time.perf_counter()
+    th = O.static_frame_thresholds(Nf, Nt, Bs, w.gamma, w.lam, rn, rf, seed, query_frames=[f])
+    kept = O.static_select_rows(blocks, Nf, Nt, Bs, w.gamma, w.lam, rn, rf, seed, w.theta_c, w.theta_m,
+                                thresholds=th)
+    klist = [np.zeros(0, dtype=np.int64)] * w.num_blocks
+    for a, ks in zip(blocks, kept):
+        klist[a] = ks
+    O.sparse_attention_rows(q, k, v, Bs, klist, blocks)
+    dt = time.perf_counter() - t0
+    flops = 4.0 * Bs ** 2 * w.head_dim * sum(len(x) for x in kept)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "seconds": round(dt, 3),
+            "sample": f"{w.name}: {len(blocks)} query blocks inside frame {f}, all stages (sample cuts of that "
+                      f"frame's {len(th)} sampled frame pairs, decay-state static selection, attention on head 0), "
+                      f"float64 NumPy"}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -157,9 +196,11 @@ def main():
         from block_sparse_attention_candidates_amd import build
         build.build()
     w = workloads.get_workload(args.workload)
-    taus = None
+    taus = rhos = None
     if args.mode == "token":
         w, taus = workloads.token_workload(args.workload, args.preset)
+    if args.mode == "decay-static":
+        w, rhos = workloads.static_workload(args.workload, args.preset)
     ratio = w.static_ratio if args.mode == "static" else 1.0
     tau = w.dynamic_tau if args.mode == "dynamic" else 1.0
     print(f"# generating {w.name}: B={w.batch} H={w.heads} S={w.seq_len} D={w.head_dim}", file=sys.stderr, flush=True)
@@ -172,7 +213,19 @@ def main():
     L = _lib.lib()
     dims = _lib.Dims(w.batch, w.heads, w.head_dim, 0)
     wsb = ctypes.c_size_t(0)
-    if args.mode == "token":
+    ms_mask = None
+    if args.mode == "decay-static":
+        # content-free mask, built once (cached across layers and steps)
+        kept = dr.static_select(cand, rhos[0], rhos[1], args.seed, batch=w.batch, heads=w.heads)
+        # wall clock of the whole build (candidate CSR, whose size the host reads, and the mask)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(3):
+            c2 = dr.build_candidates(cfg)
+            dr.static_select(c2, rhos[0], rhos[1], args.seed, batch=w.batch, heads=w.heads)
+        torch.cuda.synchronize()
+        ms_mask = (time.perf_counter() - t0) * 1e3 / 3
+    elif args.mode == "token":
         kept = dr.token_select(q, k, cand, taus[0], taus[1])
         tokc = _lib.TokenCfg(2, 0, float(taus[0]), float(taus[1]), 1e-6)
         _lib.check(L.dr_token_select_workspace(ctypes.byref(dims), ctypes.byref(cfg), ctypes.byref(tokc), cand.nnz,
@@ -188,6 +241,11 @@ def main():
     row_ptr = torch.empty_like(cand.row_ptr)
     cols = torch.empty_like(cand.cols)
     kept_col, kept_cnt = torch.empty_like(kept.kept_col), torch.empty_like(kept.kept_cnt)
+    if args.mode == "decay-static":
+        row_ptr.copy_(cand.row_ptr)
+        cols.copy_(cand.cols)
+        kept_col.copy_(kept.kept_col)
+        kept_cnt.copy_(kept.kept_cnt)
     scale = 1.0 / math.sqrt(w.head_dim)
 
     def stream():
@@ -215,6 +273,9 @@ def main():
                                     ctypes.c_float(scale), out.data_ptr(), stream()))
 
     def step():
+        if args.mode == "decay-static":   # the mask is cached: attention only
+            step_attn()
+            return
         step_candidates()
         step_select()
         step_attn()
@@ -229,8 +290,8 @@ def main():
     ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
 
     # per-stage HIP-event timing on the launch stream
-    ms_cand = event_ms(step_candidates, args.stage_iters, torch)
-    ms_sel = event_ms(step_select, args.stage_iters, torch)
+    ms_cand = event_ms(step_candidates, args.stage_iters, torch) if ms_mask is None else None
+    ms_sel = event_ms(step_select, args.stage_iters, torch) if ms_mask is None else None
     ms_attn = event_ms(step_attn, args.stage_iters, torch)
     kept_total = int(kept_cnt.sum().item())
     Sb = cand.num_blocks
@@ -251,7 +312,9 @@ def main():
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": w.name, "mode": args.mode, "ratio": ratio if args.mode == "static" else None,
                    "tau": tau if args.mode == "dynamic" else None,
-                   "tau_near_far": list(taus) if taus else None, "theta_c": w.theta_c, "theta_m": w.theta_m,
+                   "tau_near_far": list(taus) if taus else None,
+                   "rho_near_far": list(rhos) if rhos else None, "seed": args.seed if rhos else None,
+                   "theta_c": w.theta_c, "theta_m": w.theta_m,
                    "batch": w.batch, "heads": w.heads,
                    "seq_len": w.seq_len, "head_dim": w.head_dim, "block_size": w.block_size, "gamma": w.gamma,
                    "lambda": w.lam, "parallelism": "single-gpu"},
@@ -260,9 +323,10 @@ def main():
         "kept_blocks": kept_total,
         "speedup_vs_dense": round(ms_dense / ms_step, 3) if ms_dense else None,
         "speedup_vs_dense_attention_only": round(ms_dense / ms_attn, 3) if ms_dense else None,
-        "stage_ms": {"build_candidates": round(ms_cand, 4),
-                     ("token_select" if args.mode == "token" else "score_select"): round(ms_sel, 4),
-                     "sparse_attn": round(ms_attn, 4), "dense_attn": round(ms_dense, 3) if ms_dense else None},
+        "stage_ms": ({"mask_build": round(ms_mask, 4)} if ms_mask is not None else
+                     {"build_candidates": round(ms_cand, 4),
+                      ("token_select" if args.mode == "token" else "score_select"): round(ms_sel, 4)}) |
+                    {"sparse_attn": round(ms_attn, 4), "dense_attn": round(ms_dense, 3) if ms_dense else None},
         "dense_tflops": round(dense_flops / (ms_dense * 1e-3) / 1e12, 2) if ms_dense else None,
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
@@ -281,8 +345,8 @@ def main():
         del src, dst
     if not args.no_cpu:
         print("# timing the CPU oracle sample", file=sys.stderr, flush=True)
-        res["cpu_baseline"] = cpu_baseline(w, args.mode, ratio, taus if args.mode == "token" else tau,
-                                           args.cpu_blocks)
+        extra = taus if args.mode == "token" else ((rhos[0], rhos[1], args.seed) if rhos else tau)
+        res["cpu_baseline"] = cpu_baseline(w, args.mode, ratio, extra, args.cpu_blocks)
     print(json.dumps(res), flush=True)
 
 
