@@ -42,6 +42,11 @@ Stages:
                           sample of max(1, floor(|P(i, j)| * rho)) candidate pairs
                           drawn with a seeded counter-based generator
                           (Philox4x32-10), then the same aggregation to blocks
+12. proxy_*               the proxy-task objective ([DR] App. C.2 / C.4, Eq. 22):
+                          normalised squared error of the sparse attention
+                          matrix against the dense one plus a sparsity penalty;
+                          exactly on tiny inputs, and through a random probe
+                          (the form the attention kernels can evaluate)
 
 Readings where the pages leave a step open are stated at each function.
 """
@@ -759,3 +764,81 @@ def static_select(num_frames: int, tokens_per_frame: int, block_size: int, gamma
     S_b = -(-(num_frames * tokens_per_frame) // block_size)
     return static_select_rows(range(S_b), num_frames, tokens_per_frame, block_size, gamma, lam, rho_near,
                               rho_far, seed, theta_c, theta_m)
+
+
+# ---------------------------------------------------------------------------
+# 12. Proxy-task objective ([DR] App. C.2 "Mathematical Formulation of the
+#     Proxy Task", C.4 "Optimization Objective", Eq. 22):
+#     L(x) = ||A_dense - A_sparse(x)||_F^2 / ||A_dense||_F^2
+#            + alpha * ReLU(target - S(x)),  alpha = 10, target = 0.8,
+#     with A the row-softmax attention matrix (A_sparse: the softmax restricted
+#     to the kept blocks, Eq. 13 with eps -> 0) and S the sparsity ratio.
+#     Reading: over several heads (and batch elements) both norms are summed
+#     before the ratio. The attention kernels return O = A V, not A; with V a
+#     probe Z of independent N(0, 1) entries, E ||(A - A') Z||_F^2 =
+#     D ||A - A'||_F^2 and E ||A Z||_F^2 = D ||A||_F^2, so the ratio of the
+#     output errors estimates the normalised error of the matrices.
+# ---------------------------------------------------------------------------
+PROXY_ALPHA = 10.0
+PROXY_TARGET = 0.8
+
+
+def proxy_attention_matrices(q, k, kept, block_size: int, scale: float = None):
+    """Dense and kept-block attention matrices [S, S] of one head (tiny sizes)."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    S = q.shape[0]
+    scale = 1.0 / math.sqrt(q.shape[1]) if scale is None else scale
+    logits = (q @ k.T) * scale
+    dense = _softmax_rows(logits)
+    mask = np.zeros((S, S), dtype=bool)
+    for a, ks in enumerate(kept):
+        for b in ks:
+            mask[a * block_size:min(S, (a + 1) * block_size), b * block_size:min(S, (b + 1) * block_size)] = True
+    sparse = np.zeros((S, S))
+    for i in range(S):
+        if mask[i].any():
+            sparse[i, mask[i]] = _softmax_rows(logits[i:i + 1, mask[i]])[0]
+    return dense, sparse
+
+
+def proxy_nmse_exact(q_heads, k_heads, kept_heads, block_size: int) -> float:
+    """Eq. 22's normalised squared error of the attention matrices, summed over
+    heads before the ratio."""
+    num = den = 0.0
+    for q, k, kept in zip(q_heads, k_heads, kept_heads):
+        d, s = proxy_attention_matrices(q, k, kept, block_size)
+        num += float(((d - s) ** 2).sum())
+        den += float((d ** 2).sum())
+    return num / den
+
+
+def proxy_error_sums(q, k, z, kept, block_size: int, rows=None):
+    """(sum (O_sparse - O_dense)^2, sum O_dense^2) over the given query rows
+    (all by default) of one head, O = A Z."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    z = np.asarray(z, dtype=np.float64)
+    S = q.shape[0]
+    rows = np.arange(S) if rows is None else np.asarray(rows)
+    o_d = dense_attention(q, k, z, rows=rows)
+    blocks = sorted({int(r) // block_size for r in rows})
+    stacked = sparse_attention_rows(q, k, z, block_size, kept, blocks)   # valid rows of `blocks`, in order
+    o_s = np.zeros((S, z.shape[1]))
+    at = 0
+    for a in blocks:
+        n = min(S, (a + 1) * block_size) - a * block_size
+        o_s[a * block_size:a * block_size + n] = stacked[at:at + n]
+        at += n
+    o_s = o_s[rows]
+    return float(((o_s - o_d) ** 2).sum()), float((o_d ** 2).sum())
+
+
+def proxy_sparsity(kept_heads, S_b: int) -> float:
+    """1 - (kept block pairs) / (heads * S_b^2): the sparsity ratio S(x)."""
+    return 1.0 - sum(len(x) for kept in kept_heads for x in kept) / float(len(kept_heads) * S_b * S_b)
+
+
+def proxy_loss(nmse: float, sparsity: float, alpha: float = PROXY_ALPHA, target: float = PROXY_TARGET) -> float:
+    """Eq. 22: normalised error + alpha * ReLU(target - sparsity)."""
+    return nmse + alpha * max(0.0, target - sparsity)

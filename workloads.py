@@ -231,6 +231,43 @@ def qkv_bits_parallel(w: Workload, heads: Optional[Sequence[int]] = None, worker
     return tuple(out)
 
 
+def proxy_qkz(num_frames: int, frame_h: int, frame_w: int, head_dim: int, heads: int, delta: float, seed: int,
+              batch: int = 1, as_bits: bool = False):
+    """Inputs of the proxy task of "DynamicRad" (arXiv 2604.20470) App. C.2:
+    per token (spatial position) a feature that drifts over frames as the AR(1)
+    process of Eq. 20, h_f = sqrt(1 - delta^2) h_{f-1} + delta eps_f with
+    h_0, eps_f ~ N(0, I) (unit variance at every frame); queries and keys are
+    that feature (the proxy attention A_ij ~ exp(h_i . h_j / sqrt(D))), and the
+    values are an independent N(0, I) probe Z. Per (b, h):
+    rng = default_rng([seed, 7, b, h]); draws in the order h_0, eps_1 ..
+    eps_{N_f-1}, Z; float32, rounded to bfloat16. Returns [B, H, S, D] arrays
+    (Q, K, Z), Q and K identical."""
+    S, D = num_frames * frame_h * frame_w, head_dim
+    dt = np.uint16 if as_bits else np.float32
+    q = np.empty((batch, heads, S, D), dtype=dt)
+    z = np.empty((batch, heads, S, D), dtype=dt)
+    keep = np.float32(math.sqrt(1.0 - delta * delta))
+    fresh = np.float32(delta)
+    for b in range(batch):
+        for h in range(heads):
+            rng = np.random.default_rng([seed, 7, b, h])
+            shape = (frame_h * frame_w, D)
+            X = np.empty((num_frames,) + shape, dtype=np.float32)
+            X[0] = rng.standard_normal(shape, dtype=np.float32)
+            for f in range(1, num_frames):
+                X[f] = keep * X[f - 1] + fresh * rng.standard_normal(shape, dtype=np.float32)
+            Z = rng.standard_normal((S, D), dtype=np.float32)
+            if as_bits:
+                q[b, h], z[b, h] = bf16_bits(X.reshape(S, D)), bf16_bits(Z)
+            else:
+                q[b, h], z[b, h] = bf16_round(X.reshape(S, D)), bf16_round(Z)
+    return q, q.copy(), z
+
+
+# drift rates of the proxy task's motion regimes (App. C.2)
+PROXY_DRIFT = {"low": 0.02, "mid": 0.15, "high": 0.40}
+
+
 # [DR] Table 2, dynamic-threshold rows (BO-optimised presets of the paper's
 # token-level selector): decay gamma, long-range lambda, mask threshold
 # theta_m, column threshold theta_c, near / far thresholds tau_1 / tau_2.
