@@ -27,8 +27,8 @@ from . import _lib as _L
 from ._lib import Dims, DynradError, RadialCfg, SelectCfg, check, lib
 
 __all__ = ["radial_cfg", "num_blocks", "distance_table", "Candidates", "Kept", "build_candidates",
-           "score_select", "token_select", "static_select", "sparse_attn", "attn", "DynradError",
-           "kept_from_lists"]
+           "score_select", "token_select", "static_select", "sparse_attn", "attn", "proxy_error", "proxy_loss",
+           "DynradError", "kept_from_lists"]
 
 
 def radial_cfg(num_frames: int, tokens_per_frame: int, block_size: int, gamma: float, lam: float,
@@ -231,3 +231,37 @@ def kept_from_lists(lists, row_ptr_host, batch: int, heads: int, device="cuda") 
             col[base + row_ptr_host[a]: base + row_ptr_host[a] + len(ks)] = ks
             cnt[(b * heads + h) * Sb + a] = len(ks)
     return Kept(torch.from_numpy(col).to(device), torch.from_numpy(cnt).to(device))
+
+
+def proxy_error(o_ref, o_test, kept: Optional[Kept] = None, workspace=None):
+    """dr_proxy_error: (sum (o_test - o_ref)^2, sum o_ref^2, sum of kept counts)
+    over two bf16 device tensors of equal size (synchronises to read them)."""
+    torch = _torch()
+    if o_ref.dtype != torch.bfloat16 or o_test.dtype != torch.bfloat16 or o_ref.numel() != o_test.numel():
+        raise ValueError("o_ref and o_test must be bf16 tensors of equal size")
+    if not (o_ref.is_contiguous() and o_test.is_contiguous()):
+        raise ValueError("o_ref and o_test must be contiguous")
+    dev = o_ref.device
+    out = torch.empty(3, dtype=torch.float64, device=dev)
+    if workspace is None or workspace.numel() < _L.PROXY_WS_BYTES:
+        workspace = torch.empty(_L.PROXY_WS_BYTES, dtype=torch.uint8, device=dev)
+    cnt = kept.kept_cnt if kept is not None else None
+    check(lib().dr_proxy_error(o_ref.data_ptr(), o_test.data_ptr(), o_ref.numel(),
+                               cnt.data_ptr() if cnt is not None else None, cnt.numel() if cnt is not None else 0,
+                               out.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream(dev)))
+    a, b, c = out.cpu().tolist()
+    return a, b, c
+
+
+def proxy_loss(q, k, z, cand: Candidates, kept: Kept, alpha: float = 10.0, target: float = 0.8) -> dict:
+    """The proxy-task objective of [DR] App. C.4 Eq. 22 for one mask, through
+    the probe z: dense and kept-block attention of (q, k, z), the normalised
+    error of the outputs, the sparsity of the mask and the penalised loss."""
+    o_ref = attn(q, k, z)
+    o_test = sparse_attn(q, k, z, cand, kept)
+    num, den, n_kept = proxy_error(o_ref, o_test, kept)
+    B, H = int(q.shape[0]), int(q.shape[1])
+    sparsity = 1.0 - n_kept / float(B * H * cand.num_blocks ** 2)
+    nmse = num / den
+    return {"nmse": nmse, "sparsity": sparsity, "loss": nmse + alpha * max(0.0, target - sparsity),
+            "err_sum": num, "ref_sum": den, "kept_blocks": int(n_kept)}

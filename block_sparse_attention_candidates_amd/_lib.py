@@ -37,6 +37,9 @@ class TokenCfg(ctypes.Structure):
                 ("tau_near", ctypes.c_double), ("tau_far", ctypes.c_double), ("eps", ctypes.c_double)]
 
 
+PROXY_WS_BYTES = 24576   # DR_PROXY_WS_BYTES
+
+
 class StaticCfg(ctypes.Structure):
     _fields_ = [("rho_near", ctypes.c_double), ("rho_far", ctypes.c_double), ("seed", ctypes.c_uint64)]
 
@@ -75,6 +78,8 @@ def lib() -> ctypes.CDLL:
         "dr_static_select_workspace": (c_int32, [P(RadialCfg), c_int64, P(c_size_t)]),
         "dr_static_select": (c_int32, [P(Dims), P(RadialCfg), P(StaticCfg), c_void_p, c_void_p, c_int64, c_void_p,
                                        c_void_p, c_void_p, c_size_t, c_void_p]),
+        "dr_proxy_error": (c_int32, [c_void_p, c_void_p, c_int64, c_void_p, c_int64, c_void_p, c_void_p, c_size_t,
+                                     c_void_p]),
         "dr_sparse_attn": (c_int32, [P(Dims), P(RadialCfg), c_void_p, c_void_p, c_void_p, c_void_p, c_int64,
                                      c_void_p, c_void_p, c_float, c_void_p, c_void_p]),
         "dr_attn": (c_int32, [P(Dims), c_int32, c_void_p, c_void_p, c_void_p, c_float, c_void_p, c_void_p]),

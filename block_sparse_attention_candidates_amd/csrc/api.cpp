@@ -480,6 +480,29 @@ dr_status dr_static_select(const dr_dims* dims, const dr_radial_cfg* cfg, const 
   return ok();
 }
 
+dr_status dr_proxy_error(const void* o_ref, const void* o_test, int64_t n, const int32_t* kept_cnt, int64_t n_cnt,
+                         double* out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!o_ref || !o_test || !out || !ws) return fail(DR_ERR_INVALID_ARG, "o_ref, o_test, out and ws must be non-NULL");
+  if (n < 1) return fail(DR_ERR_INVALID_ARG, "n must be >= 1");
+  if (n_cnt < 0 || (n_cnt > 0 && !kept_cnt)) return fail(DR_ERR_INVALID_ARG, "n_cnt must be >= 0 (0 when kept_cnt is NULL)");
+  if ((reinterpret_cast<uintptr_t>(o_ref) | reinterpret_cast<uintptr_t>(o_test)) & 15)
+    return fail(DR_ERR_INVALID_ARG, "o_ref and o_test must be 16-byte aligned");
+  static_assert(DR_PROXY_WS_BYTES == dr::kProxyPartials * 3 * sizeof(double), "proxy workspace size");
+  if (ws_bytes < (size_t)DR_PROXY_WS_BYTES)
+    return fail(DR_ERR_CAPACITY, "workspace of %zu bytes below the %d required", ws_bytes, DR_PROXY_WS_BYTES);
+  dr::ProxyParams p;
+  p.ref = static_cast<const uint16_t*>(o_ref);
+  p.test = static_cast<const uint16_t*>(o_test);
+  p.n = n;
+  p.kept_cnt = kept_cnt;
+  p.n_cnt = kept_cnt ? n_cnt : 0;
+  p.partial = static_cast<double*>(ws);
+  p.out = out;
+  const hipError_t e = dr::launch_proxy_error(p, stream);
+  if (e != hipSuccess) return hip_fail(e, "proxy error kernels");
+  return ok();
+}
+
 dr_status dr_sparse_attn(const dr_dims* dims, const dr_radial_cfg* cfg, const void* q, const void* k,
                          const void* v, const int32_t* row_ptr, int64_t nnz, const int32_t* kept_col,
                          const int32_t* kept_cnt, float softmax_scale, void* out, hipStream_t stream) {

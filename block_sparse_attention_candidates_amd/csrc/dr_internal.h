@@ -192,6 +192,19 @@ struct StaticParams {
 };
 constexpr int kStaticBins = 2048;
 hipError_t launch_static_select(const StaticParams& p, hipStream_t stream);
+
+// Proxy-task error sums ([DR] App. C.4 Eq. 22 through a random probe).
+constexpr int kProxyPartials = 1024;   // workgroups of the first pass (one float64 triple each)
+struct ProxyParams {
+  const uint16_t* ref;    // bf16 [n], 16-byte aligned
+  const uint16_t* test;   // bf16 [n], 16-byte aligned
+  long long n;
+  const int32_t* kept_cnt;
+  long long n_cnt;
+  double* partial;        // [kProxyPartials][3]
+  double* out;            // [3]
+};
+hipError_t launch_proxy_error(const ProxyParams& p, hipStream_t stream);
 hipError_t launch_token_select(const TokParams& p, int B, int D, int Bs, int Hf, hipStream_t stream);
 
 hipError_t launch_candidates(const CandParams& p, int32_t* row_ptr, int32_t* cols, long long cap,

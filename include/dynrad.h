@@ -18,6 +18,8 @@
  *                           blocks only ([DR] §3.3, Eq. 13 with eps -> 0).
  *   dr_attn                 dense forward attention, the speedup denominator
  *                           ([DR] App. A, Eq. 16).
+ *   dr_proxy_error          error sums of the proxy-task objective ([DR]
+ *                           App. C.4, Eq. 22) from dense and sparse outputs.
  *
  * Conventions shared by every entry point:
  *  - Tensors are [B, H, S, D] row-major and contiguous, bfloat16 (raw 16-bit
@@ -243,6 +245,24 @@ dr_status dr_sparse_attn(const dr_dims* dims, const dr_radial_cfg* cfg, const vo
  * dr_sparse_attn; seq_len >= 1. */
 dr_status dr_attn(const dr_dims* dims, int32_t seq_len, const void* q, const void* k,
                   const void* v, float softmax_scale, void* out, hipStream_t stream);
+
+/* Proxy-task error sums ([DR] App. C.4 "Optimization Objective", Eq. 22).
+ * Eq. 22 compares the dense attention matrix A with the kept-block one A'.
+ * With o_ref = dr_attn(Q, K, Z) and o_test = dr_sparse_attn(Q, K, Z, mask) for
+ * a probe Z of independent N(0, 1) entries, E ||o_test - o_ref||^2 =
+ * D ||A' - A||_F^2 and E ||o_ref||^2 = D ||A||_F^2, so
+ *   out[0] = sum_i (o_test[i] - o_ref[i])^2     (i < n, bf16 inputs)
+ *   out[1] = sum_i o_ref[i]^2
+ *   out[2] = sum_j kept_cnt[j]                  (j < n_cnt; 0 if kept_cnt is NULL)
+ * give the normalised error out[0] / out[1] and the sparsity
+ * 1 - out[2] / (B * H * S_b^2); the loss is that error plus
+ * alpha * max(0, target - sparsity) (alpha = 10, target = 0.8 in [DR]).
+ * Sums in float64, fixed summation order (bit-reproducible).
+ * o_ref, o_test: device, 16-byte aligned; out: device, 3 doubles; ws: device
+ * workspace of at least DR_PROXY_WS_BYTES bytes. */
+#define DR_PROXY_WS_BYTES 24576
+dr_status dr_proxy_error(const void* o_ref, const void* o_test, int64_t n, const int32_t* kept_cnt, int64_t n_cnt,
+                         double* out, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Static description of a status code. */
 const char* dr_status_string(dr_status status);

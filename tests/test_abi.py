@@ -193,3 +193,18 @@ def test_static_select_validation(dynrad_lib):
     assert ss(nnz=0) == L.DR_ERR_INVALID_ARG
     assert ss(rp=None) == L.DR_ERR_INVALID_ARG
     assert ss(ws_bytes=100) == L.DR_ERR_CAPACITY
+
+
+def test_proxy_error_validation(dynrad_lib):
+    """dr_proxy_error checks pointers, sizes, alignment and workspace before any HIP call."""
+    from block_sparse_attention_candidates_amd import _lib as L
+    A, B = ctypes.c_void_p(4096), ctypes.c_void_p(8192)
+
+    def pe(r=A, t=B, n=100, cnt=None, n_cnt=0, out=A, ws=B, ws_bytes=L.PROXY_WS_BYTES):
+        return dynrad_lib.dr_proxy_error(r, t, n, cnt, n_cnt, out, ws, ws_bytes, None)
+    assert pe(r=None) == L.DR_ERR_INVALID_ARG
+    assert pe(out=None) == L.DR_ERR_INVALID_ARG
+    assert pe(n=0) == L.DR_ERR_INVALID_ARG
+    assert pe(n_cnt=5) == L.DR_ERR_INVALID_ARG            # counts without a pointer
+    assert pe(t=ctypes.c_void_p(8200)) == L.DR_ERR_INVALID_ARG   # not 16-byte aligned
+    assert pe(ws_bytes=L.PROXY_WS_BYTES - 8) == L.DR_ERR_CAPACITY
