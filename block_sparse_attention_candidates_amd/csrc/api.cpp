@@ -51,8 +51,8 @@ dr_status check_radial(const dr_radial_cfg* c, Layout* out) {
     return fail(DR_ERR_INVALID_ARG, "theta_c must be in [0, 1]");
   if (!finite(c->theta_m) || c->theta_m < 0.0 || c->theta_m > 1.0)
     return fail(DR_ERR_INVALID_ARG, "theta_m must be in [0, 1]");
-  if (c->block_size != 32 && c->block_size != 64)
-    return fail(DR_ERR_UNSUPPORTED, "block_size %d not built (32 or 64)", c->block_size);
+  if (c->block_size != 32 && c->block_size != 64 && c->block_size != 128)
+    return fail(DR_ERR_UNSUPPORTED, "block_size %d not built (32, 64 or 128)", c->block_size);
   if (c->num_frames > dr::kMaxFrames)
     return fail(DR_ERR_UNSUPPORTED, "num_frames %d above the limit %d", c->num_frames, dr::kMaxFrames);
   const long long S = (long long)c->num_frames * c->tokens_per_frame;

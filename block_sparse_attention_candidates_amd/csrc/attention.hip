@@ -490,6 +490,8 @@ hipError_t launch_sparse_attn(const AttnParams& p, int D, int Bs, hipStream_t st
   if (D == 128 && Bs == 64) return launch_one<128, 64, true>(p, stream);
   if (D == 64 && Bs == 32) return launch_one<64, 32, true>(p, stream);
   if (D == 64 && Bs == 64) return launch_one<64, 64, true>(p, stream);
+  if (D == 128 && Bs == 128) return launch_one<128, 128, true>(p, stream);
+  if (D == 64 && Bs == 128) return launch_one<64, 128, true>(p, stream);
   return hipErrorInvalidValue;
 }
 

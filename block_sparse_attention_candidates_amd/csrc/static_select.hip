@@ -223,7 +223,7 @@ __global__ __launch_bounds__(kThreads) void pick_kernel(StaticParams p) {
 // workgroup per query block.
 template <int BS>
 __global__ __launch_bounds__(kThreads) void mark_kernel(StaticParams p) {
-  constexpr int FRMAX = 4;   // query frames a block can touch (B_s <= 64, N_t >= 32)
+  constexpr int FRMAX = BS / 32 + 1;   // query frames a block can touch (N_t >= 32)
   const int a = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   __shared__ int s_w[kMaxTokenFrames], s_sf[kMaxTokenFrames];
@@ -259,7 +259,7 @@ __global__ __launch_bounds__(kThreads) void mark_kernel(StaticParams p) {
   for (int e = e0 + wave; e < e1; e += kThreads / 64) {
     const int b = p.cols[e];
     const int nk = min(BS, S - b * BS);
-    int cnt = 0;   // lane c: selected count of key column c of the block
+    int cnt = 0, cnt_hi = 0;   // lane c: selected count of key columns c and 64 + c of the block
 #pragma unroll
     for (int qt = 0; qt < BS / 32; ++qt) {
 #pragma unroll
@@ -322,12 +322,19 @@ __global__ __launch_bounds__(kThreads) void mark_kernel(StaticParams p) {
         for (int c = 0; c < 16; ++c) {
           const unsigned long long m = __ballot((bits >> c) & 1u);
           const int lo = __popcll(m & 0xffffffffull), hi = __popcll(m >> 32);
-          if (lane == 32 * kt + c) cnt += lo;
-          if (lane == 32 * kt + 16 + c) cnt += hi;
+          const int col = 32 * kt + c;   // (+16 for the upper half-wave's keys)
+          if (col < 64) {
+            if (lane == col) cnt += lo;
+            if (lane == col + 16) cnt += hi;
+          } else {
+            if (lane == col - 64) cnt_hi += lo;
+            if (lane == col - 48) cnt_hi += hi;
+          }
         }
       }
     }
-    const int n_act = __popcll(__ballot(lane < nk && cnt >= min_c[nq]));
+    const int n_act = __popcll(__ballot(lane < nk && cnt >= min_c[nq])) +
+                      (BS > 64 ? __popcll(__ballot(64 + lane < nk && cnt_hi >= min_c[nq])) : 0);
     if (lane == 0) p.flags[e] = n_act >= min_a[nk] ? 1 : 0;
   }
 }
@@ -358,7 +365,10 @@ hipError_t launch_all(const StaticParams& p, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_static_select(const StaticParams& p, hipStream_t stream) {
-  return p.Bs == 32 ? launch_all<32>(p, stream) : launch_all<64>(p, stream);
+  if (p.Bs == 32) return launch_all<32>(p, stream);
+  if (p.Bs == 64) return launch_all<64>(p, stream);
+  if (p.Bs == 128) return launch_all<128>(p, stream);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace dr

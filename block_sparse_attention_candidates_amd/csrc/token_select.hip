@@ -106,7 +106,7 @@ struct Geo {
   static constexpr int QB = kRows / BS;             // query blocks per workgroup
   static constexpr int WPQ = BS / 32;               // waves per query block
   // key-block ring in LDS: NB buffers, blocks prefetched NB - 1 steps ahead
-  static constexpr int NB = KBUF <= 16384 ? 5 : 3;
+  static constexpr int NB = KBUF <= 16384 ? 5 : (KBUF <= 32768 ? 3 : 2);
   static constexpr int NI = KBUF / 1024;            // 1 KB direct-to-LDS loads per block
   static constexpr int PERW = NI >= kWaves ? NI / kWaves : 1;   // per issuing wave
 };
@@ -722,10 +722,15 @@ __global__ __launch_bounds__(kThreads) void mark_kernel(TokParams p) {
       if (kb_prev >= 0 && sub == 0 && a < p.Sb && ((L.bits[qb * L.nword + (kb_prev >> 5)] >> (kb_prev & 31)) & 1u)) {
         int* cnt = colcnt + ((j - 1) & 1) * G::QB * BS + qb * BS;
         const int nk = min(BS, p.S - kb_prev * BS);
-        const int c = lane < BS ? cnt[lane] : 0;
-        const int n_act = __popcll(__ballot(lane < nk && c >= min_c[nq]));
+        int n_act = 0;
+#pragma unroll
+        for (int c0 = 0; c0 < BS; c0 += 64) {   // 64 key columns per pass
+          const int c = c0 + lane;
+          const int v = c < BS ? cnt[c] : 0;
+          n_act += __popcll(__ballot(c < nk && v >= min_c[nq]));
+          if (c < BS) cnt[c] = 0;
+        }
         if (lane == 0) flags_l[qb * MS + pos_of(qb, kb_prev) - pos_lo[qb]] = n_act >= min_a[nk] ? 1 : 0;
-        if (lane < BS) cnt[lane] = 0;
       }
     }
     if (j == n) break;
@@ -775,8 +780,8 @@ __global__ __launch_bounds__(kThreads) void mark_kernel(TokParams p) {
 // ---------------------------------------------------------------------------
 template <int D, int BS, int HF>
 __global__ __launch_bounds__(64) void fallback_kernel(TokParams p) {
-  using G = Geo<D, BS, HF>;
-  __shared__ __align__(16) unsigned char kbuf[G::KBUF];
+  using G32 = Geo<D, 32, HF>;   // one 32-key sub-block of all fused heads at a time
+  __shared__ __align__(16) unsigned char kbuf[G32::KBUF];
   __shared__ int s_w[kMaxTokenFrames], s_sf[kMaxTokenFrames];
   __shared__ int cnt[BS];
   const int lane = threadIdx.x, half = lane >> 5;
@@ -802,7 +807,8 @@ __global__ __launch_bounds__(64) void fallback_kernel(TokParams p) {
   // the lowest-numbered one decides for all of them
   const int fa0 = (a * BS) / p.Nt, fa1 = (min(p.S, (a + 1) * BS) - 1) / p.Nt;
   const int fb0 = (kbk * BS) / p.Nt, fb1 = (min(p.S, (kbk + 1) * BS) - 1) / p.Nt;
-  int extra_q[4], extra_k[4], n_extra = 0;
+  constexpr int kFramesPerBlock = BS / 32 + 1;   // frames a block can span (N_t >= 32)
+  int extra_q[kFramesPerBlock * kFramesPerBlock], extra_k[kFramesPerBlock * kFramesPerBlock], n_extra = 0;
   for (int i = fa0; i <= fa1; ++i)
     for (int j = fb0; j <= fb1; ++j) {
       if (!unserved(i, j)) continue;
@@ -829,26 +835,26 @@ __global__ __launch_bounds__(64) void fallback_kernel(TokParams p) {
     s_sf[t] = sf;
   }
   for (int c = lane; c < BS; c += 64) cnt[c] = 0;
-  // stage key block kbk (one wavefront: loop over the chunks)
-  for (int c = lane; c < HF * BS * (D / 8); c += 64) {
-    const int h = c / (BS * (D / 8));
-    const int rem = c - h * (BS * (D / 8));
-    const int key = rem / (D / 8), ch = rem - key * (D / 8);
-    const int tok = kbk * BS + key;
-    u32x4 v = {0, 0, 0, 0};
-    if (tok < p.S) v = *reinterpret_cast<const u32x4*>(p.k + ((size_t)(b * p.H + h) * p.S + tok) * D + ch * 8);
-    *reinterpret_cast<u32x4*>(kbuf + (h * BS + key) * G::RB + ((ch ^ swz<D>(key)) << 4)) = v;
-  }
-  __syncthreads();
-  for (int sub = 0; sub < BS / 32; ++sub) {
-    const int q0 = a * BS + 32 * sub;
-    if (q0 >= p.S) break;
-    bf16x8 qf[HF][D / 16];
-    load_q<D, HF>(p, b, q0, lane, qf);
-    for (int ksub = 0; ksub < BS / 32; ++ksub) {
-      const int ktok0 = kbk * BS + 32 * ksub;
-      if (ktok0 >= p.S) break;
-      const floatx16 acc = tile_scores<D, BS, HF>(qf, kbuf, ksub, lane);
+  for (int ksub = 0; ksub < BS / 32; ++ksub) {
+    const int ktok0 = kbk * BS + 32 * ksub;
+    if (ktok0 >= p.S) break;
+    __syncthreads();   // the previous sub-block's reads are done
+    for (int c = lane; c < HF * 32 * (D / 8); c += 64) {
+      const int h = c / (32 * (D / 8));
+      const int rem = c - h * (32 * (D / 8));
+      const int key = rem / (D / 8), ch = rem - key * (D / 8);
+      const int tok = ktok0 + key;
+      u32x4 v = {0, 0, 0, 0};
+      if (tok < p.S) v = *reinterpret_cast<const u32x4*>(p.k + ((size_t)(b * p.H + h) * p.S + tok) * D + ch * 8);
+      *reinterpret_cast<u32x4*>(kbuf + (h * 32 + key) * G32::RB + ((ch ^ swz<D>(key)) << 4)) = v;
+    }
+    __syncthreads();
+    for (int sub = 0; sub < BS / 32; ++sub) {
+      const int q0 = a * BS + 32 * sub;
+      if (q0 >= p.S) break;
+      bf16x8 qf[HF][D / 16];
+      load_q<D, HF>(p, b, q0, lane, qf);
+      const floatx16 acc = tile_scores<D, 32, HF>(qf, kbuf, 0, lane);
       const TileFrames f = tile_frames(p, q0, ktok0 + (lane & 31));
       const float thr0 = f.kvalid ? p.thr[base + (size_t)f.f0 * p.Nf + f.fk] : INFINITY;
       const float thr1 = (f.kvalid && f.f0 + 1 < p.Nf) ? p.thr[base + (size_t)(f.f0 + 1) * p.Nf + f.fk] : INFINITY;
@@ -862,9 +868,9 @@ __global__ __launch_bounds__(64) void fallback_kernel(TokParams p) {
       int c = __popc(sel);
       c += __shfl_xor(c, 32);
       if (half == 0) cnt[32 * ksub + lane] += c;
-      __syncthreads();
     }
   }
+  __syncthreads();
   if (lane == 0) {
     const int nq = min(BS, p.S - a * BS), nk = min(BS, p.S - kbk * BS);
     p.flags[(long long)b * p.nnz + lo] = block_kept(p, cnt, nq, nk) ? 1 : 0;
@@ -910,6 +916,8 @@ size_t lds_need(int Sb, int Nf, int FR) {
 }
 
 size_t token_lds_bytes(int D, int Bs, int Hf, int Sb, int Nf, int FR) {
+  if (D == 128 && Bs == 128) return Hf == 1 ? lds_need<128, 128, 1>(Sb, Nf, FR) : lds_need<128, 128, 2>(Sb, Nf, FR);
+  if (D == 64 && Bs == 128) return Hf == 1 ? lds_need<64, 128, 1>(Sb, Nf, FR) : lds_need<64, 128, 2>(Sb, Nf, FR);
   if (D == 128 && Bs == 32) return Hf == 1 ? lds_need<128, 32, 1>(Sb, Nf, FR) : lds_need<128, 32, 2>(Sb, Nf, FR);
   if (D == 128 && Bs == 64) return Hf == 1 ? lds_need<128, 64, 1>(Sb, Nf, FR) : lds_need<128, 64, 2>(Sb, Nf, FR);
   if (D == 64 && Bs == 32) return Hf == 1 ? lds_need<64, 32, 1>(Sb, Nf, FR) : lds_need<64, 32, 2>(Sb, Nf, FR);
@@ -954,6 +962,10 @@ hipError_t launch_token_select(const TokParams& p, int B, int D, int Bs, int Hf,
   if (D == 64 && Bs == 32 && Hf == 2) return launch_all<64, 32, 2>(p, B, stream);
   if (D == 64 && Bs == 64 && Hf == 1) return launch_all<64, 64, 1>(p, B, stream);
   if (D == 64 && Bs == 64 && Hf == 2) return launch_all<64, 64, 2>(p, B, stream);
+  if (D == 128 && Bs == 128 && Hf == 1) return launch_all<128, 128, 1>(p, B, stream);
+  if (D == 128 && Bs == 128 && Hf == 2) return launch_all<128, 128, 2>(p, B, stream);
+  if (D == 64 && Bs == 128 && Hf == 1) return launch_all<64, 128, 1>(p, B, stream);
+  if (D == 64 && Bs == 128 && Hf == 2) return launch_all<64, 128, 2>(p, B, stream);
   return hipErrorInvalidValue;
 }
 

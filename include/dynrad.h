@@ -36,7 +36,7 @@
  *  - Arguments are validated before any launch; an invalid call launches
  *    nothing. No entry point aborts or throws. dr_last_error() describes the
  *    most recent failure on the calling thread.
- *  - Limits: head_dim in {64, 128}; block_size in {32, 64}; S_b <= 16384;
+ *  - Limits: head_dim in {64, 128}; block_size in {32, 64, 128}; S_b <= 16384;
  *    N_f <= 4096; batch * heads * nnz < 2^31.
  */
 #ifndef DYNRAD_H
@@ -63,7 +63,7 @@ typedef enum dr_status {
 typedef struct dr_radial_cfg {
   int32_t num_frames;       /* N_f >= 1                                              */
   int32_t tokens_per_frame; /* N_t >= 1 (spatial tokens of one latent frame)         */
-  int32_t block_size;       /* B_s: 32 or 64                                         */
+  int32_t block_size;       /* B_s: 32, 64 or 128 ([DR] Table 4)                     */
   int32_t reserved;         /* must be 0                                             */
   double gamma;             /* decay factor of Eq. 2, > 0                            */
   double lambda;            /* long-range factor of Eq. 4, >= 0                      */

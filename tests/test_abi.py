@@ -66,7 +66,8 @@ FAKE = ctypes.c_void_p(4096)     # never dereferenced: validation fails first
 
 def test_radial_validation(dynrad_lib):
     from block_sparse_attention_candidates_amd import _lib as L
-    bad = [(_cfg(4, 64, 128, 1.0, 2.0), L.DR_ERR_UNSUPPORTED),      # B_s = 128 not built
+    bad = [(_cfg(4, 64, 256, 1.0, 2.0), L.DR_ERR_UNSUPPORTED),      # B_s = 256 not built
+           (_cfg(4, 64, 48, 1.0, 2.0), L.DR_ERR_UNSUPPORTED),       # B_s must be 32, 64 or 128
            (_cfg(4, 64, 0, 1.0, 2.0), L.DR_ERR_INVALID_ARG),
            (_cfg(0, 64, 32, 1.0, 2.0), L.DR_ERR_INVALID_ARG),
            (_cfg(4, 64, 32, 0.0, 2.0), L.DR_ERR_INVALID_ARG),         # gamma must be > 0
@@ -81,6 +82,7 @@ def test_radial_validation(dynrad_lib):
         nnz = ctypes.c_int64(-1)
         assert dynrad_lib.dr_build_candidates(ctypes.byref(cfg), FAKE, FAKE, 10, ctypes.byref(nnz), None) == want
         assert dynrad_lib.dr_last_error().decode() != ""
+    assert dynrad_lib.dr_num_blocks(ctypes.byref(_cfg(4, 64, 128, 1.0, 2.0))) == 2   # B_s = 128 is built
     cfg = _cfg(4, 64, 32, 1.0, 2.0)
     cfg.reserved = 1
     assert dynrad_lib.dr_num_blocks(ctypes.byref(cfg)) == -L.DR_ERR_INVALID_ARG

@@ -116,7 +116,8 @@ def _random_case(B, H, S, D, Bs, seed, density=0.3, empty_rows=(), bad_entries=F
 
 
 @pytest.mark.parametrize("B,H,S,D,Bs", [(2, 3, 1000, 128, 32), (1, 2, 777, 64, 64), (2, 1, 300, 64, 32),
-                                        (1, 2, 40, 128, 32), (1, 1, 1100, 128, 64), (3, 2, 513, 128, 64)])
+                                        (1, 2, 40, 128, 32), (1, 1, 1100, 128, 64), (3, 2, 513, 128, 64),
+                                        (1, 2, 1000, 128, 128), (2, 1, 777, 64, 128)])
 def test_sparse_attention_random_masks(B, H, S, D, Bs):
     G.log(f"[attn] random masks B={B} H={H} S={S} D={D} Bs={Bs}")
     q, k, v, cand, kept, lists, f64 = _random_case(B, H, S, D, Bs, seed=S + D)

@@ -95,3 +95,26 @@ def test_select_edge_cases_and_determinism():
         la = G.kept_lists(a, rp, cand.nnz, cand.num_blocks, bh)
         lb = G.kept_lists(b, rp, cand.nnz, cand.num_blocks, bh)
         assert all(np.array_equal(x, y) for x, y in zip(la, lb))
+
+
+@pytest.mark.parametrize("mode,ratio,tau", [("static", 0.3, 1.0), ("dynamic", 1.0, 0.8)])
+def test_score_select_block_size_128(mode, ratio, tau):
+    """B_s = 128 ([DR] Table 4): 10 frames of 300 tokens (ragged last block),
+    3 heads, D = 128, random bf16 Q/K, every head against the oracle."""
+    import torch
+    G.log(f"[select] B_s = 128 {mode}")
+    rng = np.random.default_rng(128)
+    H, S, D, Bs = 3, 3000, 128, 128
+    bits = workloads.bf16_bits(rng.standard_normal((2, 1, H, S, D)).astype(np.float32))
+    q, k = (torch.from_numpy(np.ascontiguousarray(bits[i])).view(torch.bfloat16).cuda() for i in range(2))
+    f64 = (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    cand = G.dr().build_candidates(G.dr().radial_cfg(10, 300, Bs, 1.0, 0.5))
+    rp, cols = G.host_csr(cand)
+    kept = G.dr().score_select(q, k, cand, mode=mode, ratio=ratio, tau=tau, return_scores=True)
+    scores = kept.scores.cpu().numpy().reshape(H, cand.nnz)
+    for h in range(H):
+        s = O.block_scores(O.pool_blocks(f64[0, 0, h], Bs), O.pool_blocks(f64[1, 0, h], Bs), rp, cols)
+        ora, margins = O.select_all(s, rp, cols, mode, ratio=ratio, tau=tau)
+        np.testing.assert_allclose(scores[h], s, rtol=1e-5, atol=G.SCORE_ATOL, err_msg=f"head {h} scores")
+        gl = G.kept_lists(kept, rp, cand.nnz, cand.num_blocks, h)
+        G.check_selection(gl, ora, margins, s, rp, cols, mode, ratio, tau)

@@ -80,6 +80,15 @@ def test_static_straddling_bs64_batch2_heads3():
     _compare_rows(cand, kept, *args, bh_count=6, label="bs64")
 
 
+@pytest.mark.parametrize("case", [(6, 200, 128, 1.4, 0.7, 0.2, 0.3, 0.3, 0.2, 77),
+                                  (9, 33, 128, 1.2, 0.2, 0.1, 0.3, 0.5, 0.4, 78)])
+def test_static_block_size_128(case):
+    """B_s = 128, incl. N_t = 33 where a block spans up to 5 frames."""
+    G.log(f"[static] B_s = 128 {case}")
+    cand, kept = _run(*case)
+    _compare_rows(cand, kept, *case, label="bs128")
+
+
 def test_static_split_stride():
     """lambda = 0.1: sf(t) > 1 drops whole frame distances (Eq. 6)."""
     G.log("[static] split stride > 1")

@@ -108,6 +108,16 @@ def test_token_select_straddling_blocks_bs64_hf1_batch2():
     _run_and_compare(qb, kb, 6, 200, 64, 1.2, 0.5, 0.3, 0.5, -0.5, 1.5, 1, label="bs64")
 
 
+def test_token_select_block_size_128():
+    """B_s = 128: 6 frames of 200 tokens (blocks span up to 2 frames), D = 128,
+    2 heads fused, theta = (0.2, 0.4)."""
+    G.log("[token] B_s = 128")
+    rng = np.random.default_rng(29)
+    qb = _random_bits(rng, (1, 2, 1200, 128))
+    kb = _random_bits(rng, (1, 2, 1200, 128))
+    _run_and_compare(qb, kb, 6, 200, 128, 1.2, 0.5, 0.2, 0.4, -0.5, 1.5, 2, label="bs128")
+
+
 def test_token_select_full_size_sampled():
     """wan13b_480p shape (21 frames x 1560 tokens, 12 heads) with the Table 2
     'mid' preset: oracle statistics over every frame pair, decisions compared

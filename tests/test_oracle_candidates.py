@@ -54,6 +54,7 @@ CASES = [
     (5, 130, 32, 0.6, 1.0, 0.5, 0.1),
     (5, 130, 32, 0.6, 1.0, 0.03, 0.9),
     (17, 24, 64, 1.0, 0.05, 0.1, 0.2),    # B_s = 64, many frames per block
+    (9, 33, 128, 1.2, 0.2, 0.1, 0.3),     # B_s = 128, a block spans up to 5 frames
 ]
 
 
