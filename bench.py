@@ -47,6 +47,7 @@ def parse():
     ap.add_argument("--preset", default="mid", choices=["low", "mid", "high"],
                     help="Table 2 preset (dynamic rows for --mode token, static rows for --mode decay-static)")
     ap.add_argument("--seed", type=int, default=2024, help="sampling seed of --mode decay-static")
+    ap.add_argument("--block-size", type=int, default=None, help="override the workload's block size (32, 64, 128)")
     ap.add_argument("--stage-iters", type=int, default=20)
     ap.add_argument("--dense-iters", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -201,6 +202,9 @@ def main():
         w, taus = workloads.token_workload(args.workload, args.preset)
     if args.mode == "decay-static":
         w, rhos = workloads.static_workload(args.workload, args.preset)
+    if args.block_size:
+        import dataclasses
+        w = dataclasses.replace(w, name=f"{w.name}+bs{args.block_size}", block_size=args.block_size)
     ratio = w.static_ratio if args.mode == "static" else 1.0
     tau = w.dynamic_tau if args.mode == "dynamic" else 1.0
     print(f"# generating {w.name}: B={w.batch} H={w.heads} S={w.seq_len} D={w.head_dim}", file=sys.stderr, flush=True)
