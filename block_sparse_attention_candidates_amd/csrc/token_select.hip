@@ -47,6 +47,19 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
 constexpr int kRows = kWaves * 32;      // query tokens per workgroup
+constexpr int kRingMax = 16;            // ring depth limit (key blocks)
+constexpr int kSpinLimit = 1 << 26;     // bound of every wait
+constexpr int kDone = 0x3fffffff;       // progress of a wave that reads no more blocks
+
+typedef int intx4 __attribute__((ext_vector_type(4)));
+#define DR_LDS __attribute__((address_space(3)))
+__device__ __forceinline__ int ld_relaxed(const int* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+__device__ __forceinline__ void st_relaxed(int* p, int v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+__device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
 
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
@@ -105,10 +118,9 @@ struct Geo {
   static constexpr int KBUF = HF * BS * RB;         // one key block, all fused heads
   static constexpr int QB = kRows / BS;             // query blocks per workgroup
   static constexpr int WPQ = BS / 32;               // waves per query block
-  // key-block ring in LDS: NB buffers, blocks prefetched NB - 1 steps ahead
-  static constexpr int NB = KBUF <= 16384 ? 5 : (KBUF <= 32768 ? 3 : 2);
+  // key-block ring in LDS: NB buffers within a 96 KB budget (at least 2)
+  static constexpr int NB = 98304 / KBUF < 2 ? 2 : (98304 / KBUF > kRingMax ? kRingMax : 98304 / KBUF);
   static constexpr int NI = KBUF / 1024;            // 1 KB direct-to-LDS loads per block
-  static constexpr int PERW = NI >= kWaves ? NI / kWaves : 1;   // per issuing wave
 };
 
 // Fused-head logits of one 32x32 token tile: A = this wave's Q rows (registers),
@@ -150,32 +162,23 @@ __device__ __forceinline__ void load_q(const TokParams& p, int b, int q0, int la
 }
 
 // Stage key block kb of batch b (all fused heads) into LDS buffer buf with
-// direct-to-LDS loads: load n (64 lanes x 16 B) of the block is issued by wave
-// n % kWaves and fills bytes [1024 n, 1024 n + 1024) of the buffer, that is
-// chunk slots 64 n .. 64 n + 63 in row-major order. Slot s of key row r holds
-// the row's logical chunk s ^ swz(key), so the source address carries the
-// swizzle. Keys >= S read the last token instead (finite values that no
-// selection uses: tiles holding them take the masked path).
+// direct-to-LDS loads issued by one wave: load n (64 lanes x 16 B) fills bytes
+// [1024 n, 1024 n + 1024) of the buffer, that is chunk slots 64 n .. 64 n + 63
+// in row-major order. Slot s of key row r holds the row's logical chunk
+// s ^ swz(key), so the source address carries the swizzle. Keys >= S read the
+// last token instead (finite values that no selection uses: tiles holding them
+// take the masked path).
 template <int D, int BS, int HF>
-__device__ __forceinline__ void issue_block(const TokParams& p, int b, int kb, unsigned char* buf, int wave, int lane) {
+__device__ __forceinline__ void issue_block(const TokParams& p, int b, int kb, unsigned char* buf, int lane) {
   using G = Geo<D, BS, HF>;
-  for (int n = wave; n < G::NI; n += kWaves) {
+#pragma unroll 4
+  for (int n = 0; n < G::NI; ++n) {
     const int c = n * 64 + lane;
     const int row = c / (D / 8), slot = c % (D / 8);
     const int h = row / BS, key = row % BS;
     const int tok = min(kb * BS + key, p.S - 1);
     dma16(p.k + ((size_t)(b * p.H + h) * p.S + tok) * D + (size_t)(slot ^ swz<D>(key)) * 8, buf + n * 1024);
   }
-}
-
-// Wait until this wave's loads of a step have landed, `later` steps having
-// been issued after it (later <= NB - 2).
-template <int D, int BS, int HF>
-__device__ __forceinline__ void wait_block(int later, int wave) {
-  using G = Geo<D, BS, HF>;
-  if (G::NI < kWaves && wave >= G::NI) return;     // issues nothing
-  if (later >= G::NB - 2) wait_vmcnt<G::PERW * (G::NB - 2)>();
-  else wait_vmcnt<0>();
 }
 
 // Per-lane view of one tile's token pairs: the lane's key token and, for its
@@ -267,6 +270,8 @@ __device__ __forceinline__ void select_bits(const TokParams& p, const floatx16& 
 // LDS layout shared by the stats and mark kernels: key staging (2 buffers),
 // per-query-block candidate bitmaps and their CSR word prefixes, the union
 // bitmap, and the per-distance table; then kernel-specific areas.
+constexpr int kCtlBytes = 128;   // ring control: prog[8], ready[16], next_issue, padding
+
 template <int D, int BS, int HF>
 struct Lds {
   using G = Geo<D, BS, HF>;
@@ -279,6 +284,9 @@ struct Lds {
   int* steps;           // [Sb / kTokSplit + 2] key blocks of this workgroup's union steps
   int* s_w;             // [Nf]
   int* s_sf;            // [Nf]
+  int* prog;            // [kWaves] ring step each wave may still read (kDone: none)
+  int* ready;           // [kRingMax] step held by each ring buffer (-1: none)
+  int* next_issue;      // next step to be claimed for loading
   unsigned char* rest;  // 16-byte aligned
   __host__ __device__ static size_t align16(size_t x) { return (x + 15) & ~(size_t)15; }
   __device__ unsigned char* kbuf(int j) const { return ring + (j % G::NB) * G::KBUF; }
@@ -293,14 +301,16 @@ struct Lds {
     steps = upre + nword;
     s_w = steps + max_steps(Sb);
     s_sf = s_w + Nf;
-    const size_t used = (size_t)(reinterpret_cast<unsigned char*>(s_sf + Nf) - smem);
-    rest = smem + align16(used);
+    prog = reinterpret_cast<int*>(smem + align16((size_t)(reinterpret_cast<unsigned char*>(s_sf + Nf) - smem)));
+    ready = prog + kWaves;
+    next_issue = ready + kRingMax;
+    rest = reinterpret_cast<unsigned char*>(prog) + kCtlBytes;
   }
   __host__ __device__ static size_t bytes(int Sb, int Nf) {
     const size_t nw = (size_t)(Sb + 31) / 32;
     const size_t used = (size_t)G::NB * G::KBUF + (size_t)G::QB * nw * 8 + nw * 8 + (size_t)max_steps(Sb) * 4 +
                         (size_t)Nf * 8;
-    return (used + 15) & ~(size_t)15;
+    return ((used + 15) & ~(size_t)15) + kCtlBytes;
   }
 };
 
@@ -308,6 +318,94 @@ struct Lds {
 // query group's walk, each taking a contiguous run of its steps).
 __device__ __forceinline__ int step_begin(int nsteps, int split) {
   return (int)(((long long)nsteps * split) / kTokSplit);
+}
+
+// The key-block ring without workgroup barriers. Waves walk only the steps
+// their own query block needs. A wave claims the next step in order with an
+// LDS compare-and-swap when its buffer is free (every wave past the step it
+// held, and that step published), issues its direct-to-LDS copies, and
+// publishes it at its next service point after s_waitcnt vmcnt(0): its only
+// vector-memory operations in the walk are these copies. Every wave services
+// before each step and while waiting, so the lowest wanted step can always be
+// claimed (its buffer is free); waits are bounded.
+template <int D, int BS, int HF>
+__device__ __forceinline__ void ring_service(const TokParams& p, int b, const Lds<D, BS, HF>& L, int n, int& pending,
+                                             int lane) {
+  using G = Geo<D, BS, HF>;
+  if (pending >= 0) {
+    wait_vmcnt<0>();
+    compiler_fence();
+    st_relaxed(&L.ready[pending % G::NB], pending);
+    pending = -1;
+  }
+  const int j = uniform(ld_relaxed(L.next_issue));
+  if (j >= n) return;
+  // explicit LDS loads (a generic load would also wait for copies in flight)
+  const volatile DR_LDS intx4* pv = (const volatile DR_LDS intx4*)(L.prog);
+  const intx4 a = pv[0];
+  const intx4 c = pv[1];
+  const int mn = uniform(min(min(min(a[0], a[1]), min(a[2], a[3])), min(min(c[0], c[1]), min(c[2], c[3]))));
+  if (mn < j - G::NB + 1) return;
+  if (j >= G::NB && uniform(ld_relaxed(&L.ready[j % G::NB])) != j - G::NB) return;
+  int old = 0;
+  if (lane == 0) old = atomicCAS(L.next_issue, j, j + 1);
+  if (uniform(old) != j) return;
+  compiler_fence();
+  __builtin_amdgcn_s_setprio(2);
+  issue_block<D, BS, HF>(p, b, uniform(L.steps[j]), L.kbuf(j), lane);
+  __builtin_amdgcn_s_setprio(0);
+  pending = j;
+}
+
+// Announce step j, then wait (servicing) until its key block is in the ring.
+template <int D, int BS, int HF>
+__device__ __forceinline__ void ring_wait(const TokParams& p, int b, const Lds<D, BS, HF>& L, int n, int& pending,
+                                          int wave, int lane, int j) {
+  using G = Geo<D, BS, HF>;
+  compiler_fence();
+  st_relaxed(&L.prog[wave], j);
+  ring_service<D, BS, HF>(p, b, L, n, pending, lane);
+  int spins = 0;
+  while (ld_relaxed(&L.ready[j % G::NB]) != j && ++spins <= kSpinLimit) {
+    ring_service<D, BS, HF>(p, b, L, n, pending, lane);
+    __builtin_amdgcn_s_sleep(1);
+  }
+  compiler_fence();
+}
+
+// Leave the walk: no more reads, and this wave's last copy published.
+template <int D, int BS, int HF>
+__device__ __forceinline__ void ring_leave(const Lds<D, BS, HF>& L, int& pending, int wave) {
+  using G = Geo<D, BS, HF>;
+  compiler_fence();
+  st_relaxed(&L.prog[wave], kDone);
+  if (pending >= 0) {
+    wait_vmcnt<0>();
+    compiler_fence();
+    st_relaxed(&L.ready[pending % G::NB], pending);
+    pending = -1;
+  }
+}
+
+// Visit the steps of this wave's query block (bitmap row `mine`) within the
+// split's key range in ascending order: f(local step, key block).
+template <int D, int BS, int HF, typename F>
+__device__ __forceinline__ void walk_own(const Lds<D, BS, HF>& L, const unsigned int* mine, int n, int j0, F&& f) {
+  if (n <= 0) return;
+  const int kb_lo = L.steps[0], kb_hi = L.steps[n - 1];
+  for (int wi = kb_lo >> 5; wi <= (kb_hi >> 5); ++wi) {
+    unsigned int m = mine[wi];
+    if (wi == (kb_lo >> 5)) m &= ~0u << (kb_lo & 31);
+    if (wi == (kb_hi >> 5) && (kb_hi & 31) != 31) m &= (1u << ((kb_hi & 31) + 1)) - 1u;
+    if (!m) continue;
+    const unsigned int uw = L.uword[wi];
+    const int up = L.upre[wi] - j0;
+    while (m) {
+      const int bit = __ffs(m) - 1;
+      m &= m - 1;
+      f(up + __popc(uw & ((1u << bit) - 1u)), wi * 32 + bit);
+    }
+  }
 }
 
 // Exclusive prefix sum over a wavefront (lane order); returns the total.
@@ -330,6 +428,9 @@ template <int D, int BS, int HF>
 __device__ __forceinline__ int setup(const TokParams& p, Lds<D, BS, HF>& L, int a0, int split, int* s_nsteps) {
   using G = Geo<D, BS, HF>;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (tid < kWaves) L.prog[tid] = 0;
+  if (tid < kRingMax) L.ready[tid] = -1;
+  if (tid == 0) *L.next_issue = 0;
   for (int t = tid; t < p.Nf; t += kThreads) {
     int w, sf;
     table_entry(t, p.Nt, BS, p.L0, p.gamma, p.lambda, &w, &sf);
@@ -419,7 +520,7 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(TokParams p) {
   // Per-lane running statistics, four sets: query frame f0w + fo (the wave's
   // 32 rows span at most two frames) x key frame parity kp. Keys are walked in
   // ascending order and the 32 keys of a tile span at most two adjacent frames,
-  // so the set of parity kp holds one key frame, tag[kp], at a time; it is
+  // so the set of parity kp holds one key frame (tag0 / tag1) at a time; it is
   // reduced over the wave and merged into the wave's LDS statistics once the
   // walk has passed that frame. Sums are float64 power sums of the float32
   // scores; the highest score keeps its position for safeguard (ii).
@@ -427,9 +528,14 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(TokParams p) {
   int rn[4] = {0, 0, 0, 0};
   float rm[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
   unsigned int rl[4] = {0xffffffffu, 0xffffffffu, 0xffffffffu, 0xffffffffu};
-  int tag[2] = {-1, -1};
+  int tag0 = -1, tag1 = -1;   // key frame held by the parity-0 / parity-1 sets
+  auto tag_of = [&](int kp) -> int { return kp ? tag1 : tag0; };
+  auto set_tag = [&](int kp, int f) {
+    if (kp) tag1 = f;
+    else tag0 = f;
+  };
   auto flush = [&](int kp) {
-    if (tag[kp] < 0) return;
+    if (tag_of(kp) < 0) return;
 #pragma unroll
     for (int fo = 0; fo < 2; ++fo) {
       const int x = 2 * fo + kp;
@@ -442,14 +548,14 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(TokParams p) {
         const double nn = (double)cnt, mean = sum / nn;
         double m2 = sq - sum * mean;
         if (m2 < 0.0) m2 = 0.0;
-        if (lane == 0) merge(mine[fo * p.Nf + tag[kp]], nn, mean, m2, mx);
+        if (lane == 0) merge(mine[fo * p.Nf + tag_of(kp)], nn, mean, m2, mx);
       }
       rs[x] = rq[x] = 0.0;
       rn[x] = 0;
       rm[x] = -INFINITY;
       rl[x] = 0xffffffffu;
     }
-    tag[kp] = -1;
+    set_tag(kp, -1);
   };
   // add a lane's tile sums to set x (x may differ between lanes)
   auto add = [&](int x, double ts, double tq, int tn, float tm, unsigned int tl) {
@@ -466,17 +572,13 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(TokParams p) {
       }
   };
 
-  // key blocks stream through the LDS ring, NB - 1 steps ahead of use
-  constexpr int PF = G::NB - 1;
-  for (int j = 0; j < PF && j < n; ++j) issue_block<D, BS, HF>(p, b, uniform(L.steps[j]), L.kbuf(j), wave, lane);
-  for (int j = 0; j < n; ++j) {
-    wait_block<D, BS, HF>(min(PF - 1, n - 1 - j), wave);
-    __syncthreads();   // step j staged by every wave; step j - 1's buffer free
-    if (j + PF < n) issue_block<D, BS, HF>(p, b, uniform(L.steps[j + PF]), L.kbuf(j + PF), wave, lane);
-    const int kb = uniform(L.steps[j]);
-    const unsigned char* kbuf = L.kbuf(j);
-    const bool need = active_wave && ((L.bits[qb * L.nword + (kb >> 5)] >> (kb & 31)) & 1u);
-    if (need) {
+  // key blocks stream through the LDS ring; this wave visits only its own
+  int pending = -1;
+  const int j0 = step_begin(s_nsteps, split);
+  if (active_wave) {
+    walk_own(L, L.bits + qb * L.nword, n, j0, [&](int j, int kb) __attribute__((always_inline)) {
+      ring_wait<D, BS, HF>(p, b, L, n, pending, wave, lane, j);
+      const unsigned char* kbuf = L.kbuf(j);
 #pragma unroll
       for (int ksub = 0; ksub < BS / 32; ++ksub) {
         const int ktok0 = kb * BS + 32 * ksub;
@@ -487,11 +589,11 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(TokParams p) {
         const int fk_first = ktok0 / p.Nt;
 #pragma unroll
         for (int kp = 0; kp < 2; ++kp)
-          if (tag[kp] >= 0 && tag[kp] < fk_first) flush(kp);
+          if (tag_of(kp) >= 0 && tag_of(kp) < fk_first) flush(kp);
         const floatx16 acc = tile_scores<D, BS, HF>(qf, kbuf, ksub, lane);
         if (ti.cls == kAllScored) {
           // all 1024 pairs in P(fq, fk): one set, no masks
-          tag[ti.fk & 1] = ti.fk;
+          set_tag(ti.fk & 1, ti.fk);
           float v[16], m = -INFINITY;
           double ts = 0.0, tq = 0.0;
 #pragma unroll
@@ -515,17 +617,19 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(TokParams p) {
         }
         // general tile: pairs split by query frame f0 + fo and the lane's key frame
         const TileFrames f = tile_frames(p, q0, ktok0 + (lane & 31));
-        tag[fk_first & 1] = fk_first;
-        if ((min(ktok0 + 31, p.S - 1)) / p.Nt != fk_first) tag[(fk_first + 1) & 1] = fk_first + 1;
+        set_tag(fk_first & 1, fk_first);
+        if ((min(ktok0 + 31, p.S - 1)) / p.Nt != fk_first) set_tag((fk_first + 1) & 1, fk_first + 1);
         const int t0 = f.f0 > f.fk ? f.f0 - f.fk : f.fk - f.f0;
         const int t1 = f.f0 + 1 > f.fk ? f.f0 + 1 - f.fk : f.fk - f.f0 - 1;
         const bool ok0 = f.kvalid && t0 > 1 && t0 < p.Nf && (t0 % L.s_sf[t0]) == 0;
         const bool ok1 = f.kvalid && t1 > 1 && t1 < p.Nf && (t1 % L.s_sf[t1]) == 0;
         const int w0 = t0 < p.Nf ? L.s_w[t0] : 0, w1 = t1 < p.Nf ? L.s_w[t1] : 0;
-        double ts[2] = {0.0, 0.0}, tq[2] = {0.0, 0.0};
-        int tn[2] = {0, 0};
-        float tm[2] = {-INFINITY, -INFINITY};
-        unsigned int tl[2] = {0xffffffffu, 0xffffffffu};
+        // per query frame f0 (suffix 0) and f0 + 1 (suffix 1); scalars, so that
+        // a lane-dependent choice never indexes memory
+        double ts0 = 0.0, tq0 = 0.0, ts1 = 0.0, tq1 = 0.0;
+        int tn0 = 0, tn1 = 0;
+        float tm0 = -INFINITY, tm1 = -INFINITY;
+        unsigned int tl0 = 0xffffffffu, tl1 = 0xffffffffu;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int r = row_of(i, half);
@@ -537,22 +641,33 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(TokParams p) {
           if (!(second ? (ok1 && du <= w1) : (ok0 && du <= w0))) continue;
           const float v = acc[i] * p.scale;
           const double d = (double)v;
-          const int fo = second ? 1 : 0;
-          ts[fo] += d;
-          tq[fo] = fma(d, d, tq[fo]);
-          tn[fo] += 1;
-          if (v > tm[fo]) {   // rows ascend with i: the first maximum has the lowest position
-            tm[fo] = v;
-            tl[fo] = (unsigned)(u * p.Nt + f.uk);
+          const unsigned int loc = (unsigned)(u * p.Nt + f.uk);
+          // rows ascend with i: the first maximum has the lowest position
+          if (second) {
+            ts1 += d;
+            tq1 = fma(d, d, tq1);
+            ++tn1;
+            if (v > tm1) {
+              tm1 = v;
+              tl1 = loc;
+            }
+          } else {
+            ts0 += d;
+            tq0 = fma(d, d, tq0);
+            ++tn0;
+            if (v > tm0) {
+              tm0 = v;
+              tl0 = loc;
+            }
           }
         }
         const int kp = f.fk & 1;
-#pragma unroll
-        for (int fo = 0; fo < 2; ++fo)
-          if (tn[fo] > 0) add(2 * fo + kp, ts[fo], tq[fo], tn[fo], tm[fo], tl[fo]);
+        if (tn0 > 0) add(kp, ts0, tq0, tn0, tm0, tl0);
+        if (tn1 > 0) add(2 + kp, ts1, tq1, tn1, tm1, tl1);
       }
-    }
+    });
   }
+  ring_leave(L, pending, wave);
   flush(0);
   flush(1);
   __syncthreads();
@@ -637,14 +752,15 @@ __global__ __launch_bounds__(kThreads) void mark_kernel(TokParams p) {
   const int MS = Lds<D, BS, HF>::max_steps(p.Sb);
   float* thr_l = reinterpret_cast<float*>(L.rest);                      // [FR][Nf]
   int* served_l = reinterpret_cast<int*>(thr_l + p.FR * p.Nf);          // [FR][Nf]
-  int* colcnt = served_l + p.FR * p.Nf;                                 // [2][QB][BS] when BS > 32
-  unsigned char* flags_l = reinterpret_cast<unsigned char*>(colcnt + (G::WPQ > 1 ? 2 * G::QB * BS : 0));  // [QB][MS]
+  int* colcnt = served_l + p.FR * p.Nf;                                 // [QB][NB][BS] when BS > 32
+  int* arrive = colcnt + (G::WPQ > 1 ? G::QB * G::NB * BS : 0);          // [QB][NB] when BS > 32
+  unsigned char* flags_l = reinterpret_cast<unsigned char*>(arrive + (G::WPQ > 1 ? G::QB * G::NB : 0));  // [QB][MS]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5;
   const int wg = blockIdx.x / kTokSplit, split = blockIdx.x - wg * kTokSplit, b = blockIdx.y;
   const int a0 = wg * G::QB;
   const int f_lo = (a0 * BS) / p.Nt;
   if (G::WPQ > 1)
-    for (int i = tid; i < 2 * G::QB * BS; i += kThreads) colcnt[i] = 0;
+    for (int i = tid; i < G::QB * G::NB * (BS + 1); i += kThreads) colcnt[i] = 0;   // counts and arrivals
   for (int i = tid; i < p.FR * p.Nf; i += kThreads) {
     const int fr = i / p.Nf, fk = i - fr * p.Nf;
     const int fq = f_lo + fr;
@@ -670,6 +786,7 @@ __global__ __launch_bounds__(kThreads) void mark_kernel(TokParams p) {
   const int q0 = a * BS + 32 * sub;
   const bool active_wave = a < p.Sb && q0 < p.S;
   const int nq = a < p.Sb ? min(BS, p.S - a * BS) : 0;
+  const int n_sub = (nq + 31) / 32;   // waves of this query block holding rows
   bf16x8 qf[HF][D / 16];
   if (active_wave) load_q<D, HF>(p, b, q0, lane, qf);
   wait_vmcnt<0>();   // Q resident before the ring's loads are counted
@@ -710,43 +827,23 @@ __global__ __launch_bounds__(kThreads) void mark_kernel(TokParams p) {
     return c + __shfl_xor(c, 32);
   };
 
-  // key blocks stream through the LDS ring, NB - 1 steps ahead of use
-  constexpr int PF = G::NB - 1;
-  for (int j = 0; j < PF && j < n; ++j) issue_block<D, BS, HF>(p, b, uniform(L.steps[j]), L.kbuf(j), wave, lane);
-  int kb_prev = -1;
-  for (int j = 0; j <= n; ++j) {
-    if (j < n) wait_block<D, BS, HF>(min(PF - 1, n - 1 - j), wave);
-    __syncthreads();   // step j staged by every wave; step j - 1 finished
-    if (G::WPQ > 1) {
-      // decide step j - 1 from the counts of all its waves
-      if (kb_prev >= 0 && sub == 0 && a < p.Sb && ((L.bits[qb * L.nword + (kb_prev >> 5)] >> (kb_prev & 31)) & 1u)) {
-        int* cnt = colcnt + ((j - 1) & 1) * G::QB * BS + qb * BS;
-        const int nk = min(BS, p.S - kb_prev * BS);
-        int n_act = 0;
-#pragma unroll
-        for (int c0 = 0; c0 < BS; c0 += 64) {   // 64 key columns per pass
-          const int c = c0 + lane;
-          const int v = c < BS ? cnt[c] : 0;
-          n_act += __popcll(__ballot(c < nk && v >= min_c[nq]));
-          if (c < BS) cnt[c] = 0;
-        }
-        if (lane == 0) flags_l[qb * MS + pos_of(qb, kb_prev) - pos_lo[qb]] = n_act >= min_a[nk] ? 1 : 0;
-      }
-    }
-    if (j == n) break;
-    if (j + PF < n) issue_block<D, BS, HF>(p, b, uniform(L.steps[j + PF]), L.kbuf(j + PF), wave, lane);
-    const int kb = uniform(L.steps[j]);
-    const unsigned char* kbuf = L.kbuf(j);
-    const bool need = active_wave && ((L.bits[qb * L.nword + (kb >> 5)] >> (kb & 31)) & 1u);
-    if (need) {
+  // key blocks stream through the LDS ring; this wave visits only its own.
+  // B_s > 32: the waves of a query block add their column counts in LDS (one
+  // count row per ring buffer) and the last one to arrive decides.
+  int pending = -1;
+  const int j0 = step_begin(s_nsteps, split);
+  if (active_wave) {
+    walk_own(L, L.bits + qb * L.nword, n, j0, [&](int j, int kb) __attribute__((always_inline)) {
+      ring_wait<D, BS, HF>(p, b, L, n, pending, wave, lane, j);
+      const unsigned char* kbuf = L.kbuf(j);
+      const int nk = min(BS, p.S - kb * BS);
       if (G::WPQ == 1) {
         // one wave holds the whole block pair: decide in registers
-        const int nk = min(BS, p.S - kb * BS);
         const int c = tile_count(kbuf, 0, kb * BS);
         const int n_act = __popcll(__ballot(lane < nk && c >= min_c[nq]));
         if (lane == 0) flags_l[qb * MS + pos_of(qb, kb) - pos_lo[qb]] = n_act >= min_a[nk] ? 1 : 0;
       } else {
-        int* cnt = colcnt + (j & 1) * G::QB * BS + qb * BS;
+        int* cnt = colcnt + (qb * G::NB + j % G::NB) * BS;
 #pragma unroll
         for (int ksub = 0; ksub < BS / 32; ++ksub) {
           const int ktok0 = kb * BS + 32 * ksub;
@@ -754,10 +851,29 @@ __global__ __launch_bounds__(kThreads) void mark_kernel(TokParams p) {
           const int c = tile_count(kbuf, ksub, ktok0);
           if (half == 0) atomicAdd(&cnt[32 * ksub + lane], c);
         }
+        // LDS operations of a wave complete in order: its counts are in
+        // before its arrival is counted
+        int arrived = 0;
+        if (lane == 0) arrived = atomicAdd(&arrive[qb * G::NB + j % G::NB], 1) + 1;
+        if (uniform(arrived) == n_sub) {
+          compiler_fence();
+          int n_act = 0;
+#pragma unroll
+          for (int c0 = 0; c0 < BS; c0 += 64) {   // 64 key columns per pass
+            const int col = c0 + lane;
+            const int v = col < BS ? ld_relaxed(&cnt[col]) : 0;
+            n_act += __popcll(__ballot(col < nk && v >= min_c[nq]));
+            if (col < BS) cnt[col] = 0;
+          }
+          if (lane == 0) {
+            flags_l[qb * MS + pos_of(qb, kb) - pos_lo[qb]] = n_act >= min_a[nk] ? 1 : 0;
+            arrive[qb * G::NB + j % G::NB] = 0;
+          }
+        }
       }
-    }
-    kb_prev = kb;
+    });
   }
+  ring_leave(L, pending, wave);
   __syncthreads();
   // write out this split's flags (a contiguous run of each candidate row) and
   // the served frame pairs
@@ -884,7 +1000,7 @@ hipError_t launch_all(const TokParams& p, int B, hipStream_t stream) {
   using G = Geo<D, BS, HF>;
   const size_t base = Lds<D, BS, HF>::bytes(p.Sb, p.Nf);
   const size_t lds_stats = base + (size_t)kWaves * 2 * p.Nf * sizeof(Stat);
-  const size_t lds_mark = base + (size_t)p.FR * p.Nf * 8 + (G::WPQ > 1 ? (size_t)2 * G::QB * BS * 4 : 0) +
+  const size_t lds_mark = base + (size_t)p.FR * p.Nf * 8 + (G::WPQ > 1 ? (size_t)G::QB * G::NB * (BS + 1) * 4 : 0) +
                           (size_t)G::QB * Lds<D, BS, HF>::max_steps(p.Sb);
   const dim3 grid((unsigned)(p.n_wg * kTokSplit), (unsigned)B);
   hipLaunchKernelGGL((stats_kernel<D, BS, HF>), grid, dim3(kThreads), lds_stats, stream, p);
@@ -910,7 +1026,7 @@ size_t lds_need(int Sb, int Nf, int FR) {
   const size_t base = Lds<D, BS, HF>::bytes(Sb, Nf);
   const size_t stats = base + (size_t)kWaves * 2 * Nf * sizeof(Stat);
   // (+ the static arrays of the mark kernel: the integer thresholds and the step count)
-  const size_t mark = base + (size_t)FR * Nf * 8 + (G::WPQ > 1 ? (size_t)2 * G::QB * BS * 4 : 0) +
+  const size_t mark = base + (size_t)FR * Nf * 8 + (G::WPQ > 1 ? (size_t)G::QB * G::NB * (BS + 1) * 4 : 0) +
                       (size_t)G::QB * Lds<D, BS, HF>::max_steps(Sb) + (size_t)(2 * (BS + 1) + G::QB) * 4 + 16;
   return stats > mark ? stats : mark;
 }
