@@ -200,6 +200,33 @@ __device__ __forceinline__ TileFrames tile_frames(const TokParams& p, int q0, in
   return f;
 }
 
+// Frame and spatial index of a token given those of an earlier token of the
+// same or an earlier frame, `add` tokens before it (no division).
+struct FrameAt {
+  int f, u;
+};
+__device__ __forceinline__ FrameAt frame_after(FrameAt at, int add, int Nt) {
+  at.u += add;
+  while (at.u >= Nt) {
+    at.u -= Nt;
+    ++at.f;
+  }
+  return at;
+}
+
+// The same view from the frames of the tile's first query and key tokens
+// (lane key = k0 + lane % 32, N_t >= 32 so at most one frame boundary).
+__device__ __forceinline__ TileFrames tile_frames_at(const TokParams& p, FrameAt q, FrameAt k, int k0, int lane) {
+  TileFrames f;
+  f.f0 = q.f;
+  f.u0 = q.u;
+  f.kvalid = k0 + (lane & 31) < p.S;
+  const FrameAt kl = frame_after(k, lane & 31, p.Nt);
+  f.fk = kl.f;
+  f.uk = kl.u;
+  return f;
+}
+
 // Row i of the lane: query token q0 + r, r = 8*(i/4) + 4*half + i%4.
 __device__ __forceinline__ int row_of(int i, int half) { return 8 * (i >> 2) + 4 * half + (i & 3); }
 
@@ -211,19 +238,20 @@ enum TileClass { kGeneral = 0, kNone = 1, kAllNear = 2, kAllScored = 3 };
 struct TileInfo {
   int cls, fq, fk;
 };
-__device__ __forceinline__ TileInfo classify(const TokParams& p, int q0, int k0, const int* s_w, const int* s_sf) {
+__device__ __forceinline__ TileInfo classify(const TokParams& p, int q0, FrameAt q, int k0, FrameAt k, const int* s_w,
+                                             const int* s_ret) {
   TileInfo ti{kGeneral, 0, 0};
   if (q0 + 31 >= p.S || k0 + 31 >= p.S) return ti;
-  const int fq = q0 / p.Nt, fk = k0 / p.Nt;
-  if ((q0 + 31) / p.Nt != fq || (k0 + 31) / p.Nt != fk) return ti;
+  if (q.u + 31 >= p.Nt || k.u + 31 >= p.Nt) return ti;   // the tile crosses a frame boundary
+  const int fq = q.f, fk = k.f;
   ti.fq = fq;
   ti.fk = fk;
   const int t = fq > fk ? fq - fk : fk - fq;
-  if (t % s_sf[t] != 0) {
+  if (!s_ret[t]) {
     ti.cls = kNone;
     return ti;
   }
-  const int uq = q0 - fq * p.Nt, uk = k0 - fk * p.Nt, w = s_w[t];
+  const int uq = q.u, uk = k.u, w = s_w[t];
   const int dmax = max(uq + 31 - uk, uk + 31 - uq);                  // largest |u - v| in the tile
   const int dmin = max(0, max(uk - (uq + 31), uq - (uk + 31)));      // smallest
   if (dmin > w) ti.cls = kNone;
@@ -234,17 +262,18 @@ __device__ __forceinline__ TileInfo classify(const TokParams& p, int q0, int k0,
 // Selection bits (one per element i) of a tile under the thresholds of the
 // frame pairs involved; inP bits mark the candidate pairs of P with t > 1.
 // thr0 / thr1: thresholds (score units) for query frame f0 / f0 + 1 against
-// the lane's key frame. w/sf: per-distance table in LDS.
+// the lane's key frame. s_w / s_ret: per-distance window and "retained"
+// (t mod sf(t) = 0) tables in LDS.
 __device__ __forceinline__ void select_bits(const TokParams& p, const floatx16& acc, const TileFrames& f, int q0, int half,
-                                   const int* s_w, const int* s_sf, float thr0, float thr1, unsigned& sel,
+                                   const int* s_w, const int* s_ret, float thr0, float thr1, unsigned& sel,
                                    unsigned& inP2) {
   sel = 0;
   inP2 = 0;
   if (!f.kvalid) return;
   const int t0 = f.f0 > f.fk ? f.f0 - f.fk : f.fk - f.f0;
   const int t1 = f.f0 + 1 > f.fk ? f.f0 + 1 - f.fk : f.fk - f.f0 - 1;
-  const bool ret0 = t0 < p.Nf && (t0 % s_sf[t0]) == 0;
-  const bool ret1 = t1 < p.Nf && (t1 % s_sf[t1]) == 0;
+  const bool ret0 = t0 < p.Nf && s_ret[t0];
+  const bool ret1 = t1 < p.Nf && s_ret[t1];
   const int w0 = t0 < p.Nf ? s_w[t0] : 0, w1 = t1 < p.Nf ? s_w[t1] : 0;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
@@ -282,8 +311,9 @@ struct Lds {
   unsigned int* uword;  // [nword]
   int* upre;            // [nword] exclusive prefix of the union popcounts (union step of each word)
   int* steps;           // [Sb / kTokSplit + 2] key blocks of this workgroup's union steps
-  int* s_w;             // [Nf]
-  int* s_sf;            // [Nf]
+  int* sinfo;           // [Sb / kTokSplit + 2] frame f and index u of each step's first key: (u << 8) | f
+  int* s_w;             // [Nf] window w(t), clamped to N_t
+  int* s_ret;           // [Nf] 1 iff t mod sf(t) = 0 (Eq. 6)
   int* prog;            // [kWaves] ring step each wave may still read (kDone: none)
   int* ready;           // [kRingMax] step held by each ring buffer (-1: none)
   int* next_issue;      // next step to be claimed for loading
@@ -299,16 +329,17 @@ struct Lds {
     uword = reinterpret_cast<unsigned int*>(pre + G::QB * nword);
     upre = reinterpret_cast<int*>(uword + nword);
     steps = upre + nword;
-    s_w = steps + max_steps(Sb);
-    s_sf = s_w + Nf;
-    prog = reinterpret_cast<int*>(smem + align16((size_t)(reinterpret_cast<unsigned char*>(s_sf + Nf) - smem)));
+    sinfo = steps + max_steps(Sb);
+    s_w = sinfo + max_steps(Sb);
+    s_ret = s_w + Nf;
+    prog = reinterpret_cast<int*>(smem + align16((size_t)(reinterpret_cast<unsigned char*>(s_ret + Nf) - smem)));
     ready = prog + kWaves;
     next_issue = ready + kRingMax;
     rest = reinterpret_cast<unsigned char*>(prog) + kCtlBytes;
   }
   __host__ __device__ static size_t bytes(int Sb, int Nf) {
     const size_t nw = (size_t)(Sb + 31) / 32;
-    const size_t used = (size_t)G::NB * G::KBUF + (size_t)G::QB * nw * 8 + nw * 8 + (size_t)max_steps(Sb) * 4 +
+    const size_t used = (size_t)G::NB * G::KBUF + (size_t)G::QB * nw * 8 + nw * 8 + (size_t)max_steps(Sb) * 8 +
                         (size_t)Nf * 8;
     return ((used + 15) & ~(size_t)15) + kCtlBytes;
   }
@@ -435,7 +466,7 @@ __device__ __forceinline__ int setup(const TokParams& p, Lds<D, BS, HF>& L, int 
     int w, sf;
     table_entry(t, p.Nt, BS, p.L0, p.gamma, p.lambda, &w, &sf);
     L.s_w[t] = w < p.Nt ? w : p.Nt;
-    L.s_sf[t] = sf;
+    L.s_ret[t] = t % sf == 0 ? 1 : 0;
   }
   for (int i = tid; i < G::QB * L.nword; i += kThreads) L.bits[i] = 0;
   __syncthreads();
@@ -485,7 +516,12 @@ __device__ __forceinline__ int setup(const TokParams& p, Lds<D, BS, HF>& L, int 
     int j = L.upre[wi];
     if (j >= j1 || j + __popc(u) <= j0) continue;
     for (; u != 0u; u &= u - 1u, ++j)
-      if (j >= j0 && j < j1) L.steps[j - j0] = wi * 32 + __ffs(u) - 1;
+      if (j >= j0 && j < j1) {
+        const int kb = wi * 32 + __ffs(u) - 1;
+        const int k0 = kb * BS, fk = k0 / p.Nt;
+        L.steps[j - j0] = kb;
+        L.sinfo[j - j0] = ((k0 - fk * p.Nt) << 8) | fk;
+      }
   }
   __syncthreads();
   return j1 - j0;
@@ -515,6 +551,7 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(TokParams p) {
   if (active_wave) load_q<D, HF>(p, b, q0, lane, qf);
   wait_vmcnt<0>();   // Q resident before the ring's loads are counted
   const int f0w = q0 / p.Nt;
+  const FrameAt qat{f0w, q0 - f0w * p.Nt};   // frame and index of the wave's first row
   Stat* mine = acc_l + wave * 2 * p.Nf;
 
   // Per-lane running statistics, four sets: query frame f0w + fo (the wave's
@@ -579,14 +616,17 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(TokParams p) {
     walk_own(L, L.bits + qb * L.nword, n, j0, [&](int j, int kb) __attribute__((always_inline)) {
       ring_wait<D, BS, HF>(p, b, L, n, pending, wave, lane, j);
       const unsigned char* kbuf = L.kbuf(j);
+      const int info = L.sinfo[j];
+      const FrameAt kat0{info & 255, info >> 8};
 #pragma unroll
       for (int ksub = 0; ksub < BS / 32; ++ksub) {
         const int ktok0 = kb * BS + 32 * ksub;
         if (ktok0 >= p.S) break;
-        const TileInfo ti = classify(p, q0, ktok0, L.s_w, L.s_sf);
+        const FrameAt kat = frame_after(kat0, 32 * ksub, p.Nt);
+        const TileInfo ti = classify(p, q0, qat, ktok0, kat, L.s_w, L.s_ret);
         if (ti.cls == kNone || ti.cls == kAllNear) continue;      // no t > 1 pair of P
         // retire the sets whose key frame the walk has passed
-        const int fk_first = ktok0 / p.Nt;
+        const int fk_first = kat.f;
 #pragma unroll
         for (int kp = 0; kp < 2; ++kp)
           if (tag_of(kp) >= 0 && tag_of(kp) < fk_first) flush(kp);
@@ -616,13 +656,13 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(TokParams p) {
           continue;
         }
         // general tile: pairs split by query frame f0 + fo and the lane's key frame
-        const TileFrames f = tile_frames(p, q0, ktok0 + (lane & 31));
+        const TileFrames f = tile_frames_at(p, qat, kat, ktok0, lane);
         set_tag(fk_first & 1, fk_first);
         if ((min(ktok0 + 31, p.S - 1)) / p.Nt != fk_first) set_tag((fk_first + 1) & 1, fk_first + 1);
         const int t0 = f.f0 > f.fk ? f.f0 - f.fk : f.fk - f.f0;
         const int t1 = f.f0 + 1 > f.fk ? f.f0 + 1 - f.fk : f.fk - f.f0 - 1;
-        const bool ok0 = f.kvalid && t0 > 1 && t0 < p.Nf && (t0 % L.s_sf[t0]) == 0;
-        const bool ok1 = f.kvalid && t1 > 1 && t1 < p.Nf && (t1 % L.s_sf[t1]) == 0;
+        const bool ok0 = f.kvalid && t0 > 1 && t0 < p.Nf && L.s_ret[t0];
+        const bool ok1 = f.kvalid && t1 > 1 && t1 < p.Nf && L.s_ret[t1];
         const int w0 = t0 < p.Nf ? L.s_w[t0] : 0, w1 = t1 < p.Nf ? L.s_w[t1] : 0;
         // per query frame f0 (suffix 0) and f0 + 1 (suffix 1); scalars, so that
         // a lane-dependent choice never indexes memory
@@ -787,6 +827,7 @@ __global__ __launch_bounds__(kThreads) void mark_kernel(TokParams p) {
   const bool active_wave = a < p.Sb && q0 < p.S;
   const int nq = a < p.Sb ? min(BS, p.S - a * BS) : 0;
   const int n_sub = (nq + 31) / 32;   // waves of this query block holding rows
+  const FrameAt qat{q0 / p.Nt, q0 - (q0 / p.Nt) * p.Nt};   // frame and index of the wave's first row
   bf16x8 qf[HF][D / 16];
   if (active_wave) load_q<D, HF>(p, b, q0, lane, qf);
   wait_vmcnt<0>();   // Q resident before the ring's loads are counted
@@ -794,8 +835,8 @@ __global__ __launch_bounds__(kThreads) void mark_kernel(TokParams p) {
   // selected count of key column lane % 32 of the tile (q0, ktok0) over the
   // wave's 32 query rows (the same value in both half-waves); marks served
   // frame pairs
-  auto tile_count = [&](const unsigned char* kbuf, int ksub, int ktok0) -> int {
-    const TileInfo ti = classify(p, q0, ktok0, L.s_w, L.s_sf);
+  auto tile_count = [&](const unsigned char* kbuf, int ksub, int ktok0, FrameAt kat) -> int {
+    const TileInfo ti = classify(p, q0, qat, ktok0, kat, L.s_w, L.s_ret);
     if (ti.cls == kNone) return 0;
     if (ti.cls == kAllNear) return 32;
     const floatx16 acc = tile_scores<D, BS, HF>(qf, kbuf, ksub, lane);
@@ -807,11 +848,11 @@ __global__ __launch_bounds__(kThreads) void mark_kernel(TokParams p) {
         if (acc[i] * p.scale >= thr) sel |= 1u << i;
       if (__ballot(sel != 0u) != 0ull && lane == 0) served_l[(ti.fq - f_lo) * p.Nf + ti.fk] = 1;
     } else {
-      const TileFrames f = tile_frames(p, q0, ktok0 + (lane & 31));
+      const TileFrames f = tile_frames_at(p, qat, kat, ktok0, lane);
       const float thr0 = f.kvalid ? thr_l[(f.f0 - f_lo) * p.Nf + f.fk] : INFINITY;
       const float thr1 = (f.kvalid && f.f0 + 1 - f_lo < p.FR) ? thr_l[(f.f0 + 1 - f_lo) * p.Nf + f.fk] : INFINITY;
       unsigned inP2;
-      select_bits(p, acc, f, q0, half, L.s_w, L.s_sf, thr0, thr1, sel, inP2);
+      select_bits(p, acc, f, q0, half, L.s_w, L.s_ret, thr0, thr1, sel, inP2);
       // frame pairs with a selected t > 1 pair are served
       const unsigned s2 = sel & inP2;
       if (s2) {
@@ -837,9 +878,11 @@ __global__ __launch_bounds__(kThreads) void mark_kernel(TokParams p) {
       ring_wait<D, BS, HF>(p, b, L, n, pending, wave, lane, j);
       const unsigned char* kbuf = L.kbuf(j);
       const int nk = min(BS, p.S - kb * BS);
+      const int info = L.sinfo[j];
+      const FrameAt kat0{info & 255, info >> 8};
       if (G::WPQ == 1) {
         // one wave holds the whole block pair: decide in registers
-        const int c = tile_count(kbuf, 0, kb * BS);
+        const int c = tile_count(kbuf, 0, kb * BS, kat0);
         const int n_act = __popcll(__ballot(lane < nk && c >= min_c[nq]));
         if (lane == 0) flags_l[qb * MS + pos_of(qb, kb) - pos_lo[qb]] = n_act >= min_a[nk] ? 1 : 0;
       } else {
@@ -848,7 +891,7 @@ __global__ __launch_bounds__(kThreads) void mark_kernel(TokParams p) {
         for (int ksub = 0; ksub < BS / 32; ++ksub) {
           const int ktok0 = kb * BS + 32 * ksub;
           if (ktok0 >= p.S) break;
-          const int c = tile_count(kbuf, ksub, ktok0);
+          const int c = tile_count(kbuf, ksub, ktok0, frame_after(kat0, 32 * ksub, p.Nt));
           if (half == 0) atomicAdd(&cnt[32 * ksub + lane], c);
         }
         // LDS operations of a wave complete in order: its counts are in
@@ -898,7 +941,7 @@ template <int D, int BS, int HF>
 __global__ __launch_bounds__(64) void fallback_kernel(TokParams p) {
   using G32 = Geo<D, 32, HF>;   // one 32-key sub-block of all fused heads at a time
   __shared__ __align__(16) unsigned char kbuf[G32::KBUF];
-  __shared__ int s_w[kMaxTokenFrames], s_sf[kMaxTokenFrames];
+  __shared__ int s_w[kMaxTokenFrames], s_ret[kMaxTokenFrames];
   __shared__ int cnt[BS];
   const int lane = threadIdx.x, half = lane >> 5;
   const int fp = blockIdx.x, b = blockIdx.y;
@@ -948,7 +991,7 @@ __global__ __launch_bounds__(64) void fallback_kernel(TokParams p) {
     int w, sf;
     table_entry(t, p.Nt, BS, p.L0, p.gamma, p.lambda, &w, &sf);
     s_w[t] = w < p.Nt ? w : p.Nt;
-    s_sf[t] = sf;
+    s_ret[t] = t % sf == 0 ? 1 : 0;
   }
   for (int c = lane; c < BS; c += 64) cnt[c] = 0;
   for (int ksub = 0; ksub < BS / 32; ++ksub) {
@@ -975,7 +1018,7 @@ __global__ __launch_bounds__(64) void fallback_kernel(TokParams p) {
       const float thr0 = f.kvalid ? p.thr[base + (size_t)f.f0 * p.Nf + f.fk] : INFINITY;
       const float thr1 = (f.kvalid && f.f0 + 1 < p.Nf) ? p.thr[base + (size_t)(f.f0 + 1) * p.Nf + f.fk] : INFINITY;
       unsigned sel, inP2;
-      select_bits(p, acc, f, q0, half, s_w, s_sf, thr0, thr1, sel, inP2);
+      select_bits(p, acc, f, q0, half, s_w, s_ret, thr0, thr1, sel, inP2);
       const int ktok = ktok0 + (lane & 31);
       for (int e = 0; e < n_extra; ++e)
         if (extra_k[e] == ktok)
