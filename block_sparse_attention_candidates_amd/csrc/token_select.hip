@@ -632,33 +632,38 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(TokParams p) {
           if (tag_of(kp) >= 0 && tag_of(kp) < fk_first) flush(kp);
         const floatx16 acc = tile_scores<D, BS, HF>(qf, kbuf, ksub, lane);
         if (ti.cls == kAllScored) {
-          // all 1024 pairs in P(fq, fk): one set, no masks
+          // all 1024 pairs in P(fq, fk): one set, no masks. Sums of the lane's
+          // 16 logits in float32, scaled into the float64 set; the scale is
+          // positive, so the tile maximum scales to the maximum score.
           set_tag(ti.fk & 1, ti.fk);
-          float v[16], m = -INFINITY;
-          double ts = 0.0, tq = 0.0;
+          const int x = 2 * (ti.fq - f0w) + (ti.fk & 1);
+          float ts = 0.f, tq = 0.f, m = -INFINITY;
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
-            v[i] = acc[i] * p.scale;
-            const double d = (double)v[i];
-            ts += d;
-            tq = fma(d, d, tq);
-            m = fmaxf(m, v[i]);
+            ts += acc[i];
+            tq = fmaf(acc[i], acc[i], tq);
+            m = fmaxf(m, acc[i]);
           }
-          // first of the lane's rows reaching m: rows ascend with i, and so
-          // does the position u * N_t + v
-          int first = 15;
+          const float ms = m * p.scale;
+          const float cur = x == 0 ? rm[0] : (x == 1 ? rm[1] : (x == 2 ? rm[2] : rm[3]));
+          unsigned int loc = 0xffffffffu;
+          if (__ballot(ms >= cur) != 0ull) {
+            // first of the lane's rows reaching m: rows ascend with i, and so
+            // does the position u * N_t + v
+            int first = 15;
 #pragma unroll
-          for (int i = 15; i >= 0; --i)
-            if (v[i] == m) first = i;
-          const unsigned int loc = (unsigned)((q0 - ti.fq * p.Nt + row_of(first, half)) * p.Nt +
-                                              (ktok0 + (lane & 31) - ti.fk * p.Nt));
-          add(2 * (ti.fq - f0w) + (ti.fk & 1), ts, tq, 16, m, loc);
+            for (int i = 15; i >= 0; --i)
+              if (acc[i] == m) first = i;
+            loc = (unsigned)((qat.u + row_of(first, half)) * p.Nt + (kat.u + (lane & 31)));
+          }
+          const double sc = (double)p.scale;
+          add(x, (double)ts * sc, (double)tq * (sc * sc), 16, ms, loc);
           continue;
         }
         // general tile: pairs split by query frame f0 + fo and the lane's key frame
         const TileFrames f = tile_frames_at(p, qat, kat, ktok0, lane);
         set_tag(fk_first & 1, fk_first);
-        if ((min(ktok0 + 31, p.S - 1)) / p.Nt != fk_first) set_tag((fk_first + 1) & 1, fk_first + 1);
+        if (kat.u + min(31, p.S - 1 - ktok0) >= p.Nt) set_tag((fk_first + 1) & 1, fk_first + 1);
         const int t0 = f.f0 > f.fk ? f.f0 - f.fk : f.fk - f.f0;
         const int t1 = f.f0 + 1 > f.fk ? f.f0 + 1 - f.fk : f.fk - f.f0 - 1;
         const bool ok0 = f.kvalid && t0 > 1 && t0 < p.Nf && L.s_ret[t0];
