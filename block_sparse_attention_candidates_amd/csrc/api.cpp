@@ -102,7 +102,7 @@ dr_status check_nnz(long long nnz, int Sb, const dr_dims* d) {
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct WsLayout {
-  size_t qbar, kbar, scores, total;
+  size_t qbar, kbar, scores, tiles, total;
   int Hp, Hm, g;
 };
 
@@ -115,7 +115,8 @@ WsLayout ws_layout(const dr_dims* d, int Sb, const dr_select_cfg* s, long long n
   w.qbar = 0;
   w.kbar = pooled;
   w.scores = 2 * pooled;
-  w.total = w.scores + align256((size_t)d->batch * w.Hm * nnz * sizeof(float));
+  w.tiles = w.scores + align256((size_t)d->batch * w.Hm * nnz * sizeof(float));
+  w.total = w.tiles + dr::tile_desc_bytes(Sb);
   return w;
 }
 
@@ -286,6 +287,9 @@ dr_status dr_score_select(const dr_dims* dims, const dr_radial_cfg* cfg, const d
   sp.g = w.g;
   sp.D = dims->head_dim;
   sp.scale = (float)(1.0 / (sqrt((double)dims->head_dim) * (double)w.g));
+  sp.tiles = dr::tile_desc_at(wsb + w.tiles, L.Sb);
+  e = dr::launch_tile_desc(sp, stream);
+  if (e != hipSuccess) return hip_fail(e, "tile kernel");
   e = dr::launch_scores(sp, dims->batch, stream);
   if (e != hipSuccess) return hip_fail(e, "score kernel");
 

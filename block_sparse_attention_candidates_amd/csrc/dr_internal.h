@@ -61,6 +61,15 @@ __host__ __device__ inline int min_count(int n, double theta) {
   return c;
 }
 
+// Workgroups go to the 8 XCDs round-robin in dispatch order, and each XCD has
+// its own L2. This maps dispatch index L of n to a work index such that every
+// XCD receives one contiguous range of the work.
+constexpr int kXcds = 8;
+__device__ inline int xcd_contiguous(int L, int n) {
+  const int x = L % kXcds, i = L / kXcds, q = n / kXcds, r = n % kXcds;
+  return x < r ? x * (q + 1) + i : r * (q + 1) + (x - r) * q + i;
+}
+
 struct CandParams {
   int Nf, Nt, Bs, S, Sb, L0;
   double gamma, lambda, theta_c, theta_m;
@@ -75,12 +84,25 @@ struct PoolParams {
   int S, Sb, Bs, D;
 };
 
+// Head-independent description of the candidate tiles of each group of 32
+// consecutive query blocks: the 32-block words (key tiles) holding a candidate
+// of any of the group's rows, and per tile and row the candidate bitmap and the
+// CSR position of the word's first candidate.
+struct TileDesc {
+  int32_t* count;   // [ngroups] active tiles
+  int32_t* word;    // [ngroups][nword] key tile of active tile j
+  uint32_t* bits;   // [ngroups][nword][32] row bitmaps of active tile j
+  int32_t* pos;     // [ngroups][nword][32] CSR position of its first candidate
+  int ngroups, nword;
+};
+
 struct ScoreParams {
   const float* qbar;
   const float* kbar;
   const int32_t* row_ptr;
   const int32_t* cols;
   float* scores;   // [B * Hm * nnz]
+  TileDesc tiles;
   long long nnz;
   int Sb, Hp, Hm, g;  // g heads summed per score (1: per-head)
   int D;
@@ -97,7 +119,8 @@ struct SelectParams {
   int Sb, H, Hm;
   int mode;
   double ratio, tau;
-  int max_row;     // LDS capacity in scores (>= longest row)
+  int max_row;     // longest row (bounds the per-wave register and LDS capacity)
+  int min_n;       // rows of at most min_n candidates are left to the per-wave kernel
 };
 
 struct AttnParams {
@@ -210,6 +233,9 @@ hipError_t launch_token_select(const TokParams& p, int B, int D, int Bs, int Hf,
 hipError_t launch_candidates(const CandParams& p, int32_t* row_ptr, int32_t* cols, long long cap,
                              hipStream_t stream);
 hipError_t launch_pool(const PoolParams& p, hipStream_t stream);
+size_t tile_desc_bytes(int Sb);
+TileDesc tile_desc_at(void* base, int Sb);
+hipError_t launch_tile_desc(const ScoreParams& p, hipStream_t stream);
 hipError_t launch_scores(const ScoreParams& p, int B, hipStream_t stream);
 hipError_t launch_select(const SelectParams& p, int B, hipStream_t stream);
 hipError_t launch_sparse_attn(const AttnParams& p, int D, int Bs, hipStream_t stream);

@@ -5,17 +5,20 @@
 //   pool:   one wavefront per (tensor, b, h, block): coalesced 16-byte bf16 loads
 //           of the block's valid rows, float32 sums, cross-lane reduction, mean.
 //           HBM-bound (reads Q and K once).
-//   scores: one workgroup per (b, h, 32 query blocks): LDS bitmaps of the 32
-//           rows' candidates locate every entry's CSR position; each 32x32
-//           tile of (query block, key block) pairs holding a candidate gets
-//           all 1024 dot products Qbar . Kbar in float32 from three bf16 MFMA
-//           products of split operands, and its candidate entries are
-//           written in place.
-//   select: one workgroup per (b, h, query block): radix select (4 passes of
-//           8 bits) over order-preserving score keys with integer histograms:
-//           counts for static-ratio, fixed-point softmax mass for
-//           dynamic-threshold; ties at the cut go to the lower key index; the
-//           kept flags are compacted in candidate (ascending) order.
+//   tiles:  one workgroup per group of 32 query blocks (head-independent): LDS
+//           bitmaps of the 32 rows' candidates give every candidate's CSR
+//           position; the active 32x32 tiles and their bitmaps are written out.
+//   scores: one workgroup per (b, h, group): each active tile gets all 1024
+//           dot products Qbar . Kbar in float32 from three bf16 MFMA products
+//           of split operands, and its candidate entries are written in place.
+//   select: one wavefront per (b, h, query block), the row's order-preserving
+//           score keys in registers: the cut key is found bit by bit from the
+//           top (32 passes of compares and ballot popcounts for static-ratio,
+//           of fixed-point softmax-mass sums for dynamic-threshold); ties at
+//           the cut go to the lower key index; the kept flags are compacted in
+//           candidate (ascending) order. Rows longer than the register
+//           capacity take a workgroup radix select (4 passes of 8 bits) with
+//           the same keys, weights and tie rule.
 #include "dr_internal.h"
 
 namespace dr {
@@ -73,14 +76,89 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolParams p) {
 }
 
 // ---------------------------------------------------------------------------
+// Candidate tiles. The candidate mask is the same for every (b, h), so the
+// map from (query block, key block) to CSR position is built once per group
+// of 32 consecutive query blocks: their candidate entries are one contiguous
+// CSR range, turned into per-row bitmaps over the key blocks in LDS plus, per
+// row and 32-block word, the CSR position of the word's first entry. A word
+// with a bit set in any row is an active 32x32 tile; its bitmaps and
+// positions are written out in tile order.
+// ---------------------------------------------------------------------------
+constexpr int kPrepThreads = 256;
+
+__global__ __launch_bounds__(kPrepThreads) void tile_desc_kernel(ScoreParams p) {
+  extern __shared__ unsigned int s_bits[];          // [32][nword] row bitmaps
+  __shared__ int s_ntiles;
+  const TileDesc& td = p.tiles;
+  const int nword = td.nword;
+  int* s_pos = reinterpret_cast<int*>(s_bits + 32 * nword);   // [32][nword]
+  int* s_tiles = s_pos + 32 * nword;                          // active words
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int grp = blockIdx.x, a0 = grp * 32;
+
+  for (int i = tid; i < 32 * nword; i += kPrepThreads) s_bits[i] = 0;
+  __syncthreads();
+  for (int m = wave; m < 32; m += kPrepThreads / 64) {
+    const int a = a0 + m;
+    if (a >= p.Sb) continue;
+    const int e1 = p.row_ptr[a + 1];
+    for (int e = p.row_ptr[a] + lane; e < e1; e += 64) {
+      const int c = p.cols[e];
+      atomicOr(&s_bits[m * nword + (c >> 5)], 1u << (c & 31));
+    }
+  }
+  __syncthreads();
+  for (int m = wave; m < 32; m += kPrepThreads / 64) {
+    const int a = a0 + m;
+    int run = a < p.Sb ? p.row_ptr[a] : 0;
+    for (int w0 = 0; w0 < nword; w0 += 64) {
+      const int w = w0 + lane;
+      const int cnt = w < nword ? __popc(s_bits[m * nword + w]) : 0;
+      int incl = cnt;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int o = __shfl_up(incl, off);
+        if (lane >= off) incl += o;
+      }
+      if (w < nword) s_pos[m * nword + w] = run + incl - cnt;
+      run += __shfl(incl, 63);
+    }
+  }
+  if (wave == 0) {
+    int n = 0;
+    for (int w0 = 0; w0 < nword; w0 += 64) {
+      const int w = w0 + lane;
+      unsigned int any = 0;
+      if (w < nword)
+        for (int m = 0; m < 32; ++m) any |= s_bits[m * nword + w];
+      const unsigned long long bal = __ballot(any != 0);
+      const int before = __builtin_amdgcn_mbcnt_hi((unsigned)(bal >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)bal, 0));
+      if (any) s_tiles[n + before] = w;
+      n += __popcll(bal);
+    }
+    if (lane == 0) {
+      s_ntiles = n;
+      td.count[grp] = n;
+    }
+  }
+  __syncthreads();
+  const int ntiles = s_ntiles;
+  const size_t base = (size_t)grp * nword;
+  for (int j = tid; j < ntiles; j += kPrepThreads) td.word[base + j] = s_tiles[j];
+  for (int i = tid; i < ntiles * 32; i += kPrepThreads) {
+    const int j = i >> 5, m = i & 31, t = s_tiles[j];
+    td.bits[(base + j) * 32 + m] = s_bits[m * nword + t];
+    td.pos[(base + j) * 32 + m] = s_pos[m * nword + t];
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Candidate scores: float32 dot products from the bf16 MFMA in three parts.
-// A workgroup (4 wavefronts) owns 32 consecutive query blocks (rows) of one
-// (b, h). Their candidate entries are one contiguous CSR range; the workgroup
-// turns it into per-row bitmaps over the key blocks in LDS plus, per row and
-// 32-block word, the CSR position of the word's first entry. A word with any
-// bit set in any row is an active 32x32 tile; the waves share the active
-// tiles, compute all 1024 dot products of a tile and write the candidate
-// entries straight to their CSR positions.
+// A workgroup (4 wavefronts) owns one group of 32 query blocks of one (b, h);
+// the waves share the group's active tiles, compute all 1024 dot products of
+// a tile and write its candidate entries straight to their CSR positions (a
+// popcount into the row's bitmap). The pooled K rows of a wave's next tile
+// are loaded while the current one is on the matrix cores.
 // Each float32 operand is split as x = hi + lo (bf16 each, exact up to
 // 2^-17 |x|) and q.k is accumulated in float32 as ql.kh + qh.kl + qh.kh with
 // v_mfma_f32_32x32x16_bf16 (the dropped ql.kl and the split remainders are
@@ -109,61 +187,21 @@ __device__ inline floatx8 load8(const float* src) {
 template <int D>
 __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreParams p) {
   constexpr int KS = D / 16;   // 16-dim steps of v_mfma_f32_32x32x16_bf16
-  extern __shared__ unsigned int s_bits[];          // [32][nword] row bitmaps
-  __shared__ int s_ntiles;
-  const int nword = (p.Sb + 31) >> 5;
-  int* s_pos = reinterpret_cast<int*>(s_bits + 32 * nword);   // [32][nword] CSR position of each word
-  int* s_tiles = s_pos + 32 * nword;                          // active words
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int a0 = blockIdx.x * 32;
-  const int bm = blockIdx.y;              // b * Hm + hm
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const TileDesc& td = p.tiles;
+  // (b, h) major: an XCD works through whole heads, whose pooled Q and K
+  // (2 * S_b * D * 4 bytes) then stay in its L2
+  const int w = xcd_contiguous(blockIdx.x, gridDim.x);
+  const int bm = w / td.ngroups;          // b * Hm + hm
+  const int grp = w - bm * td.ngroups, a0 = grp * 32;
   const int b = bm / p.Hm, hm = bm - b * p.Hm;
   const long long out_base = (long long)bm * p.nnz;
-
-  for (int i = tid; i < 32 * nword; i += kScoreThreads) s_bits[i] = 0;
+  const int ntiles = td.count[grp];
+  const size_t dbase = (size_t)grp * td.nword;
+  __shared__ int s_word[kMaxBlocks / 32];   // key tile of each active tile
+  for (int i = threadIdx.x; i < ntiles; i += kScoreThreads) s_word[i] = td.word[dbase + i];
   __syncthreads();
-  for (int m = wave; m < 32; m += 4) {
-    const int a = a0 + m;
-    if (a >= p.Sb) continue;
-    const int e1 = p.row_ptr[a + 1];
-    for (int e = p.row_ptr[a] + lane; e < e1; e += 64) {
-      const int c = p.cols[e];
-      atomicOr(&s_bits[m * nword + (c >> 5)], 1u << (c & 31));
-    }
-  }
-  __syncthreads();
-  for (int m = wave; m < 32; m += 4) {
-    const int a = a0 + m;
-    int run = a < p.Sb ? p.row_ptr[a] : 0;
-    for (int w0 = 0; w0 < nword; w0 += 64) {
-      const int w = w0 + lane;
-      const int cnt = w < nword ? __popc(s_bits[m * nword + w]) : 0;
-      int incl = cnt;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const int o = __shfl_up(incl, off);
-        if (lane >= off) incl += o;
-      }
-      if (w < nword) s_pos[m * nword + w] = run + incl - cnt;
-      run += __shfl(incl, 63);
-    }
-  }
-  if (wave == 0) {
-    int n = 0;
-    for (int w0 = 0; w0 < nword; w0 += 64) {
-      const int w = w0 + lane;
-      unsigned int any = 0;
-      if (w < nword)
-        for (int m = 0; m < 32; ++m) any |= s_bits[m * nword + w];
-      const unsigned long long bal = __ballot(any != 0);
-      const int before = __builtin_amdgcn_mbcnt_hi((unsigned)(bal >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)bal, 0));
-      if (any) s_tiles[n + before] = w;
-      n += __popcll(bal);
-    }
-    if (lane == 0) s_ntiles = n;
-  }
-  __syncthreads();
-  const int ntiles = s_ntiles;
 
   const int m32 = lane & 31, half = lane >> 5;
   const int row = a0 + m32;
@@ -182,35 +220,100 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreParams p) {
       split(v, qh[kk], ql[kk]);
     }
   };
-  if (p.g == 1) load_q(0);
-  for (int j = wave; j < ntiles; j += 4) {
-    const int t = s_tiles[j];
-    const int kc = t * 32 + m32;
-    const bool kc_ok = kc < p.Sb;
-    floatx16 acc = {};
-    for (int hh = 0; hh < p.g; ++hh) {
-      if (p.g != 1) load_q(hh);
-      const float* ksrc = p.kbar + (pooled(hh) + (kc_ok ? kc : 0)) * D + 8 * half;
-      floatx8 kv[KS];
+  // K rows past S_b read the last row (every lane loads, so the loads are
+  // unconditional and counted exactly) and are zeroed at use
+  auto load_k = [&](floatx8* kv, int t, int hh) {
+    const int kc = min(t * 32 + m32, p.Sb - 1);
+    const float* ksrc = p.kbar + (pooled(hh) + kc) * D + 8 * half;
 #pragma unroll
-      for (int kk = 0; kk < KS; ++kk) kv[kk] = kc_ok ? load8(ksrc + 16 * kk) : floatx8{0, 0, 0, 0, 0, 0, 0, 0};
+    for (int kk = 0; kk < KS; ++kk) kv[kk] = load8(ksrc + 16 * kk);
+  };
+  auto mma = [&](floatx16& acc, const floatx8* kv, int t) {
+    const bool kc_ok = t * 32 + m32 < p.Sb;
 #pragma unroll
-      for (int kk = 0; kk < KS; ++kk) {
-        bf16x8 kh, kl;
-        split(kv[kk], kh, kl);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ql[kk], kh, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qh[kk], kl, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qh[kk], kh, acc, 0, 0, 0);
-      }
+    for (int kk = 0; kk < KS; ++kk) {
+      bf16x8 kh, kl;
+      split(kc_ok ? kv[kk] : floatx8{0, 0, 0, 0, 0, 0, 0, 0}, kh, kl);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ql[kk], kh, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qh[kk], kl, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qh[kk], kh, acc, 0, 0, 0);
     }
-    // element i of this lane is (row 8*(i/4) + 4*half + i%4, key block t*32 + m32)
+  };
+  // element i of this lane is (row 8*(i/4) + 4*half + i%4, key block t*32 + m32):
+  // the lane's 16 rows are 4 runs of 4 consecutive rows, whose bitmaps and
+  // positions it loads as 16-byte vectors together with the tile's K rows
+  typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+  typedef int i32x4_t __attribute__((ext_vector_type(4)));
+  auto load_desc = [&](u32x4_t* bw, i32x4_t* ps, int j) {
+    const u32x4_t* b4 = reinterpret_cast<const u32x4_t*>(td.bits + (dbase + j) * 32 + 4 * half);
+    const i32x4_t* p4 = reinterpret_cast<const i32x4_t*>(td.pos + (dbase + j) * 32 + 4 * half);
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      bw[x] = b4[2 * x];
+      ps[x] = p4[2 * x];
+    }
+  };
+  auto store = [&](const floatx16& acc, const u32x4_t* bw, const i32x4_t* ps) {
     const unsigned int below = (1u << m32) - 1u;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const int m = 8 * (i >> 2) + 4 * half + (i & 3);
-      const unsigned int bits = s_bits[m * nword + t];
-      if ((bits >> m32) & 1u)
-        p.scores[out_base + s_pos[m * nword + t] + __popc(bits & below)] = acc[i] * p.scale;
+      const unsigned int bits = bw[i >> 2][i & 3];
+      if ((bits >> m32) & 1u) p.scores[out_base + ps[i >> 2][i & 3] + __popc(bits & below)] = acc[i] * p.scale;
+    }
+  };
+
+  u32x4_t bw[4];
+  i32x4_t ps[4];
+  if (p.g == 1) {
+    // per tile: its bitmaps and positions are requested first, then the
+    // products, then the next tile's K rows, so the stores wait only for the
+    // former (loads complete in issue order)
+    // The next tile's K rows are requested step by step as the current
+    // tile's are split for the matrix cores, so they are in flight during
+    // its products and stores; the last tile's rows are loaded once more
+    // rather than branched around, so every iteration issues the same loads.
+    load_q(0);
+    floatx8 kv[KS];
+    int j = wave;
+    if (j < ntiles) {
+      int t = s_word[j];
+      load_k(kv, t, 0);
+      while (true) {
+        load_desc(bw, ps, j);
+        __builtin_amdgcn_sched_barrier(0);
+        const int jn = j + kScoreThreads / 64;
+        const int tn = s_word[min(jn, ntiles - 1)];
+        const float* knext = p.kbar + (pooled(0) + min(tn * 32 + m32, p.Sb - 1)) * D + 8 * half;
+        const bool kc_ok = t * 32 + m32 < p.Sb;
+        floatx16 acc = {};
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) {
+          bf16x8 kh, kl;
+          split(kc_ok ? kv[kk] : floatx8{0, 0, 0, 0, 0, 0, 0, 0}, kh, kl);
+          kv[kk] = load8(knext + 16 * kk);
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ql[kk], kh, acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qh[kk], kl, acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qh[kk], kh, acc, 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        store(acc, bw, ps);
+        if (jn >= ntiles) break;
+        j = jn;
+        t = tn;
+      }
+    }
+  } else {
+    for (int j = wave; j < ntiles; j += kScoreThreads / 64) {
+      const int t = s_word[j];
+      load_desc(bw, ps, j);
+      floatx16 acc = {};
+      for (int hh = 0; hh < p.g; ++hh) {
+        load_q(hh);
+        floatx8 kv[KS];
+        load_k(kv, t, hh);
+        mma(acc, kv, t);
+      }
+      store(acc, bw, ps);
     }
   }
 }
@@ -246,6 +349,10 @@ __device__ inline int static_keep(int n, double ratio) {
   return k;
 }
 
+// Histogram weight: counts (static-ratio) or fixed-point mass (dynamic).
+template <bool DYN> struct Weight { typedef unsigned int type; };
+template <> struct Weight<true> { typedef unsigned long long type; };
+
 __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectParams p) {
   extern __shared__ float s_sc[];
   __shared__ unsigned long long s_hist[256];
@@ -258,6 +365,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectParams p) {
   const int bm = blockIdx.y;             // b * Hm + hm
   const int r0 = p.row_ptr[a];
   const int n = p.row_ptr[a + 1] - r0;
+  if (n <= p.min_n) return;
   const float* sc = p.scores + (long long)bm * p.nnz + r0;
   for (int i = tid; i < n; i += kSelThreads) s_sc[i] = sc[i];
   __syncthreads();
@@ -393,6 +501,168 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectParams p) {
     for (int h = h_lo; h < h_hi; ++h) p.kept_cnt[(long long)(b * H + h) * p.Sb + a] = kept_base;
 }
 
+
+// One wavefront per row of at most 64 * NR candidates; candidate i of the
+// row sits in slot i / 64 of lane i % 64 (slots are visited in runs of 8, and
+// a run past the row's end is skipped). The radix select is that of the
+// workgroup kernel (same keys, weights, digit order and tie rule, so the same
+// cut), on a histogram of the wave's own in LDS: no workgroup barrier. LDS
+// operations of one wavefront complete in issue order, so a lane reads the
+// bins after every lane's additions have landed.
+template <int NR, bool DYN>
+__global__ __launch_bounds__(256) void select_wave_kernel(SelectParams p) {
+  typedef typename Weight<DYN>::type W;
+  static_assert(NR % 8 == 0, "slots come in runs of 8");
+  __shared__ W s_hist[4][256];
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int a = blockIdx.x * 4 + wv;
+  if (a >= p.Sb) return;
+  const int bm = blockIdx.y;             // b * Hm + hm
+  const int r0 = p.row_ptr[a];
+  const int n = p.row_ptr[a + 1] - r0;
+  if (n > 64 * NR) return;               // left to the workgroup kernel
+  const int ns = (n + 63) >> 6;          // slots in use
+  const float* sc = p.scores + (long long)bm * p.nnz + r0;
+  W* hist = s_hist[wv];
+
+  const bool keep_all = n == 0 || (DYN ? p.tau >= 1.0 : static_keep(n, p.ratio) >= n);
+  unsigned int key[NR];
+  W wt[DYN ? NR : 1];
+  unsigned int T = 0;
+  unsigned long long tie_keep = 0;
+  if (!keep_all) {
+    unsigned int kmax = 0;
+#pragma unroll
+    for (int j = 0; j < NR; ++j) key[j] = 0;
+#pragma unroll
+    for (int r = 0; r < NR / 8; ++r) {
+      if (8 * r >= ns) break;
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        const int j = 8 * r + jj, i = j * 64 + lane;
+        if (i < n) key[j] = order_key(sc[i]);
+        kmax = max(kmax, key[j]);
+      }
+    }
+    unsigned long long need;
+    float smax = 0.0f;
+    if (DYN) {
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) kmax = max(kmax, (unsigned int)__shfl_xor((int)kmax, off));
+      smax = key_to_float(kmax);
+      unsigned long long z = 0;
+#pragma unroll
+      for (int j = 0; j < NR; ++j) wt[DYN ? j : 0] = 0;
+#pragma unroll
+      for (int r = 0; r < NR / 8; ++r) {
+        if (8 * r >= ns) break;
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+          const int j = 8 * r + jj;
+          if (j * 64 + lane < n) wt[DYN ? j : 0] = mass_weight(key_to_float(key[j]), smax);
+          z += wt[DYN ? j : 0];
+        }
+      }
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) z += __shfl_xor(z, off);
+      need = (unsigned long long)ceil(p.tau * (double)z);
+    } else {
+      need = (unsigned long long)static_keep(n, p.ratio);
+    }
+#pragma unroll
+    for (int x = 0; x < 4; ++x) hist[lane + 64 * x] = 0;
+    // most significant digit first: T is the key at which the weight of keys
+    // > T is < need and of keys >= T is >= need
+    unsigned int prefix = 0, pmask = 0;
+    unsigned long long rem = need;
+    for (int shift = 24; shift >= 0; shift -= 8) {
+#pragma unroll
+      for (int r = 0; r < NR / 8; ++r) {
+        if (8 * r >= ns) break;
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+          const int j = 8 * r + jj;
+          if (j * 64 + lane < n && (key[j] & pmask) == prefix)
+            atomicAdd(&hist[(key[j] >> shift) & 255u], DYN ? wt[DYN ? j : 0] : (W)1);
+        }
+      }
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      // lane l holds bins 255-4l .. 252-4l (descending), and clears them
+      W v[4];
+#pragma unroll
+      for (int x = 0; x < 4; ++x) v[x] = hist[255 - 4 * lane - x];
+#pragma unroll
+      for (int x = 0; x < 4; ++x) hist[255 - 4 * lane - x] = 0;
+      const unsigned long long mine = (unsigned long long)v[0] + v[1] + v[2] + v[3];
+      unsigned long long incl = mine;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const unsigned long long o = __shfl_up(incl, off);
+        if (lane >= off) incl += o;
+      }
+      const unsigned long long excl = incl - mine;
+      // exactly one lane holds the bin at which the running weight reaches rem
+      const bool here = excl < rem && incl >= rem;
+      unsigned long long c = excl;
+      int dg = 255 - 4 * lane;
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        if (c + v[x] >= rem) { dg = 255 - 4 * lane - x; break; }
+        c += v[x];
+      }
+      const int src = __builtin_ctzll(__ballot(here));
+      const unsigned int d = (unsigned int)__shfl(dg, src);
+      rem -= __shfl(c, src);
+      prefix |= d << shift;
+      pmask |= 255u << shift;
+    }
+    T = prefix;
+    // ties at T: keep the lowest-index ones until the remaining need is met
+    if (DYN) {
+      const unsigned long long wT = mass_weight(key_to_float(T), smax);
+      tie_keep = (rem + wT - 1) / wT;
+    } else {
+      tie_keep = rem;
+    }
+  }
+
+  // ordered compaction of the kept flags (candidate order is ascending)
+  const int H = p.H;
+  const int b = bm / p.Hm, hm = bm - b * p.Hm;
+  const int h_lo = p.Hm == 1 ? 0 : hm, h_hi = p.Hm == 1 ? H : hm + 1;
+  int kept = 0;
+  unsigned long long tie_base = 0;
+#pragma unroll
+  for (int r = 0; r < NR / 8; ++r) {
+    if (8 * r >= ns) break;
+    int col[8];
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+      const int i = (8 * r + jj) * 64 + lane;
+      col[jj] = i < n ? p.cols[r0 + i] : 0;
+    }
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+      const int j = 8 * r + jj, i = j * 64 + lane;
+      const bool valid = i < n;
+      bool keep = valid && (keep_all || key[j] > T);
+      const bool tie = valid && !keep_all && key[j] == T;
+      const unsigned long long mt = __ballot(tie);
+      const int tie_before = __builtin_amdgcn_mbcnt_hi((unsigned)(mt >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)mt, 0));
+      if (tie && tie_base + tie_before < tie_keep) keep = true;
+      tie_base += __popcll(mt);
+      const unsigned long long mk = __ballot(keep);
+      const int k_before = __builtin_amdgcn_mbcnt_hi((unsigned)(mk >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)mk, 0));
+      if (keep)
+        for (int h = h_lo; h < h_hi; ++h) p.kept_col[(long long)(b * H + h) * p.nnz + r0 + kept + k_before] = col[jj];
+      kept += __popcll(mk);
+    }
+  }
+  if (lane == 0)
+    for (int h = h_lo; h < h_hi; ++h) p.kept_cnt[(long long)(b * H + h) * p.Sb + a] = kept;
+}
 }  // namespace
 
 hipError_t launch_pool(const PoolParams& p, hipStream_t stream) {
@@ -405,18 +675,58 @@ hipError_t launch_pool(const PoolParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_scores(const ScoreParams& p, int B, hipStream_t stream) {
-  const dim3 grid((unsigned)((p.Sb + 31) / 32), (unsigned)(B * p.Hm));
-  const int nword = (p.Sb + 31) / 32;
+size_t tile_desc_bytes(int Sb) {
+  const size_t ng = (size_t)(Sb + 31) / 32, nword = ng;
+  auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  return al(ng * 4) + al(ng * nword * 4) + 2 * al(ng * nword * 32 * 4);
+}
+
+TileDesc tile_desc_at(void* base, int Sb) {
+  const size_t ng = (size_t)(Sb + 31) / 32, nword = ng;
+  auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  unsigned char* c = static_cast<unsigned char*>(base);
+  TileDesc t;
+  t.count = reinterpret_cast<int32_t*>(c);
+  c += al(ng * 4);
+  t.word = reinterpret_cast<int32_t*>(c);
+  c += al(ng * nword * 4);
+  t.bits = reinterpret_cast<uint32_t*>(c);
+  c += al(ng * nword * 32 * 4);
+  t.pos = reinterpret_cast<int32_t*>(c);
+  t.ngroups = (int)ng;
+  t.nword = (int)nword;
+  return t;
+}
+
+hipError_t launch_tile_desc(const ScoreParams& p, hipStream_t stream) {
+  const int nword = p.tiles.nword;
   const size_t lds = (size_t)nword * (32 * 4 + 32 * 4 + 4);
-  if (p.D == 128)
-    hipLaunchKernelGGL(score_kernel<128>, grid, dim3(kScoreThreads), lds, stream, p);
-  else
-    hipLaunchKernelGGL(score_kernel<64>, grid, dim3(kScoreThreads), lds, stream, p);
+  hipLaunchKernelGGL(tile_desc_kernel, dim3((unsigned)p.tiles.ngroups), dim3(kPrepThreads), lds, stream, p);
   return hipGetLastError();
 }
 
-hipError_t launch_select(const SelectParams& p, int B, hipStream_t stream) {
+hipError_t launch_scores(const ScoreParams& p, int B, hipStream_t stream) {
+  const dim3 grid((unsigned)(p.tiles.ngroups * B * p.Hm));
+  if (p.D == 128)
+    hipLaunchKernelGGL(score_kernel<128>, grid, dim3(kScoreThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL(score_kernel<64>, grid, dim3(kScoreThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+// Register capacity of the per-wave selection: 64 * kSelSlots candidates.
+constexpr int kSelSlots = 40;
+
+hipError_t launch_select(const SelectParams& p0, int B, hipStream_t stream) {
+  SelectParams p = p0;
+  p.min_n = 64 * kSelSlots;
+  const dim3 wgrid((unsigned)((p.Sb + 3) / 4), (unsigned)(B * p.Hm));
+  if (p.mode == 1)
+    hipLaunchKernelGGL((select_wave_kernel<kSelSlots, true>), wgrid, dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL((select_wave_kernel<kSelSlots, false>), wgrid, dim3(256), 0, stream, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.max_row <= p.min_n) return e;
   const dim3 grid((unsigned)p.Sb, (unsigned)(B * p.Hm));
   hipLaunchKernelGGL(select_kernel, grid, dim3(kSelThreads), (size_t)p.max_row * sizeof(float), stream, p);
   return hipGetLastError();

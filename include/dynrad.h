@@ -122,8 +122,9 @@ dr_status dr_build_candidates(const dr_radial_cfg* cfg, int32_t* row_ptr, int32_
                               int64_t cap, int64_t* nnz, hipStream_t stream);
 
 /* Device workspace (bytes) dr_score_select needs: pooled Q and K means (float32,
- * [B, Hs, S_b, D] each, Hs = H or score_heads) plus the score buffer (float32,
- * [B * Hm * nnz], Hm = H or 1). Host only. */
+ * [B, Hs, S_b, D] each, Hs = H or score_heads), the score buffer (float32,
+ * [B * Hm * nnz], Hm = H or 1) and a head-independent map of the candidate
+ * tiles (about 260 * ceil(S_b / 32)^2 bytes). Host only. */
 dr_status dr_score_select_workspace(const dr_dims* dims, const dr_radial_cfg* cfg,
                                     const dr_select_cfg* sel, int64_t nnz, size_t* bytes);
 

@@ -100,12 +100,13 @@ def test_select_and_attention_validation(dynrad_lib):
     size = ctypes.c_size_t(0)
     assert dynrad_lib.dr_score_select_workspace(ctypes.byref(dims), ctypes.byref(cfg), ctypes.byref(sel), 64,
                                                 ctypes.byref(size)) == L.DR_OK
-    # pooled Q and K: 2 * (1*2*8*64*4 = 4096 B) + scores 1*2*64*4 = 512 B (each rounded up to 256 B)
-    assert size.value == 4096 + 4096 + 512
+    # pooled Q and K: 2 * (1*2*8*64*4 = 4096 B) + scores 1*2*64*4 = 512 B + the tile map of one group of
+    # 32 query blocks (count, tile words, bitmaps, positions: 4 parts), each rounded up to 256 B
+    assert size.value == 4096 + 4096 + 512 + 4 * 256
     fused = L.SelectCfg(L.DR_DYNAMIC_THRESHOLD, 1, 0.5, 0.8)
     assert dynrad_lib.dr_score_select_workspace(ctypes.byref(dims), ctypes.byref(cfg), ctypes.byref(fused), 64,
                                                 ctypes.byref(size)) == L.DR_OK
-    assert size.value == 2048 + 2048 + 256
+    assert size.value == 2048 + 2048 + 256 + 4 * 256
 
     def ss(d=dims, s=sel, nnz=64, ws_bytes=1 << 20, q=FAKE):
         return dynrad_lib.dr_score_select(ctypes.byref(d), ctypes.byref(cfg), ctypes.byref(s), q, FAKE, FAKE, FAKE,

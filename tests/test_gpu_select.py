@@ -24,6 +24,18 @@ CASES = [
 ]
 
 
+def _static_exact_on_gpu_scores(gpu_lists, gpu_scores, row_ptr, cols, ratio):
+    """The static cut is pure order statistics: on the kernel's own float32
+    scores the oracle's selection (score descending, ties to the lower key
+    index, k = max(1, ceil(r n))) must give the same kept lists, bit for bit,
+    on every row."""
+    s = gpu_scores.astype(np.float64)
+    for a, g in enumerate(gpu_lists):
+        lo, hi = row_ptr[a], row_ptr[a + 1]
+        o = O.select_static(s[lo:hi], cols[lo:hi], ratio)
+        assert np.array_equal(g, o), f"row {a}: gpu {g[:8]}.. != selection on its own scores {o[:8]}.."
+
+
 @pytest.mark.parametrize("name,mode,ratio,tau", CASES)
 def test_score_select_parity(name, mode, ratio, tau):
     G.log(f"[select] {name} {mode} r={ratio} tau={tau}")
@@ -42,6 +54,8 @@ def test_score_select_parity(name, mode, ratio, tau):
         d, nd = G.check_selection(gl, ora, margins, s, rp, cols, mode, ratio, tau)
         tot_dec += d
         tot_nondec += nd
+        if mode == "static":
+            _static_exact_on_gpu_scores(gl, scores[h], rp, cols, ratio)
     G.log(f"   decisive rows {tot_dec}, within-margin rows {tot_nondec}")
     assert tot_dec > 0.5 * (tot_dec + tot_nondec)
 
@@ -118,3 +132,35 @@ def test_score_select_block_size_128(mode, ratio, tau):
         np.testing.assert_allclose(scores[h], s, rtol=1e-5, atol=G.SCORE_ATOL, err_msg=f"head {h} scores")
         gl = G.kept_lists(kept, rp, cand.nnz, cand.num_blocks, h)
         G.check_selection(gl, ora, margins, s, rp, cols, mode, ratio, tau)
+
+
+@pytest.mark.parametrize("mode,ratio,tau", [("static", 0.2, 1.0), ("dynamic", 1.0, 0.8)])
+def test_score_select_long_rows(mode, ratio, tau):
+    """4 frames of 24,000 tokens, B_s = 32 (S_b = 3000), gamma = 1: rows of
+    about 2000 to 2760 candidates, so one call selects short rows in a
+    wavefront's registers (up to 2560 candidates) and long rows with the
+    workgroup radix select. D = 64, one head, random bf16 Q/K; every row
+    against the oracle, and (static) bit-exact against the oracle's selection
+    on the kernel's own scores."""
+    import torch
+    G.log(f"[select] long rows {mode}")
+    rng = np.random.default_rng(2560)
+    S, D, Bs = 96000, 64, 32
+    bits = workloads.bf16_bits(rng.standard_normal((2, 1, 1, S, D)).astype(np.float32))
+    q, k = (torch.from_numpy(np.ascontiguousarray(bits[i])).view(torch.bfloat16).cuda() for i in range(2))
+    f64 = (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    cand = G.dr().build_candidates(G.dr().radial_cfg(4, 24000, Bs, 1.0, 4.0))
+    rp, cols = G.host_csr(cand)
+    n = np.diff(rp)
+    assert (n <= 2560).any() and (n > 2560).any(), (n.min(), n.max())
+    kept = G.dr().score_select(q, k, cand, mode=mode, ratio=ratio, tau=tau, return_scores=True)
+    gs = kept.scores.cpu().numpy()
+    s = O.block_scores(O.pool_blocks(f64[0, 0, 0], Bs), O.pool_blocks(f64[1, 0, 0], Bs), rp, cols)
+    np.testing.assert_allclose(gs, s, rtol=1e-5, atol=G.SCORE_ATOL)
+    ora, margins = O.select_all(s, rp, cols, mode, ratio=ratio, tau=tau)
+    gl = G.kept_lists(kept, rp, cand.nnz, cand.num_blocks, 0)
+    dec, nondec = G.check_selection(gl, ora, margins, s, rp, cols, mode, ratio, tau)
+    G.log(f"   rows of {n.min()}..{n.max()} candidates ({(n > 2560).sum()} above 2560): decisive {dec}, "
+          f"within-margin {nondec}")
+    if mode == "static":
+        _static_exact_on_gpu_scores(gl, gs, rp, cols, ratio)
