@@ -5,7 +5,8 @@
 
 One step = one pass of the whole hot path over one batch of synthetic input
 already resident in HBM: candidate build (asynchronous form), block mean
-pooling + scoring + selection, and block-sparse flash attention. The dense
+pooling + scoring + selection, the choice of query-block grouping, and
+block-sparse flash attention. The dense
 kernel is timed separately as the speedup denominator. Prints one JSON line.
 
 --mode decay-static: the paper's content-free static-ratio selector (Eq. 8);
@@ -52,6 +53,8 @@ def parse():
     ap.add_argument("--dense-iters", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--no-groups", action="store_true",
+                    help="consecutive query blocks per attention workgroup (skip dr_query_groups)")
     ap.add_argument("--cpu-blocks", type=int, default=960, help="query blocks in the CPU oracle sample")
     ap.add_argument("--calib-copy", action="store_true",
                     help="after timing, run one plain 1 GiB device copy (the reference for HBM byte counters)")
@@ -245,11 +248,10 @@ def main():
     row_ptr = torch.empty_like(cand.row_ptr)
     cols = torch.empty_like(cand.cols)
     kept_col, kept_cnt = torch.empty_like(kept.kept_col), torch.empty_like(kept.kept_cnt)
-    if args.mode == "decay-static":
-        row_ptr.copy_(cand.row_ptr)
-        cols.copy_(cand.cols)
-        kept_col.copy_(kept.kept_col)
-        kept_cnt.copy_(kept.kept_cnt)
+    gwsb = ctypes.c_size_t(0)
+    _lib.check(L.dr_query_groups_workspace(ctypes.byref(dims), ctypes.byref(gwsb)))
+    gws = torch.empty(gwsb.value, dtype=torch.uint8, device="cuda")
+    gmodes = torch.zeros(w.batch * w.heads, dtype=torch.int32, device="cuda")
     scale = 1.0 / math.sqrt(w.head_dim)
 
     def stream():
@@ -271,10 +273,31 @@ def main():
                                      kept_col.data_ptr(), kept_cnt.data_ptr(), None, ws.data_ptr(), ws.numel(),
                                      stream()))
 
+    def step_groups():
+        if args.no_groups:
+            return
+        _lib.check(L.dr_query_groups(ctypes.byref(dims), ctypes.byref(cfg), row_ptr.data_ptr(), cand.nnz,
+                                     kept_col.data_ptr(), kept_cnt.data_ptr(), gmodes.data_ptr(), gws.data_ptr(),
+                                     gws.numel(), stream()))
+
     def step_attn():
-        _lib.check(L.dr_sparse_attn(ctypes.byref(dims), ctypes.byref(cfg), q.data_ptr(), k.data_ptr(), v.data_ptr(),
-                                    row_ptr.data_ptr(), cand.nnz, kept_col.data_ptr(), kept_cnt.data_ptr(),
-                                    ctypes.c_float(scale), out.data_ptr(), stream()))
+        if args.no_groups:
+            _lib.check(L.dr_sparse_attn(ctypes.byref(dims), ctypes.byref(cfg), q.data_ptr(), k.data_ptr(),
+                                        v.data_ptr(), row_ptr.data_ptr(), cand.nnz, kept_col.data_ptr(),
+                                        kept_cnt.data_ptr(), ctypes.c_float(scale), out.data_ptr(), stream()))
+            return
+        _lib.check(L.dr_sparse_attn_grouped(ctypes.byref(dims), ctypes.byref(cfg), q.data_ptr(), k.data_ptr(),
+                                            v.data_ptr(), row_ptr.data_ptr(), cand.nnz, kept_col.data_ptr(),
+                                            kept_cnt.data_ptr(), gmodes.data_ptr(), ctypes.c_float(scale),
+                                            out.data_ptr(), stream()))
+
+    if args.mode == "decay-static":
+        # the cached mask and its grouping
+        row_ptr.copy_(cand.row_ptr)
+        cols.copy_(cand.cols)
+        kept_col.copy_(kept.kept_col)
+        kept_cnt.copy_(kept.kept_cnt)
+        step_groups()
 
     def step():
         if args.mode == "decay-static":   # the mask is cached: attention only
@@ -282,6 +305,7 @@ def main():
             return
         step_candidates()
         step_select()
+        step_groups()
         step_attn()
 
     for _ in range(args.warmup):
@@ -296,7 +320,9 @@ def main():
     # per-stage HIP-event timing on the launch stream
     ms_cand = event_ms(step_candidates, args.stage_iters, torch) if ms_mask is None else None
     ms_sel = event_ms(step_select, args.stage_iters, torch) if ms_mask is None else None
+    ms_groups = event_ms(step_groups, args.stage_iters, torch) if not args.no_groups else None
     ms_attn = event_ms(step_attn, args.stage_iters, torch)
+    modes_used = np.bincount(gmodes.cpu().numpy(), minlength=3).tolist() if not args.no_groups else None
     kept_total = int(kept_cnt.sum().item())
     Sb = cand.num_blocks
     flops = 4.0 * w.block_size ** 2 * w.head_dim * kept_total
@@ -330,7 +356,9 @@ def main():
         "stage_ms": ({"mask_build": round(ms_mask, 4)} if ms_mask is not None else
                      {"build_candidates": round(ms_cand, 4),
                       ("token_select" if args.mode == "token" else "score_select"): round(ms_sel, 4)}) |
+                    ({"query_groups": round(ms_groups, 4)} if ms_groups is not None else {}) |
                     {"sparse_attn": round(ms_attn, 4), "dense_attn": round(ms_dense, 3) if ms_dense else None},
+        "query_grouping": ({"heads_per_mode": modes_used} if modes_used is not None else "consecutive"),
         "dense_tflops": round(dense_flops / (ms_dense * 1e-3) / 1e12, 2) if ms_dense else None,
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4),

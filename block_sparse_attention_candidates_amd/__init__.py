@@ -27,8 +27,8 @@ from . import _lib as _L
 from ._lib import Dims, DynradError, RadialCfg, SelectCfg, check, lib
 
 __all__ = ["radial_cfg", "num_blocks", "distance_table", "Candidates", "Kept", "build_candidates",
-           "score_select", "token_select", "static_select", "sparse_attn", "attn", "proxy_error", "proxy_loss",
-           "DynradError", "kept_from_lists"]
+           "score_select", "token_select", "static_select", "query_groups", "group_table", "sparse_attn", "attn",
+           "proxy_error", "proxy_loss", "DynradError", "kept_from_lists"]
 
 
 def radial_cfg(num_frames: int, tokens_per_frame: int, block_size: int, gamma: float, lam: float,
@@ -189,16 +189,62 @@ def static_select(cand: Candidates, rho_near: float, rho_far: float, seed: int, 
     return Kept(kept_col, kept_cnt)
 
 
-def sparse_attn(q, k, v, cand: Candidates, kept: Kept, softmax_scale: Optional[float] = None, out=None):
+def group_table(cand: Candidates, mode: int) -> np.ndarray:
+    """Query blocks of every group of grouping mode `mode` (host; -1 = empty
+    slot), shape [groups, 256 / B_s]."""
+    n = lib().dr_query_group_table(ctypes.byref(cand.cfg), int(mode), None, 0)
+    if n < 0:
+        check(int(-n))
+    t = np.empty(n, dtype=np.int32)
+    m = lib().dr_query_group_table(ctypes.byref(cand.cfg), int(mode), t.ctypes.data_as(ctypes.c_void_p), n)
+    if m < 0:
+        check(int(-m))
+    return t.reshape(-1, 256 // cand.cfg.block_size)
+
+
+def query_groups(q, cand: Candidates, kept: Kept, workspace=None):
+    """Per (b, h), the query-block grouping mode with the smallest total size of
+    the groups' kept-list unions: torch.int32 [B * H] on q's device."""
+    torch = _torch()
+    dims = _dims(tuple(q.shape))
+    need = ctypes.c_size_t(0)
+    check(lib().dr_query_groups_workspace(ctypes.byref(dims), ctypes.byref(need)))
+    if workspace is None:
+        workspace = torch.empty(need.value, dtype=torch.uint8, device=q.device)
+    modes = torch.empty(dims.batch * dims.heads, dtype=torch.int32, device=q.device)
+    check(lib().dr_query_groups(ctypes.byref(dims), ctypes.byref(cand.cfg), cand.row_ptr.data_ptr(), cand.nnz,
+                                kept.kept_col.data_ptr(), kept.kept_cnt.data_ptr(), modes.data_ptr(),
+                                workspace.data_ptr(), workspace.numel(), _stream(q.device)))
+    return modes
+
+
+def sparse_attn(q, k, v, cand: Candidates, kept: Kept, softmax_scale: Optional[float] = None, out=None,
+                groups=None):
+    """groups: None (consecutive query blocks per workgroup), "auto" (the
+    grouping chosen by query_groups) or an int32 tensor of modes [B * H].
+    The output does not depend on the grouping."""
     torch = _torch()
     shape = _check_qkv(q, k, v)
     dims = _dims(shape)
     scale = 1.0 / math.sqrt(shape[3]) if softmax_scale is None else float(softmax_scale)
     if out is None:
         out = torch.empty_like(q)
-    check(lib().dr_sparse_attn(ctypes.byref(dims), ctypes.byref(cand.cfg), q.data_ptr(), k.data_ptr(),
-                               v.data_ptr(), cand.row_ptr.data_ptr(), cand.nnz, kept.kept_col.data_ptr(),
-                               kept.kept_cnt.data_ptr(), scale, out.data_ptr(), _stream(q.device)))
+    if isinstance(groups, str):
+        if groups != "auto":
+            raise ValueError(f"groups must be None, 'auto' or a tensor, not {groups!r}")
+        groups = query_groups(q, cand, kept)
+    if groups is None:
+        check(lib().dr_sparse_attn(ctypes.byref(dims), ctypes.byref(cand.cfg), q.data_ptr(), k.data_ptr(),
+                                   v.data_ptr(), cand.row_ptr.data_ptr(), cand.nnz, kept.kept_col.data_ptr(),
+                                   kept.kept_cnt.data_ptr(), scale, out.data_ptr(), _stream(q.device)))
+    else:
+        if groups.dtype != torch.int32 or groups.numel() != dims.batch * dims.heads or groups.device != q.device:
+            raise ValueError("groups must be an int32 tensor of B * H modes on q's device")
+        check(lib().dr_sparse_attn_grouped(ctypes.byref(dims), ctypes.byref(cand.cfg), q.data_ptr(), k.data_ptr(),
+                                           v.data_ptr(), cand.row_ptr.data_ptr(), cand.nnz,
+                                           kept.kept_col.data_ptr(), kept.kept_cnt.data_ptr(),
+                                           groups.contiguous().data_ptr(), scale, out.data_ptr(),
+                                           _stream(q.device)))
     return out
 
 

@@ -16,7 +16,8 @@ from concurrent.futures import ThreadPoolExecutor
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libdynrad.so")
-SOURCES = ["api.cpp", "candidates.hip", "score_select.hip", "attention.hip", "token_select.hip", "static_select.hip", "proxy.hip"]
+SOURCES = ["api.cpp", "candidates.hip", "score_select.hip", "attention.hip", "groups.hip", "token_select.hip",
+           "static_select.hip", "proxy.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

@@ -2,6 +2,7 @@
 // the host per-distance table, workspace layout and kernel launches.
 // Every check runs before any HIP call, so an invalid call touches no device.
 #include <math.h>
+#include <algorithm>
 #include <stdarg.h>
 #include <stdio.h>
 
@@ -326,6 +327,8 @@ static dr_status attn_common(const dr_dims* dims, long long S, const void* q, co
   p->S = (int)S;
   p->BH = dims->batch * dims->heads;
   p->n_tiles = (int)((S + 255) / 256);
+  p->group_mode = nullptr;
+  p->grp = dr::QGroup{};
   p->scale_log2 = scale * 1.4426950408889634f;
   return DR_OK;
 }
@@ -507,9 +510,10 @@ dr_status dr_proxy_error(const void* o_ref, const void* o_test, int64_t n, const
   return ok();
 }
 
-dr_status dr_sparse_attn(const dr_dims* dims, const dr_radial_cfg* cfg, const void* q, const void* k,
-                         const void* v, const int32_t* row_ptr, int64_t nnz, const int32_t* kept_col,
-                         const int32_t* kept_cnt, float softmax_scale, void* out, hipStream_t stream) {
+static dr_status sparse_attn_impl(const dr_dims* dims, const dr_radial_cfg* cfg, const void* q, const void* k,
+                                  const void* v, const int32_t* row_ptr, int64_t nnz, const int32_t* kept_col,
+                                  const int32_t* kept_cnt, const int32_t* group_mode, float softmax_scale,
+                                  void* out, hipStream_t stream) {
   Layout L;
   dr_status st = check_radial(cfg, &L);
   if (st != DR_OK) return st;
@@ -521,10 +525,85 @@ dr_status dr_sparse_attn(const dr_dims* dims, const dr_radial_cfg* cfg, const vo
   p.row_ptr = row_ptr;
   p.kept_col = kept_col;
   p.kept_cnt = kept_cnt;
+  p.group_mode = group_mode;
+  p.grp = dr::make_qgroup(cfg->num_frames, cfg->tokens_per_frame, cfg->block_size, L.Sb);
   p.nnz = nnz;
   p.Sb = L.Sb;
   const hipError_t e = dr::launch_sparse_attn(p, dims->head_dim, cfg->block_size, stream);
   if (e != hipSuccess) return hip_fail(e, "sparse attention kernel");
+  return ok();
+}
+
+dr_status dr_sparse_attn(const dr_dims* dims, const dr_radial_cfg* cfg, const void* q, const void* k,
+                         const void* v, const int32_t* row_ptr, int64_t nnz, const int32_t* kept_col,
+                         const int32_t* kept_cnt, float softmax_scale, void* out, hipStream_t stream) {
+  return sparse_attn_impl(dims, cfg, q, k, v, row_ptr, nnz, kept_col, kept_cnt, nullptr, softmax_scale, out,
+                          stream);
+}
+
+dr_status dr_sparse_attn_grouped(const dr_dims* dims, const dr_radial_cfg* cfg, const void* q, const void* k,
+                                 const void* v, const int32_t* row_ptr, int64_t nnz, const int32_t* kept_col,
+                                 const int32_t* kept_cnt, const int32_t* group_mode, float softmax_scale,
+                                 void* out, hipStream_t stream) {
+  if (!group_mode) return fail(DR_ERR_INVALID_ARG, "group_mode must be non-NULL");
+  return sparse_attn_impl(dims, cfg, q, k, v, row_ptr, nnz, kept_col, kept_cnt, group_mode, softmax_scale, out,
+                          stream);
+}
+
+int64_t dr_query_group_table(const dr_radial_cfg* cfg, int32_t mode, int32_t* table, int64_t cap) {
+  Layout L;
+  dr_status st = check_radial(cfg, &L);
+  if (st != DR_OK) return -(int64_t)st;
+  if (mode < 0 || mode >= dr::kGroupModes)
+    return -(int64_t)fail(DR_ERR_INVALID_ARG, "mode %d outside [0, %d)", mode, dr::kGroupModes);
+  const dr::QGroup g = dr::make_qgroup(cfg->num_frames, cfg->tokens_per_frame, cfg->block_size, L.Sb);
+  const long long n = (long long)dr::group_count(g, mode) * g.QB;
+  if (!table) {
+    ok();
+    return n;
+  }
+  if (cap < n)
+    return -(int64_t)fail(DR_ERR_CAPACITY, "table of %lld entries below the %lld required", (long long)cap, n);
+  for (int gi = 0; gi < dr::group_count(g, mode); ++gi)
+    for (int s = 0; s < g.QB; ++s) table[(long long)gi * g.QB + s] = dr::group_block(g, mode, gi, s);
+  ok();
+  return n;
+}
+
+dr_status dr_query_groups_workspace(const dr_dims* dims, size_t* bytes) {
+  dr_status st = check_dims(dims);
+  if (st != DR_OK) return st;
+  if (!bytes) return fail(DR_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = align256((size_t)dims->batch * dims->heads * dr::kGroupModes * sizeof(uint32_t));
+  return ok();
+}
+
+dr_status dr_query_groups(const dr_dims* dims, const dr_radial_cfg* cfg, const int32_t* row_ptr, int64_t nnz,
+                          const int32_t* kept_col, const int32_t* kept_cnt, int32_t* group_mode, void* ws,
+                          size_t ws_bytes, hipStream_t stream) {
+  Layout L;
+  dr_status st = check_radial(cfg, &L);
+  if (st != DR_OK) return st;
+  if ((st = check_dims(dims)) != DR_OK) return st;
+  if ((st = check_nnz(nnz, L.Sb, dims)) != DR_OK) return st;
+  if (!row_ptr || !kept_col || !kept_cnt || !group_mode || !ws)
+    return fail(DR_ERR_INVALID_ARG, "row_ptr, kept_col, kept_cnt, group_mode and ws must be non-NULL");
+  const size_t need = align256((size_t)dims->batch * dims->heads * dr::kGroupModes * sizeof(uint32_t));
+  if (ws_bytes < need) return fail(DR_ERR_CAPACITY, "workspace of %zu bytes below the %zu required", ws_bytes, need);
+  if ((long long)dims->batch * dims->heads > 65535) return fail(DR_ERR_UNSUPPORTED, "batch * heads above 65535");
+  dr::GroupCostParams p;
+  p.row_ptr = row_ptr;
+  p.kept_col = kept_col;
+  p.kept_cnt = kept_cnt;
+  p.totals = static_cast<uint32_t*>(ws);
+  p.group_mode = group_mode;
+  p.grp = dr::make_qgroup(cfg->num_frames, cfg->tokens_per_frame, cfg->block_size, L.Sb);
+  p.nnz = nnz;
+  p.BH = dims->batch * dims->heads;
+  p.gmax = 0;
+  for (int m = 0; m < dr::kGroupModes; ++m) p.gmax = std::max(p.gmax, dr::group_count(p.grp, m));
+  const hipError_t e = dr::launch_group_choice(p, stream);
+  if (e != hipSuccess) return hip_fail(e, "query grouping kernels");
   return ok();
 }
 

@@ -129,6 +129,19 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
   const int bh = blockIdx.y;
   const int row0 = blockIdx.x * kRows;
   const size_t base = (size_t)bh * p.S * D;
+  // query block of group slot s (sparse: per-(b, h) grouping mode)
+  int gmode = 0;
+  if constexpr (SPARSE) {
+    if (p.group_mode) {
+      gmode = p.group_mode[bh];
+      if (gmode < 0 || gmode >= kGroupModes || group_count(p.grp, gmode) == 0) gmode = 0;
+    }
+    if ((int)blockIdx.x >= group_count(p.grp, gmode)) return;   // uniform: before any barrier
+  }
+  auto qblock = [&](int s) -> int {
+    if constexpr (SPARSE) return group_block(p.grp, gmode, blockIdx.x, s);
+    else return row0 / BS + s;
+  };
   const int nword = (p.Sb + 31) >> 5;
   unsigned int* uword = bits + QB * nword;        // union of the query blocks' bitmaps
   int* wpre = reinterpret_cast<int*>(uword + nword);  // exclusive prefix popcounts
@@ -140,8 +153,8 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
     for (int i = tid; i < QB * nword; i += kThreads) bits[i] = 0;
     __syncthreads();
     if (wave < QB) {
-      const int qb = row0 / BS + wave;
-      if (qb < p.Sb) {
+      const int qb = qblock(wave);
+      if (qb >= 0 && qb < p.Sb) {
         const int32_t* kl = p.kept_col + (long long)bh * p.nnz + p.row_ptr[qb];
         const int cnt = p.kept_cnt[(long long)bh * p.Sb + qb];
         for (int i = lane; i < cnt; i += 64) {
@@ -290,7 +303,11 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
 
   // ---------------- compute wavefronts ----------------
   const int half = lane >> 5, l32 = lane & 31;
-  const int wrow0 = row0 + wave * 32;
+  int wrow0 = row0 + wave * 32;
+  if constexpr (SPARSE) {
+    const int qb = qblock(wave / WPQ);
+    wrow0 = qb >= 0 ? qb * BS + (wave % WPQ) * 32 : p.S;
+  }
   bf16x8 qf[D / 16];
   {
     const int r = wrow0 + l32;
@@ -473,7 +490,12 @@ size_t lds_bytes(const AttnParams& p) {
 template <int D, int BS, bool SPARSE>
 hipError_t launch_one(const AttnParams& p, hipStream_t stream) {
   constexpr int DEEP = D == 128 ? 9 : 16;
-  const dim3 grid((unsigned)p.n_tiles, (unsigned)p.BH);
+  // sparse: the widest grouping in use; a workgroup past its mode's group
+  // count exits at once
+  int gx = p.n_tiles;
+  if (SPARSE && p.group_mode)
+    for (int m = 1; m < kGroupModes; ++m) gx = max(gx, group_count(p.grp, m));
+  const dim3 grid((unsigned)gx, (unsigned)p.BH);
   const size_t deep = lds_bytes<D, BS, SPARSE, DEEP>(p);
   const size_t base = lds_bytes<D, BS, SPARSE, 8>(p);
   if (deep <= (size_t)kLdsBytes)

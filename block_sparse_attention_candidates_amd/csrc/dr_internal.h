@@ -123,6 +123,84 @@ struct SelectParams {
   int min_n;       // rows of at most min_n candidates are left to the per-wave kernel
 };
 
+// Query-block grouping of the sparse attention: a workgroup owns QB = 256 / B_s
+// query blocks, and the blocks of one (b, h) are partitioned into groups of at
+// most QB. Mode 0 groups consecutive blocks (QB g .. QB g + QB - 1). Modes 1 and
+// 2 lay the blocks out in rows, one per frame (row f holds blocks
+// [floor(f N_t / B_s), floor((f + 1) N_t / B_s)), the last row runs to S_b),
+// and group g takes F consecutive rows by R adjacent columns (F R = QB): blocks
+// at the same place in neighbouring frames, whose kept lists tend to share key
+// blocks when the selection follows content. Every mode is a partition of
+// [0, S_b); a mode without a shape for this QB has no groups.
+constexpr int kGroupModes = 3;
+
+struct QGroup {
+  int QB, Nf, Nt, Bs, Sb;
+  int cols[kGroupModes];   // column chunks per row chunk (modes 1, 2)
+};
+
+__host__ __device__ inline void group_shape(int QB, int mode, int* F, int* R) {
+  // QB = 2, 4, 8 -> index 0, 1, 2
+  const int i = QB == 2 ? 0 : QB == 4 ? 1 : 2;
+  const int f1[3] = {2, 2, 4}, r1[3] = {1, 2, 2}, f2[3] = {0, 4, 2}, r2[3] = {0, 1, 4};
+  *F = mode == 1 ? f1[i] : mode == 2 ? f2[i] : 0;
+  *R = mode == 1 ? r1[i] : mode == 2 ? r2[i] : 0;
+}
+
+__host__ __device__ inline int frame_row_start(const QGroup& q, int f) {
+  return (int)(((long long)f * q.Nt) / q.Bs);
+}
+
+__host__ __device__ inline int frame_row_end(const QGroup& q, int f) {
+  return f == q.Nf - 1 ? q.Sb : frame_row_start(q, f + 1);
+}
+
+// Groups of a mode (0 for a mode without a shape).
+__host__ __device__ inline int group_count(const QGroup& q, int mode) {
+  if (mode == 0) return (q.Sb + q.QB - 1) / q.QB;
+  int F, R;
+  group_shape(q.QB, mode, &F, &R);
+  if (F == 0) return 0;
+  return ((q.Nf + F - 1) / F) * q.cols[mode];
+}
+
+// Query block in slot s of group g (-1: empty slot).
+__host__ __device__ inline int group_block(const QGroup& q, int mode, int g, int s) {
+  if (mode == 0) {
+    const int a = g * q.QB + s;
+    return a < q.Sb ? a : -1;
+  }
+  int F, R;
+  group_shape(q.QB, mode, &F, &R);
+  if (F == 0) return -1;
+  const int rc = g / q.cols[mode], cc = g - rc * q.cols[mode];
+  const int f = rc * F + s / R, c = cc * R + s % R;
+  if (f >= q.Nf) return -1;
+  const int s0 = frame_row_start(q, f);
+  return c < frame_row_end(q, f) - s0 ? s0 + c : -1;
+}
+
+// Host: the grouping geometry of a layout.
+inline QGroup make_qgroup(int Nf, int Nt, int Bs, int Sb) {
+  QGroup q;
+  q.QB = 256 / Bs;
+  q.Nf = Nf;
+  q.Nt = Nt;
+  q.Bs = Bs;
+  q.Sb = Sb;
+  int lmax = 0;
+  for (int f = 0; f < Nf; ++f) {
+    const int len = frame_row_end(q, f) - frame_row_start(q, f);
+    if (len > lmax) lmax = len;
+  }
+  for (int m = 0; m < kGroupModes; ++m) {
+    int F, R;
+    group_shape(q.QB, m, &F, &R);
+    q.cols[m] = R > 0 ? (lmax + R - 1) / R : 0;
+  }
+  return q;
+}
+
 struct AttnParams {
   const uint16_t* q;
   const uint16_t* k;
@@ -131,10 +209,23 @@ struct AttnParams {
   const int32_t* row_ptr;
   const int32_t* kept_col;
   const int32_t* kept_cnt;
+  const int32_t* group_mode;  // [BH] grouping mode per (b, h), or null (mode 0)
+  QGroup grp;
   long long nnz;
   int S, Sb, BH;
-  int n_tiles;        // query-row tiles per (b, h)
+  int n_tiles;        // query-row tiles per (b, h) (dense) / grid width (sparse)
   float scale_log2;   // softmax_scale * log2(e)
+};
+
+struct GroupCostParams {
+  const int32_t* row_ptr;
+  const int32_t* kept_col;
+  const int32_t* kept_cnt;
+  uint32_t* totals;   // [BH][kGroupModes] kept-list union sizes
+  int32_t* group_mode;
+  QGroup grp;
+  long long nnz;
+  int BH, gmax;
 };
 
 // Token-level dynamic-threshold selection ([DR] §3.2 Eqs. 9-11).
@@ -240,5 +331,6 @@ hipError_t launch_scores(const ScoreParams& p, int B, hipStream_t stream);
 hipError_t launch_select(const SelectParams& p, int B, hipStream_t stream);
 hipError_t launch_sparse_attn(const AttnParams& p, int D, int Bs, hipStream_t stream);
 hipError_t launch_dense_attn(const AttnParams& p, int D, hipStream_t stream);
+hipError_t launch_group_choice(const GroupCostParams& p, hipStream_t stream);
 
 }  // namespace dr

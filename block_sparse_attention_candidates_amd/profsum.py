@@ -62,7 +62,7 @@ def _counter(run_dir: str, counter: str):
 
 
 # the sources the sparse-attention kernel is compiled from
-ATTENTION_SOURCES = ("attention.hip", "lds_dma.h", "dr_internal.h")
+ATTENTION_SOURCES = ("attention.hip", "groups.hip", "lds_dma.h", "dr_internal.h")
 
 
 def attention_source_digest() -> str:

@@ -15,7 +15,9 @@
  *      dr_static_select     the paper's decay-state static-ratio selector
  *                           ([DR] §3.2 Eq. 8, Algorithm 1), content-free.
  *   3. dr_sparse_attn       flash-style forward attention over the kept KV
- *                           blocks only ([DR] §3.3, Eq. 13 with eps -> 0).
+ *                           blocks only ([DR] §3.3, Eq. 13 with eps -> 0);
+ *      dr_query_groups,     the same with the query blocks grouped so that a
+ *      dr_sparse_attn_grouped  workgroup's kept lists overlap most.
  *   dr_attn                 dense forward attention, the speedup denominator
  *                           ([DR] App. A, Eq. 16).
  *   dr_proxy_error          error sums of the proxy-task objective ([DR]
@@ -240,6 +242,49 @@ dr_status dr_sparse_attn(const dr_dims* dims, const dr_radial_cfg* cfg, const vo
                          const void* k, const void* v, const int32_t* row_ptr, int64_t nnz,
                          const int32_t* kept_col, const int32_t* kept_cnt, float softmax_scale,
                          void* out, hipStream_t stream);
+
+/* Query-block grouping of the sparse attention (scheduling only: the output of
+ * dr_sparse_attn_grouped is bit-identical to dr_sparse_attn's for every mode).
+ * One workgroup computes a group of Q = 256 / B_s query blocks and reads the
+ * union of their kept lists ([DR] §3.3: each kept block pair is one tile), so
+ * groups whose kept lists overlap read fewer key/value bytes. Modes:
+ *   0: consecutive blocks Q g .. Q g + Q - 1 (the grouping of dr_sparse_attn);
+ *   1, 2: blocks in rows, one per frame (row f = blocks [floor(f N_t / B_s),
+ *      floor((f + 1) N_t / B_s)), the last row up to S_b); a group is F
+ *      consecutive rows by R adjacent columns, (F, R) = (4, 2) and (2, 4) at
+ *      B_s = 32, (2, 2) and (4, 1) at 64, (2, 1) at 128 (mode 2 has no group
+ *      at 128).
+ * Each mode partitions [0, S_b) into groups of at most Q blocks.
+ *
+ * dr_query_group_table (host only): the blocks of every group of a mode, Q per
+ * group in slot order, -1 for an empty slot; returns the entry count (groups
+ * times Q) or a negative dr_status. table = NULL only returns the count; else
+ * cap must reach it. */
+int64_t dr_query_group_table(const dr_radial_cfg* cfg, int32_t mode, int32_t* table, int64_t cap);
+
+/* Device workspace (bytes) of dr_query_groups: 12 bytes per (b, h), rounded up
+ * to 256. Host only. */
+dr_status dr_query_groups_workspace(const dr_dims* dims, size_t* bytes);
+
+/* Per (b, h), the grouping mode whose groups' kept-list unions have the
+ * smallest estimated total size: the union sizes of groups 0, 4, 8, ... of a
+ * mode, summed and scaled by (groups of the mode) / (groups measured); ties go
+ * to the lower mode. Kept lists in the layout of dr_score_select. Integer work
+ * (compared by cross-multiplication), deterministic.
+ * group_mode: device int32 [B * H] (output); ws: device workspace of at least
+ * dr_query_groups_workspace bytes; B * H <= 65535. */
+dr_status dr_query_groups(const dr_dims* dims, const dr_radial_cfg* cfg, const int32_t* row_ptr,
+                          int64_t nnz, const int32_t* kept_col, const int32_t* kept_cnt,
+                          int32_t* group_mode, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* dr_sparse_attn with the query blocks of (b, h) grouped by mode
+ * group_mode[b * H + h] (device int32 [B * H], non-NULL; a value that is not a
+ * mode with groups at this B_s means mode 0). Same results as dr_sparse_attn. */
+dr_status dr_sparse_attn_grouped(const dr_dims* dims, const dr_radial_cfg* cfg, const void* q,
+                                 const void* k, const void* v, const int32_t* row_ptr, int64_t nnz,
+                                 const int32_t* kept_col, const int32_t* kept_cnt,
+                                 const int32_t* group_mode, float softmax_scale, void* out,
+                                 hipStream_t stream);
 
 /* Dense forward attention over all seq_len keys (bidirectional), the baseline
  * of [DR] App. A Eq. 16 / Table 5 "Dense". Same numerics and layouts as

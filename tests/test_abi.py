@@ -211,3 +211,64 @@ def test_proxy_error_validation(dynrad_lib):
     assert pe(n_cnt=5) == L.DR_ERR_INVALID_ARG            # counts without a pointer
     assert pe(t=ctypes.c_void_p(8200)) == L.DR_ERR_INVALID_ARG   # not 16-byte aligned
     assert pe(ws_bytes=L.PROXY_WS_BYTES - 8) == L.DR_ERR_CAPACITY
+
+
+@pytest.mark.parametrize("layout", [(21, 3600, 32), (21, 1560, 32), (33, 3600, 64), (9, 33, 128), (6, 200, 64),
+                                    (4, 64, 32), (1, 1000, 32), (13, 31, 32), (5, 300, 128)])
+def test_query_group_tables_partition_the_blocks(dynrad_lib, layout):
+    """Every grouping mode is a partition of the query blocks into groups of
+    256 / B_s slots (-1 = empty), and modes 1 and 2 take F frame rows by R
+    adjacent columns, row f being blocks [floor(f N_t / B_s), floor((f + 1) N_t / B_s))
+    (the last row up to S_b)."""
+    import block_sparse_attention_candidates_amd as dr
+    Nf, Nt, Bs = layout
+    cand_cfg = _cfg(Nf, Nt, Bs, 1.0, 1.0)
+    Sb = dr.num_blocks(cand_cfg)
+    Q = 256 // Bs
+    shapes = {32: [(4, 2), (2, 4)], 64: [(2, 2), (4, 1)], 128: [(2, 1)]}[Bs]
+    starts = [f * Nt // Bs for f in range(Nf)] + [Sb]
+    frame_of = np.searchsorted(np.array(starts[1:]), np.arange(Sb), side="right")
+
+    class _C:
+        cfg = cand_cfg
+    for mode in range(3):
+        t = dr.group_table(_C, mode)
+        assert t.shape[1] == Q
+        if mode == 2 and Bs == 128:
+            assert t.size == 0
+            continue
+        used = t[t >= 0]
+        assert np.array_equal(np.sort(used), np.arange(Sb)), f"mode {mode}: not a partition"
+        if mode == 0:
+            assert np.array_equal(t.reshape(-1)[:Sb], np.arange(Sb))
+            continue
+        F, R = shapes[mode - 1]
+        for g in t:
+            chunk = set()
+            for s, a in enumerate(g):
+                if a < 0:
+                    continue
+                f = int(frame_of[a])
+                c = int(a - starts[f])
+                # slot s holds row (chunk row) * F + s // R, column (chunk column) * R + s % R
+                assert (f - s // R) % F == 0 and (c - s % R) % R == 0, (mode, g)
+                chunk.add(((f - s // R) // F, (c - s % R) // R))
+            assert len(chunk) <= 1, (mode, g)
+    assert dynrad_lib.dr_query_group_table(ctypes.byref(cand_cfg), 3, None, 0) < 0
+    assert dynrad_lib.dr_query_group_table(ctypes.byref(cand_cfg), -1, None, 0) < 0
+
+
+def test_query_groups_validation(dynrad_lib):
+    from block_sparse_attention_candidates_amd import _lib as L
+    cfg = _cfg(4, 64, 32, 1.0, 2.0)            # S = 256, S_b = 8
+    dims = L.Dims(2, 3, 64, 0)
+    size = ctypes.c_size_t(0)
+    assert dynrad_lib.dr_query_groups_workspace(ctypes.byref(dims), ctypes.byref(size)) == L.DR_OK
+    assert size.value == 256                  # 2 * 3 * 3 * 4 = 72 bytes, rounded up
+    args = (ctypes.byref(dims), ctypes.byref(cfg), FAKE, 16, FAKE, FAKE, FAKE)
+    assert dynrad_lib.dr_query_groups(*args, FAKE, 255, None) == L.DR_ERR_CAPACITY
+    assert dynrad_lib.dr_query_groups(*args, None, 256, None) == L.DR_ERR_INVALID_ARG
+    assert dynrad_lib.dr_query_groups(ctypes.byref(dims), ctypes.byref(cfg), FAKE, 16, FAKE, FAKE, None, FAKE, 256,
+                                      None) == L.DR_ERR_INVALID_ARG
+    assert dynrad_lib.dr_sparse_attn_grouped(ctypes.byref(dims), ctypes.byref(cfg), FAKE, FAKE, FAKE, FAKE, 16,
+                                             FAKE, FAKE, None, 0.125, FAKE, None) == L.DR_ERR_INVALID_ARG
