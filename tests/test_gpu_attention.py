@@ -164,8 +164,14 @@ def test_sparse_attention_empty_rows_and_bad_entries():
         extra = torch.tensor([-5, Sb + 9, int(col[0, rp[a]])], dtype=torch.int32, device="cuda")
         col[0, rp[a] + n: rp[a] + n + 3] = extra
         cnt[0, a] = n + 3
-        out2 = G.to_np(G.dr().sparse_attn(q, k, v, cand, G.dr().Kept(col.view(-1), cnt.view(-1))))
+        bad = G.dr().Kept(col.view(-1), cnt.view(-1))
+        out2 = G.to_np(G.dr().sparse_attn(q, k, v, cand, bad))
         np.testing.assert_array_equal(out2[0, 0, a * 32:(a + 1) * 32], out[0, 0, a * 32:(a + 1) * 32])
+        # the same under every query grouping and the chosen one (bad entries ignored there too)
+        for modes in [torch.full((B * H,), m, dtype=torch.int32, device="cuda") for m in range(3)] + \
+                     [G.dr().query_groups(q, cand, bad)]:
+            out3 = G.to_np(G.dr().sparse_attn(q, k, v, cand, bad, groups=modes))
+            np.testing.assert_array_equal(out3, out2)
 
 
 def test_attention_special_cases_and_determinism():

@@ -21,14 +21,12 @@ def test_candidates_full_size_match_golden(name):
     assert G.digest(cols) == gold["cols_sha256"]
 
 
-@pytest.mark.parametrize("case", CASES + [(3, 256, 32, 1.0, 0.1, 0.0, 0.0), (1, 100, 64, 1.0, 1.0, 0.0, 0.0),
+# the oracle's small cases at the block sizes the library builds (32, 64, 128)
+@pytest.mark.parametrize("case", [c for c in CASES if c[2] in (32, 64, 128)] + [(3, 256, 32, 1.0, 0.1, 0.0, 0.0), (1, 100, 64, 1.0, 1.0, 0.0, 0.0),
                                           (40, 33, 32, 1.5, 0.05, 0.0, 0.0), (12, 500, 64, 0.9, 0.3, 0.3, 0.4),
                                           (10, 100, 128, 1.0, 0.3, 0.0, 0.0), (6, 200, 128, 1.4, 0.7, 0.45, 0.7)])
 def test_candidates_small_exact(case):
     G.log(f"[candidates] small {case}")
-    Nf, Nt, Bs, gamma, lam, tc, tm = case
-    if Bs not in (32, 64, 128):
-        pytest.skip("block size not built")
     cand = G.dr().build_candidates(G.dr().radial_cfg(*case))
     rp, cols = G.host_csr(cand)
     orp, ocols = O.candidate_csr(*case)
