@@ -185,7 +185,8 @@ __device__ inline floatx8 load8(const float* src) {
 }
 
 template <int D>
-__global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreParams p) {
+__global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreParams p, const uint32_t* __restrict__ dbits,
+                                                             const int32_t* __restrict__ dpos) {
   constexpr int KS = D / 16;   // 16-dim steps of v_mfma_f32_32x32x16_bf16
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -239,31 +240,35 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreParams p) {
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qh[kk], kh, acc, 0, 0, 0);
     }
   };
-  // element i of this lane is (row 8*(i/4) + 4*half + i%4, key block t*32 + m32):
-  // the lane's 16 rows are 4 runs of 4 consecutive rows, whose bitmaps and
-  // positions it loads as 16-byte vectors together with the tile's K rows
+  // element i of this lane is (row 8*(i/4) + 4*half + i%4, key block t*32 + m32).
+  // A tile's 32 bitmaps and positions are wave-uniform: scalar loads of both
+  // halves' rows, selected per lane.
   typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
   typedef int i32x4_t __attribute__((ext_vector_type(4)));
-  auto load_desc = [&](u32x4_t* bw, i32x4_t* ps, int j) {
-    const u32x4_t* b4 = reinterpret_cast<const u32x4_t*>(td.bits + (dbase + j) * 32 + 4 * half);
-    const i32x4_t* p4 = reinterpret_cast<const i32x4_t*>(td.pos + (dbase + j) * 32 + 4 * half);
+  struct Desc {
+    unsigned int b[32];
+    int ps[32];
+  };
+  auto load_desc = [&](Desc& dsc, int j) {
+    const size_t at = (size_t)__builtin_amdgcn_readfirstlane((int)((dbase + j) * 32));
 #pragma unroll
-    for (int x = 0; x < 4; ++x) {
-      bw[x] = b4[2 * x];
-      ps[x] = p4[2 * x];
+    for (int m = 0; m < 32; ++m) {
+      dsc.b[m] = dbits[at + m];
+      dsc.ps[m] = dpos[at + m];
     }
   };
-  auto store = [&](const floatx16& acc, const u32x4_t* bw, const i32x4_t* ps) {
+  auto store = [&](const floatx16& acc, const Desc& dsc) {
     const unsigned int below = (1u << m32) - 1u;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const unsigned int bits = bw[i >> 2][i & 3];
-      if ((bits >> m32) & 1u) p.scores[out_base + ps[i >> 2][i & 3] + __popc(bits & below)] = acc[i] * p.scale;
+      const int m0 = 8 * (i >> 2) + (i & 3);
+      const unsigned int bits = half ? dsc.b[m0 + 4] : dsc.b[m0];
+      const int ps = half ? dsc.ps[m0 + 4] : dsc.ps[m0];
+      if ((bits >> m32) & 1u) p.scores[out_base + ps + __popc(bits & below)] = acc[i] * p.scale;
     }
   };
 
-  u32x4_t bw[4];
-  i32x4_t ps[4];
+  Desc dsc;
   if (p.g == 1) {
     // per tile: its bitmaps and positions are requested first, then the
     // products, then the next tile's K rows, so the stores wait only for the
@@ -279,7 +284,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreParams p) {
       int t = s_word[j];
       load_k(kv, t, 0);
       while (true) {
-        load_desc(bw, ps, j);
+        load_desc(dsc, j);
         __builtin_amdgcn_sched_barrier(0);
         const int jn = j + kScoreThreads / 64;
         const int tn = s_word[min(jn, ntiles - 1)];
@@ -296,7 +301,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreParams p) {
           acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qh[kk], kh, acc, 0, 0, 0);
           __builtin_amdgcn_sched_barrier(0);
         }
-        store(acc, bw, ps);
+        store(acc, dsc);
         if (jn >= ntiles) break;
         j = jn;
         t = tn;
@@ -305,7 +310,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreParams p) {
   } else {
     for (int j = wave; j < ntiles; j += kScoreThreads / 64) {
       const int t = s_word[j];
-      load_desc(bw, ps, j);
+      load_desc(dsc, j);
       floatx16 acc = {};
       for (int hh = 0; hh < p.g; ++hh) {
         load_q(hh);
@@ -313,7 +318,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreParams p) {
         load_k(kv, t, hh);
         mma(acc, kv, t);
       }
-      store(acc, bw, ps);
+      store(acc, dsc);
     }
   }
 }
@@ -708,9 +713,9 @@ hipError_t launch_tile_desc(const ScoreParams& p, hipStream_t stream) {
 hipError_t launch_scores(const ScoreParams& p, int B, hipStream_t stream) {
   const dim3 grid((unsigned)(p.tiles.ngroups * B * p.Hm));
   if (p.D == 128)
-    hipLaunchKernelGGL(score_kernel<128>, grid, dim3(kScoreThreads), 0, stream, p);
+    hipLaunchKernelGGL(score_kernel<128>, grid, dim3(kScoreThreads), 0, stream, p, p.tiles.bits, p.tiles.pos);
   else
-    hipLaunchKernelGGL(score_kernel<64>, grid, dim3(kScoreThreads), 0, stream, p);
+    hipLaunchKernelGGL(score_kernel<64>, grid, dim3(kScoreThreads), 0, stream, p, p.tiles.bits, p.tiles.pos);
   return hipGetLastError();
 }
 
