@@ -8,7 +8,7 @@ Attention for Long Video Diffusion" (arXiv 2604.20470).
 
     cand = build_candidates(radial_cfg(num_frames, tokens_per_frame, block_size, gamma, lam))
     kept = score_select(q, k, cand, mode="static", ratio=0.15)      # or mode="dynamic", tau=0.8
-    out  = sparse_attn(q, k, v, cand, kept)
+    out  = sparse_attn(q, k, v, cand, kept, groups="auto")       # query blocks grouped per head
     ref  = attn(q, k, v)                                            # dense baseline
 
 q, k, v: torch.bfloat16 [B, H, S, D] contiguous CUDA (HIP) tensors,
@@ -304,7 +304,7 @@ def proxy_loss(q, k, z, cand: Candidates, kept: Kept, alpha: float = 10.0, targe
     the probe z: dense and kept-block attention of (q, k, z), the normalised
     error of the outputs, the sparsity of the mask and the penalised loss."""
     o_ref = attn(q, k, z)
-    o_test = sparse_attn(q, k, z, cand, kept)
+    o_test = sparse_attn(q, k, z, cand, kept, groups="auto")
     num, den, n_kept = proxy_error(o_ref, o_test, kept)
     B, H = int(q.shape[0]), int(q.shape[1])
     sparsity = 1.0 - n_kept / float(B * H * cand.num_blocks ** 2)
