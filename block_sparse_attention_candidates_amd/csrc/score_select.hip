@@ -102,9 +102,14 @@ __global__ __launch_bounds__(kPrepThreads) void tile_desc_kernel(ScoreParams p) 
     const int a = a0 + m;
     if (a >= p.Sb) continue;
     const int e1 = p.row_ptr[a + 1];
-    for (int e = p.row_ptr[a] + lane; e < e1; e += 64) {
-      const int c = p.cols[e];
-      atomicOr(&s_bits[m * nword + (c >> 5)], 1u << (c & 31));
+    // 8 column loads in flight per lane before their bits are set
+    for (int e0 = p.row_ptr[a] + lane; e0 < e1; e0 += 8 * 64) {
+      int c[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) c[u] = e0 + 64 * u < e1 ? p.cols[e0 + 64 * u] : -1;
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (c[u] >= 0) atomicOr(&s_bits[m * nword + (c[u] >> 5)], 1u << (c[u] & 31));
     }
   }
   __syncthreads();
