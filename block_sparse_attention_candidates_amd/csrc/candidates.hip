@@ -33,35 +33,65 @@ __device__ void build_table(const CandParams& p, int* s_w, int* s_sf) {
 // per frame segment of a as an interval intersection. Column k is active iff
 // count / n_q > theta_c; the block is a candidate iff active / n_k > theta_m.
 // active only grows, so the first time the block test passes decides it.
-__device__ bool is_candidate(int a, int b, const CandParams& p, const int* s_w, const int* s_sf) {
+__device__ bool is_candidate(int a, int b, const CandParams& p, const int* s_w, const int* s_sf, const int* s_thr) {
   const int q0 = a * p.Bs, q1 = min(q0 + p.Bs, p.S);
   const int k0 = b * p.Bs, k1 = min(k0 + p.Bs, p.S);
-  if (p.theta_c == 0.0 && p.theta_m == 0.0) {
-    // With both thresholds at 0 the block is a candidate iff some query frame
-    // segment and some key frame segment are retained (Eq. 6) and come within
-    // w(t) of each other (Eq. 7): the interval distance
-    // max(0, v_lo - u_hi, u_lo - v_hi) decides it.
-    for (int s = q0; s < q1;) {
-      const int fq = s / p.Nt;
-      const int s_end = min(q1, (fq + 1) * p.Nt);
-      const int ulo = s - fq * p.Nt, uhi = s_end - 1 - fq * p.Nt;
-      for (int k = k0; k < k1;) {
-        const int fk = k / p.Nt;
-        const int k_end = min(k1, (fk + 1) * p.Nt);
-        const int vlo = k - fk * p.Nt, vhi = k_end - 1 - fk * p.Nt;
-        const int t = fq > fk ? fq - fk : fk - fq;
-        if (t % s_sf[t] == 0 && max(0, max(vlo - uhi, ulo - vhi)) <= s_w[t]) return true;
-        k = k_end;
+  // Some query frame segment and some key frame segment retained (Eq. 6) and
+  // within w(t) of each other (Eq. 7; the interval distance
+  // max(0, v_lo - u_hi, u_lo - v_hi) decides it) is necessary for any token
+  // pair, and with both thresholds at 0 it is also sufficient.
+  bool near = false;
+  for (int s = q0; s < q1 && !near;) {
+    const int fq = s / p.Nt;
+    const int s_end = min(q1, (fq + 1) * p.Nt);
+    const int ulo = s - fq * p.Nt, uhi = s_end - 1 - fq * p.Nt;
+    for (int k = k0; k < k1;) {
+      const int fk = k / p.Nt;
+      const int k_end = min(k1, (fk + 1) * p.Nt);
+      const int vlo = k - fk * p.Nt, vhi = k_end - 1 - fk * p.Nt;
+      const int t = fq > fk ? fq - fk : fk - fq;
+      if (t % s_sf[t] == 0 && max(0, max(vlo - uhi, ulo - vhi)) <= s_w[t]) {
+        near = true;
+        break;
       }
-      s = s_end;
+      k = k_end;
     }
-    return false;
+    s = s_end;
   }
-  const double nq = (double)(q1 - q0), nk = (double)(k1 - k0);
+  if (!near || (p.theta_c == 0.0 && p.theta_m == 0.0)) return near;
+  // the shares count / n_q > theta_c and active / n_k > theta_m as integer
+  // thresholds (min_count: exact, a correctly rounded quotient being monotone)
+  const int thr_c = s_thr[0];
+  const int thr_m = k1 - k0 == p.Bs ? s_thr[1] : s_thr[2];
   int active = 0;
-  for (int k = k0; k < k1; ++k) {
-    const int fk = k / p.Nt;
-    const int uk = k - fk * p.Nt;
+  if (q0 / p.Nt == (q1 - 1) / p.Nt) {
+    // One query frame segment [u_lo, u_hi]: within a key frame segment the
+    // count of column u_k is |[u_lo, u_hi] n [u_k - w, u_k + w]|, which is at
+    // least c iff c <= n_q, c <= 2w + 1, u_k >= u_lo + c - 1 - w and
+    // u_k <= u_hi - c + 1 + w, so the active columns form one interval.
+    const int fq = q0 / p.Nt;
+    const int ulo = q0 - fq * p.Nt, uhi = q1 - 1 - fq * p.Nt;
+    const int nq = q1 - q0;
+    for (int k = k0; k < k1;) {
+      const int fk2 = k / p.Nt;
+      const int k_end = min(k1, (fk2 + 1) * p.Nt);
+      const int vlo = k - fk2 * p.Nt, vhi = k_end - 1 - fk2 * p.Nt;
+      const int t = fq > fk2 ? fq - fk2 : fk2 - fq;
+      const int w = s_w[t];
+      if (t % s_sf[t] == 0 && thr_c <= nq && thr_c <= 2 * w + 1) {
+        const int lo = max(vlo, ulo + thr_c - 1 - w), hi = min(vhi, uhi - thr_c + 1 + w);
+        if (hi >= lo) active += hi - lo + 1;
+      }
+      k = k_end;
+    }
+    return active >= thr_m;
+  }
+  int fk = k0 / p.Nt, uk = k0 - fk * p.Nt;
+  for (int k = k0; k < k1; ++k, ++uk) {
+    if (uk == p.Nt) {
+      ++fk;
+      uk = 0;
+    }
     int cnt = 0;
     for (int s = q0; s < q1;) {
       const int fq = s / p.Nt;
@@ -75,12 +105,21 @@ __device__ bool is_candidate(int a, int b, const CandParams& p, const int* s_w, 
       }
       s = seg_end;
     }
-    if ((double)cnt / nq > p.theta_c) {
-      ++active;
-      if ((double)active / nk > p.theta_m) return true;
-    }
+    if (cnt >= thr_c && ++active >= thr_m) return true;
+    if (active + (k1 - 1 - k) < thr_m) return false;   // the remaining columns cannot reach it
   }
   return false;
+}
+
+// Integer thresholds of the density control for this query block: [0] the
+// active-column count for its n_q queries, [1] the candidate test for a full
+// key block, [2] for the last (possibly ragged) key block.
+__device__ void build_thresholds(const CandParams& p, int a, int* s_thr) {
+  const int nq = min(p.Bs, p.S - a * p.Bs);
+  const int nk_last = p.S - (p.Sb - 1) * p.Bs;
+  if (threadIdx.x == 0) s_thr[0] = min_count(nq, p.theta_c);
+  if (threadIdx.x == 1) s_thr[1] = min_count(p.Bs, p.theta_m);
+  if (threadIdx.x == 2) s_thr[2] = min_count(nk_last, p.theta_m);
 }
 
 __global__ __launch_bounds__(kCandThreads) void cand_count_kernel(CandParams p, int32_t* row_ptr) {
@@ -88,11 +127,13 @@ __global__ __launch_bounds__(kCandThreads) void cand_count_kernel(CandParams p, 
   int* s_w = s_tab;
   int* s_sf = s_tab + p.Nf;
   __shared__ int s_part[kCandThreads / 64];
-  build_table(p, s_w, s_sf);
-  __syncthreads();
+  __shared__ int s_thr[3];
   const int a = blockIdx.x;
+  build_table(p, s_w, s_sf);
+  build_thresholds(p, a, s_thr);
+  __syncthreads();
   int cnt = 0;
-  for (int b = threadIdx.x; b < p.Sb; b += kCandThreads) cnt += is_candidate(a, b, p, s_w, s_sf) ? 1 : 0;
+  for (int b = threadIdx.x; b < p.Sb; b += kCandThreads) cnt += is_candidate(a, b, p, s_w, s_sf, s_thr) ? 1 : 0;
   for (int off = 32; off > 0; off >>= 1) cnt += __shfl_xor(cnt, off);
   if ((threadIdx.x & 63) == 0) s_part[threadIdx.x >> 6] = cnt;
   __syncthreads();
@@ -134,14 +175,16 @@ __global__ __launch_bounds__(kCandThreads) void cand_fill_kernel(CandParams p, c
   int* s_w = s_tab;
   int* s_sf = s_tab + p.Nf;
   __shared__ int s_wave[kCandThreads / 64];
-  build_table(p, s_w, s_sf);
-  __syncthreads();
+  __shared__ int s_thr[3];
   const int a = blockIdx.x;
+  build_table(p, s_w, s_sf);
+  build_thresholds(p, a, s_thr);
+  __syncthreads();
   const int wave = threadIdx.x >> 6;
   long long base = row_ptr[a];
   for (int b0 = 0; b0 < p.Sb; b0 += kCandThreads) {
     const int b = b0 + (int)threadIdx.x;
-    const bool flag = b < p.Sb && is_candidate(a, b, p, s_w, s_sf);
+    const bool flag = b < p.Sb && is_candidate(a, b, p, s_w, s_sf, s_thr);
     const unsigned long long m = __ballot(flag);
     const int before = __builtin_amdgcn_mbcnt_hi((unsigned)(m >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)m, 0));
     if ((threadIdx.x & 63) == 0) s_wave[wave] = __popcll(m);
