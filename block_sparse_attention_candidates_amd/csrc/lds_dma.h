@@ -14,7 +14,10 @@ namespace dr {
 // on these loads themselves with explicit s_waitcnt vmcnt. The asm has no
 // output register and the address registers are read at issue; one wait state
 // separates the M0 write from the load that reads it (the compiler cannot see
-// inside the asm to insert it).
+// inside the asm to insert it). M0 is a reserved register: naming it as
+// clobbered does not make the compiler save it, so this is sound only while no
+// compiler-generated instruction of the calling kernels uses M0 (hipcc warns
+// about the clobber; the codegen test checks the generated code for it).
 __device__ inline void dma16(const void* gptr, unsigned char* lds_wave_base) {
   const unsigned m0 = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)lds_wave_base);
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0), "v"(gptr) : "memory", "m0");
