@@ -5,7 +5,9 @@
 //
 // Workgroup = 8 compute wavefronts + 4 loader wavefronts, 256 query rows of
 // one (b, h). Each compute wavefront owns 32 query rows (one 32x32 MFMA tile);
-// in sparse mode those rows are 256 / B_s query blocks.
+// in sparse mode those rows are 256 / B_s query blocks. Sparse workgroups are
+// remapped so that runs of 8 neighbouring query groups of a head execute
+// together on one XCD, where the KV blocks their unions share hit in its L2.
 //
 // Setup (the only workgroup barriers): the kept lists of the workgroup's
 // query blocks are ORed into per-block LDS bitmaps; their union is the
@@ -63,6 +65,10 @@ constexpr int kLoaders = 4;
 constexpr int kThreads = (kConsumers + kLoaders) * 64;
 constexpr int kRows = kConsumers * 32;       // query rows per workgroup
 constexpr int kInflight = 1;                 // units in flight per loader
+// Sparse work items per XCD run (see xcd_chunked): 8 measured best (wan14b_720p
+// static 11.11 -> 10.78 ms, dynamic 38.8 -> 37.5 ms; 16: 10.88 / 37.96; 32:
+// 11.65 / 40.9; one contiguous range per XCD was slower still)
+constexpr int kXcdRun = 8;
 constexpr int kMaxSlots = 16;                // ring depth limit, in 32-key units
 constexpr int kLdsBytes = 160 * 1024;        // LDS per workgroup on gfx950
 static_assert(kConsumers == 8, "the loaders read the 8 progress entries as two int4");
@@ -129,8 +135,15 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
   unsigned int* bits = reinterpret_cast<unsigned int*>(smem + G::RING + sizeof(Shared));
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int bh = blockIdx.y;
-  const int row0 = blockIdx.x * kRows;
+  // work item: (query group gx, head bh). Sparse: runs of kXcdRun neighbouring
+  // groups, whose unions share most KV blocks, run together on one XCD (one L2)
+  int gx = blockIdx.x, bh = blockIdx.y;
+  if constexpr (SPARSE) {
+    const int w = xcd_chunked(blockIdx.y * gridDim.x + blockIdx.x, gridDim.x * gridDim.y, kXcdRun);
+    gx = w % gridDim.x;
+    bh = w / gridDim.x;
+  }
+  const int row0 = gx * kRows;
   const size_t base = (size_t)bh * p.S * D;
   // query block of group slot s (sparse: per-(b, h) grouping mode)
   int gmode = 0;
@@ -139,10 +152,10 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
       gmode = p.group_mode[bh];
       if (gmode < 0 || gmode >= kGroupModes || group_count(p.grp, gmode) == 0) gmode = 0;
     }
-    if ((int)blockIdx.x >= group_count(p.grp, gmode)) return;   // uniform: before any barrier
+    if (gx >= group_count(p.grp, gmode)) return;   // uniform: before any barrier
   }
   auto qblock = [&](int s) -> int {
-    if constexpr (SPARSE) return group_block(p.grp, gmode, blockIdx.x, s);
+    if constexpr (SPARSE) return group_block(p.grp, gmode, gx, s);
     else return row0 / BS + s;
   };
   const int nword = (p.Sb + 31) >> 5;

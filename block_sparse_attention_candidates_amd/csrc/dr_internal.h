@@ -70,6 +70,17 @@ __device__ inline int xcd_contiguous(int L, int n) {
   return x < r ? x * (q + 1) + i : r * (q + 1) + (x - r) * q + i;
 }
 
+// The same dispatch order mapped so that runs of C consecutive work items land
+// on one XCD at about the same time, while successive runs go to successive
+// XCDs (so every XCD still sweeps the whole range, in step with the others).
+// Work items past the last full round of kXcds * C runs keep their index.
+__device__ inline int xcd_chunked(int L, int n, int C) {
+  const int round = kXcds * C;
+  if (L >= n / round * round) return L;
+  const int x = L % kXcds, i = L / kXcds;
+  return ((i / C) * kXcds + x) * C + i % C;
+}
+
 struct CandParams {
   int Nf, Nt, Bs, S, Sb, L0;
   double gamma, lambda, theta_c, theta_m;
