@@ -9,7 +9,7 @@
 attention kernel, scales it by what the same counter reads for the 1 GiB
 elementwise copy in the same run (1 GiB read, 1 GiB written), and records
 the result in profiles/sparse_attn_traffic.json under "<workload>/<mode>",
-together with the SHA-256 of attention.hip it was taken on.
+together with the SHA-256 of the attention kernel's sources it was taken on.
 """
 from __future__ import annotations
 
