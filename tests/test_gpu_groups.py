@@ -135,3 +135,29 @@ def test_grouping_choice_full_size_static():
         full = [sum(len(np.unique(np.concatenate([lists[a] for a in g if a >= 0]))) for g in t if (g >= 0).any())
                 for t in tables]
         G.log(f"   head {h}: sampled union totals {tot[0].tolist()}, full {full} -> mode {got[h]}")
+
+
+@pytest.mark.parametrize("name,mode,ratio,tau", [("wan14b_720p", "static", 0.15, 1.0),
+                                                 ("wan14b_720p", "dynamic", 1.0, 0.8)])
+def test_every_output_row_written(name, mode, ratio, tau):
+    """Output pre-filled with NaN: at the benchmark's launch sizes every row of
+    every head is written (by the workgroup that owns its query block) under
+    each grouping mode and the kernel's remapping of workgroups to XCDs; the
+    dense kernel likewise."""
+    import torch
+    G.log(f"[groups] every row written: {name} {mode}")
+    w = workloads.get_workload(name)
+    q, k, v = G.device_qkv(name)
+    cand = G.candidates(name)
+    kept = G.dr().score_select(q, k, cand, mode=mode, ratio=ratio, tau=tau)
+    for m in (None, 0, 1, 2):
+        groups = None if m is None else torch.full((w.batch * w.heads,), m, dtype=torch.int32, device="cuda")
+        out = torch.full_like(q, float("nan"))
+        G.dr().sparse_attn(q, k, v, cand, kept, out=out, groups=groups)
+        torch.cuda.synchronize()
+        assert not torch.isnan(out).any().item(), f"rows left unwritten with grouping {m}"
+    if mode == "static":
+        out = torch.full_like(q, float("nan"))
+        G.dr().attn(q, k, v, out=out)
+        torch.cuda.synchronize()
+        assert not torch.isnan(out).any().item(), "dense: rows left unwritten"
