@@ -557,11 +557,14 @@ def token_select_decisive(q_heads, k_heads, blocks, num_frames: int, tokens_per_
                           eps: float = EPS_NORM, scale: float = None, stats: dict = None,
                           top2: dict = None) -> List[np.ndarray]:
     """For each given query block, a bool per key block: True where no
-    token-level decision of the block pair can flip under a perturbation of
-    every z below `margin` and of every score below `margin` * sigma. Unsure
-    are pairs of P (t > 1) within `margin` of their threshold, and every pair of
-    a frame pair whose fallback is in doubt (its highest z within `margin` of
-    tau, or a runner-up score within `margin` * sigma of the highest)."""
+    token-level decision of the block pair can flip when every z moves by less
+    than `margin` and every score by less than `margin` * (sigma + eps) / 2
+    (two scores then keep their order unless they are within `margin` *
+    (sigma + eps) of each other). Unsure are pairs of P (t > 1) within `margin`
+    of their threshold, and every pair of a frame pair whose fallback is in
+    doubt (its highest z within `margin` of tau, or no pair passing and a
+    runner-up score within `margin` * (sigma + eps) of the highest). Pinned by
+    hand-worked cases and by brute-force perturbation of tiny layouts."""
     q_heads, k_heads = _fused(q_heads), _fused(k_heads)
     scale = 1.0 / math.sqrt(q_heads[0].shape[1]) if scale is None else scale
     if stats is None:
@@ -621,7 +624,7 @@ def token_select_decisive(q_heads, k_heads, blocks, num_frames: int, tokens_per_
 #     uniformly, rho = rho_1 if L(t) >= B_s (near) else rho_2 (far). The
 #     selected pairs are aggregated to blocks as in steps 3 and 10.
 #
-#     Reading of "uniformly sample ... using a deterministic seed" (the pages
+#     Reading of the uniform sampling under a fixed seed (the pages
 #     name no generator): pair (u, v) of P(i, j) gets the 32-bit word number
 #     (v mod 4) of Philox4x32-10 applied to the counter (u, floor(v / 4), i, j)
 #     under the key (seed mod 2^32, seed div 2^32); the k pairs with the

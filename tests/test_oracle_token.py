@@ -142,3 +142,155 @@ def test_rows_subset_matches_full():
     part = O.token_select_rows(q, k, [3, 7, 14], Nf, Nt, Bs, 1.2, 0.5, -0.5, 1.5, 0.3, 0.4)
     for a, ks in zip([3, 7, 14], part):
         np.testing.assert_array_equal(ks, full[a])
+
+
+# ---------------------------------------------------------------------------
+# token_select_decisive: which block pairs the GPU comparison may hold to
+# bit-exactness. A block pair is decisive iff no token-level decision in it can
+# change when every z moves by less than the margin and every score by less
+# than half the margin times (sigma + eps).
+# ---------------------------------------------------------------------------
+
+def _unsure_pairs(dec, blocks):
+    return {(a, b) for a, row in zip(blocks, dec) for b in np.nonzero(~row)[0]}
+
+
+def test_decisive_hand_case():
+    """The hand case above (frame pair (0, 2): z(u) = (u - 1.5) / sigma with
+    sigma = sqrt(47/14 - 2.25) = 1.0522, so z = -1.426, -0.475, 0.475, 1.426;
+    tau_far = 0.5). B_s = 2: query block 1 holds u = 2, 3 and key blocks 4, 5
+    frame 2. |z(2) - tau| = 0.0248: within a margin of 0.03, outside 0.02.
+    Frame pair (2, 0) has sigma = 0, every score 0 and z = 0 < tau: its
+    fallback's arg-max is a tie (top two scores equal), so every pair of
+    P(2, 0) (query blocks 4, 5 against key blocks 0, 1) is unsure at any margin.
+    Pairs with t <= 1 are never unsure."""
+    q, k = _hand_case()
+    args = (3, 4, 2, 1.0, 4.0, 100.0, 0.5)
+    tie = {(4, 0), (4, 1), (5, 0), (5, 1)}
+    dec = O.token_select_decisive(q, k, range(6), *args, margin=0.03, scale=1.0)
+    assert _unsure_pairs(dec, range(6)) == tie | {(1, 4), (1, 5)}
+    dec = O.token_select_decisive(q, k, range(6), *args, margin=0.02, scale=1.0)
+    assert _unsure_pairs(dec, range(6)) == tie
+
+
+def _two_frame_pair_case(top, rest, tau):
+    """N_f = 3, N_t = 4, B_s = 4 (one block per frame), D = 1, scale 1:
+    frame 0's queries are (1, 0.1, 0.2, 0.3) and frame 2's keys (top, rest...),
+    so P(0, 2) (|u - v| <= 4: all 16 pairs) has s(u, v) = q_u k_v with the
+    highest score `top` at (0, 0) and the runner-up rest[0] at (0, 1) (for
+    top > rest[0] > 0.3 top). Frames 1 and 2 have zero queries."""
+    q = np.zeros((12, 1))
+    k = np.zeros((12, 1))
+    q[0:4, 0] = [1.0, 0.1, 0.2, 0.3]
+    k[8:12, 0] = [top] + list(rest)
+    return [q], [k], (3, 4, 4, 1.0, 4.0, 100.0, tau)
+
+
+def test_decisive_fallback_near_tie_and_max_near_tau():
+    """Frame pair (0, 2) is judged as a whole: it is in doubt when no pair
+    passes and the runner-up score is within margin * (sigma + eps) of the
+    highest (the fallback's arg-max could move), or when the highest z lies
+    within the margin of tau (whether the fallback acts could change). Block
+    pair (0, 2) holds all of P(0, 2) here."""
+    m = 1e-3
+    # runner-up 0.9999: no pair reaches tau = 3 and the top two are 1e-4 apart
+    q, k, args = _two_frame_pair_case(1.0, [1.0 - 1e-4, -1.0, -1.0], tau=3.0)
+    st = O.token_frame_stats(q, k, *args[:5], 100.0, 3.0, scale=1.0)
+    mu, sigma, tau, fb = st[(0, 2)]
+    assert (1.0 - mu) / sigma < tau and 1e-4 <= m * sigma       # no pair passes; a near tie
+    assert (0, 2) in _unsure_pairs(O.token_select_decisive(q, k, [0], *args, margin=m, scale=1.0), [0])
+    # the same scores with a clear gap between the top two: decisive
+    q, k, args = _two_frame_pair_case(1.0, [0.5, -1.0, -1.0], tau=3.0)
+    assert not _unsure_pairs(O.token_select_decisive(q, k, [0], *args, margin=m, scale=1.0), [0])
+    # the clear gap again, with tau just above the highest z: in doubt
+    q, k, args = _two_frame_pair_case(1.0, [0.5, -1.0, -1.0], tau=0.0)
+    mu, sigma, _, _ = O.token_frame_stats(q, k, *args[:5], 100.0, 0.0, scale=1.0)[(0, 2)]
+    zmax = (1.0 - mu) / (sigma + O.EPS_NORM)
+    q, k, args = _two_frame_pair_case(1.0, [0.5, -1.0, -1.0], tau=zmax + 0.5 * m)
+    assert (0, 2) in _unsure_pairs(O.token_select_decisive(q, k, [0], *args, margin=m, scale=1.0), [0])
+    q, k, args = _two_frame_pair_case(1.0, [0.5, -1.0, -1.0], tau=zmax + 2 * m)
+    assert not _unsure_pairs(O.token_select_decisive(q, k, [0], *args, margin=m, scale=1.0), [0])
+
+
+def _perturbed_selection(s, Nf, Nt, Bs, gamma, lam, stats, dz, ds, theta_c, theta_m, eps):
+    """Token decisions from the definitions, written out here: for each frame
+    pair (i, j) with t = |i - j|, retained iff t mod sf(t) == 0, P = {|u - v|
+    <= w(t)}; t <= 1 selects all of P; t > 1 selects z + dz >= tau on P, and if
+    none passes, the first (u, v) of highest s + ds on P. Aggregated to blocks
+    by the oracle's pinned density control."""
+    w, sf = O.distance_table(Nf, Nt, Bs, gamma, lam)
+    S = Nf * Nt
+    sel = np.zeros((S, S), dtype=bool)
+    uu = np.arange(Nt)
+    for i in range(Nf):
+        for j in range(Nf):
+            t = abs(i - j)
+            if t % sf[t] != 0:
+                continue
+            P = np.abs(uu[:, None] - uu[None, :]) <= w[t]
+            blk = (slice(i * Nt, (i + 1) * Nt), slice(j * Nt, (j + 1) * Nt))
+            if t <= 1:
+                sel[blk] = P
+                continue
+            mu, sigma, tau, _ = stats[(i, j)]
+            z = (s[blk] - mu) / (sigma + eps) + dz[blk]
+            pick = P & (z >= tau)
+            if not pick.any():
+                sp = np.where(P, s[blk] + ds[blk], -np.inf)
+                u, v = divmod(int(np.argmax(sp)), Nt)      # first in (u, v) order
+                pick[u, v] = True
+            sel[blk] = pick
+    S_b = -(-S // Bs)
+    return [O.aggregate_block_rows(sel[a * Bs:min((a + 1) * Bs, S)], a * Bs, Bs, S, theta_c, theta_m)[0]
+            for a in range(S_b)], sel
+
+
+@pytest.mark.parametrize("seed,taus,theta", [(1, (0.3, 0.9), (0.0, 0.0)), (2, (-0.2, 1.4), (0.2, 0.3)),
+                                             (3, (1.8, 2.6), (0.0, 0.0)), (4, (0.0, 0.0), (0.3, 0.5))])
+def test_decisive_pairs_survive_bounded_perturbations(seed, taus, theta):
+    """Brute force on a tiny layout (4 frames x 12 tokens, B_s = 4, D = 3,
+    H_f = 2; every distance retained, windows of 4 at t = 2, 3): under random
+    perturbations of every z by less than the margin and of every score by
+    less than margin * (sigma + eps) / 2, and under the worst case that moves
+    every z the margin's width towards its threshold, no decisive block pair
+    changes. Scores here come from a plain matmul, not the oracle's code."""
+    rng = np.random.default_rng(seed)
+    Nf, Nt, Bs, D, gamma, lam, margin = 4, 12, 4, 3, 1.0, 2.0, 0.05
+    eps = O.EPS_NORM
+    q, k = _heads(rng, Nf * Nt, D)
+    s = sum(qh @ kh.T for qh, kh in zip(q, k)) / 2 / math.sqrt(D)
+    stats = O.token_frame_stats(q, k, Nf, Nt, Bs, gamma, lam, taus[0], taus[1], eps)
+    S_b = Nf * Nt // Bs
+    dec = O.token_select_decisive(q, k, range(S_b), Nf, Nt, Bs, gamma, lam, taus[0], taus[1], margin, eps)
+    base = O.token_select(q, k, Nf, Nt, Bs, gamma, lam, taus[0], taus[1], theta[0], theta[1], eps)
+    n_dec = sum(int(d.sum()) for d in dec)
+    assert 0 < n_dec < S_b * S_b                  # both kinds occur
+    # the plain re-derivation agrees with the oracle when nothing moves
+    zero = np.zeros_like(s)
+    blocks0, sel0 = _perturbed_selection(s, Nf, Nt, Bs, gamma, lam, stats, zero, zero, *theta, eps)
+    for a, ks in enumerate(blocks0):
+        np.testing.assert_array_equal(ks, base[a])
+    sig = np.zeros_like(s)
+    tau_of = np.zeros_like(s)
+    for (i, j), (mu, sigma, tau, _) in stats.items():
+        sig[i * Nt:(i + 1) * Nt, j * Nt:(j + 1) * Nt] = sigma + eps
+        tau_of[i * Nt:(i + 1) * Nt, j * Nt:(j + 1) * Nt] = tau
+    mu_of = np.zeros_like(s)
+    for (i, j), (mu, sigma, tau, _) in stats.items():
+        mu_of[i * Nt:(i + 1) * Nt, j * Nt:(j + 1) * Nt] = mu
+    z = np.where(sig > 0, (s - mu_of) / np.where(sig > 0, sig, 1.0), 0.0)
+    trials = [(rng.uniform(-0.999, 0.999, s.shape) * margin, rng.uniform(-0.499, 0.499, s.shape) * margin * sig)
+              for _ in range(40)]
+    toward = -0.999 * margin * np.sign(z - tau_of)
+    trials += [(toward, zero), (-toward, zero), (toward, 0.499 * margin * sig), (toward, -0.499 * margin * sig)]
+    flipped = 0
+    for dz, ds in trials:
+        got, sel = _perturbed_selection(s, Nf, Nt, Bs, gamma, lam, stats, dz, ds, *theta, eps)
+        flipped += int((sel != sel0).sum())
+        for a in range(S_b):
+            gm = np.zeros(S_b, dtype=bool)
+            gm[got[a]] = True
+            bm = np.zeros(S_b, dtype=bool)
+            bm[base[a]] = True
+            assert not (dec[a] & (gm != bm)).any(), (a, np.nonzero(dec[a] & (gm != bm))[0])
+    assert flipped > 0                            # the perturbations do move token decisions
