@@ -28,7 +28,7 @@ from ._lib import Dims, DynradError, RadialCfg, SelectCfg, check, lib
 
 __all__ = ["radial_cfg", "num_blocks", "distance_table", "Candidates", "Kept", "build_candidates",
            "score_select", "token_select", "static_select", "query_groups", "group_table", "sparse_attn", "attn",
-           "proxy_error", "proxy_loss", "DynradError", "kept_from_lists"]
+           "proxy_error", "proxy_loss", "DynradError", "kept_from_lists", "wait_report", "set_wait_limit"]
 
 
 def radial_cfg(num_frames: int, tokens_per_frame: int, block_size: int, gamma: float, lam: float,
@@ -299,15 +299,41 @@ def proxy_error(o_ref, o_test, kept: Optional[Kept] = None, workspace=None):
     return a, b, c
 
 
-def proxy_loss(q, k, z, cand: Candidates, kept: Kept, alpha: float = 10.0, target: float = 0.8) -> dict:
+def proxy_loss(q, k, z, cand: Candidates, kept: Kept, alpha: float = 10.0, target: float = 0.8,
+               workspace=None) -> dict:
     """The proxy-task objective of [DR] App. C.4 Eq. 22 for one mask, through
-    the probe z: dense and kept-block attention of (q, k, z), the normalised
-    error of the outputs, the sparsity of the mask and the penalised loss."""
+    the probe z: dense and kept-block attention of (q, k, z), then
+    dr_proxy_loss forms the normalised error of the outputs, the sparsity of
+    the mask and the penalised loss (synchronises to read them)."""
+    torch = _torch()
     o_ref = attn(q, k, z)
     o_test = sparse_attn(q, k, z, cand, kept, groups="auto")
-    num, den, n_kept = proxy_error(o_ref, o_test, kept)
+    dev = q.device
     B, H = int(q.shape[0]), int(q.shape[1])
-    sparsity = 1.0 - n_kept / float(B * H * cand.num_blocks ** 2)
-    nmse = num / den
-    return {"nmse": nmse, "sparsity": sparsity, "loss": nmse + alpha * max(0.0, target - sparsity),
-            "err_sum": num, "ref_sum": den, "kept_blocks": int(n_kept)}
+    out = torch.empty(6, dtype=torch.float64, device=dev)
+    if workspace is None or workspace.numel() < _L.PROXY_WS_BYTES:
+        workspace = torch.empty(_L.PROXY_WS_BYTES, dtype=torch.uint8, device=dev)
+    cnt = kept.kept_cnt
+    check(lib().dr_proxy_loss(o_ref.data_ptr(), o_test.data_ptr(), o_ref.numel(), cnt.data_ptr(), cnt.numel(),
+                              B * H * cand.num_blocks ** 2, float(alpha), float(target), out.data_ptr(),
+                              workspace.data_ptr(), workspace.numel(), _stream(dev)))
+    num, den, n_kept, nmse, sparsity, loss = out.cpu().tolist()
+    return {"nmse": nmse, "sparsity": sparsity, "loss": loss, "err_sum": num, "ref_sum": den,
+            "kept_blocks": int(n_kept)}
+
+
+def wait_report(device=None) -> int:
+    """dr_wait_report on the current stream of `device`: synchronises, reads
+    and clears the device's flags of bounded waits that gave up; raises
+    DynradError (status DR_ERR_WAIT) if any was set, else returns 0."""
+    torch = _torch()
+    dev = torch.device("cuda") if device is None else torch.device(device)
+    flags = ctypes.c_uint32(0)
+    check(lib().dr_wait_report(_stream(dev), ctypes.byref(flags)))
+    return int(flags.value)
+
+
+def set_wait_limit(polls: int) -> None:
+    """dr_set_wait_limit: polls after which every later bounded wait gives up
+    (0 restores the default). Only tests of wait_report lower it."""
+    check(lib().dr_set_wait_limit(int(polls)))

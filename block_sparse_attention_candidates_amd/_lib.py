@@ -11,7 +11,8 @@ import os
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libdynrad.so")
 
-DR_OK, DR_ERR_INVALID_ARG, DR_ERR_UNSUPPORTED, DR_ERR_CAPACITY, DR_ERR_HIP = range(5)
+DR_OK, DR_ERR_INVALID_ARG, DR_ERR_UNSUPPORTED, DR_ERR_CAPACITY, DR_ERR_HIP, DR_ERR_WAIT = range(6)
+WAIT_ATTN_LOADER, WAIT_ATTN_COMPUTE, WAIT_TOKEN = 1, 2, 4
 DR_STATIC_RATIO, DR_DYNAMIC_THRESHOLD = 0, 1
 
 
@@ -80,6 +81,10 @@ def lib() -> ctypes.CDLL:
                                        c_void_p, c_void_p, c_size_t, c_void_p]),
         "dr_proxy_error": (c_int32, [c_void_p, c_void_p, c_int64, c_void_p, c_int64, c_void_p, c_void_p, c_size_t,
                                      c_void_p]),
+        "dr_proxy_loss": (c_int32, [c_void_p, c_void_p, c_int64, c_void_p, c_int64, c_int64, ctypes.c_double,
+                                    ctypes.c_double, c_void_p, c_void_p, c_size_t, c_void_p]),
+        "dr_wait_report": (c_int32, [c_void_p, P(ctypes.c_uint32)]),
+        "dr_set_wait_limit": (c_int32, [c_int64]),
         "dr_sparse_attn": (c_int32, [P(Dims), P(RadialCfg), c_void_p, c_void_p, c_void_p, c_void_p, c_int64,
                                      c_void_p, c_void_p, c_float, c_void_p, c_void_p]),
         "dr_sparse_attn_grouped": (c_int32, [P(Dims), P(RadialCfg), c_void_p, c_void_p, c_void_p, c_void_p, c_int64,

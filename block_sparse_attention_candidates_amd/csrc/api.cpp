@@ -6,6 +6,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <atomic>
 #include <string>
 
 #include "../../include/dynrad.h"
@@ -14,6 +15,9 @@
 namespace {
 
 thread_local std::string g_last_error;
+
+// Polls before a bounded wait of the ring kernels gives up (dr_set_wait_limit).
+std::atomic<int> g_wait_limit{dr::kDefaultSpinLimit};
 
 dr_status fail(dr_status st, const char* fmt, ...) {
   char buf[512];
@@ -330,6 +334,7 @@ static dr_status attn_common(const dr_dims* dims, long long S, const void* q, co
   p->group_mode = nullptr;
   p->grp = dr::QGroup{};
   p->scale_log2 = scale * 1.4426950408889634f;
+  p->spin_limit = g_wait_limit.load(std::memory_order_relaxed);
   return DR_OK;
 }
 
@@ -386,6 +391,7 @@ dr_status dr_token_select(const dr_dims* dims, const dr_radial_cfg* cfg, const d
   p.tau_far = tok->tau_far;
   p.eps = tok->eps;
   p.scale = (float)(1.0 / (sqrt((double)dims->head_dim) * (double)tok->fused_heads));
+  p.spin_limit = g_wait_limit.load(std::memory_order_relaxed);
   p.part = reinterpret_cast<dr::TokStat*>(wsb + w.part);
   p.thr = reinterpret_cast<float*>(wsb + w.thr);
   p.fmax = reinterpret_cast<unsigned long long*>(wsb + w.fmax);
@@ -487,8 +493,9 @@ dr_status dr_static_select(const dr_dims* dims, const dr_radial_cfg* cfg, const 
   return ok();
 }
 
-dr_status dr_proxy_error(const void* o_ref, const void* o_test, int64_t n, const int32_t* kept_cnt, int64_t n_cnt,
-                         double* out, void* ws, size_t ws_bytes, hipStream_t stream) {
+static dr_status proxy_impl(const void* o_ref, const void* o_test, int64_t n, const int32_t* kept_cnt, int64_t n_cnt,
+                            bool with_loss, int64_t total_blocks, double alpha, double target, double* out, void* ws,
+                            size_t ws_bytes, hipStream_t stream) {
   if (!o_ref || !o_test || !out || !ws) return fail(DR_ERR_INVALID_ARG, "o_ref, o_test, out and ws must be non-NULL");
   if (n < 1) return fail(DR_ERR_INVALID_ARG, "n must be >= 1");
   if (n_cnt < 0 || (n_cnt > 0 && !kept_cnt)) return fail(DR_ERR_INVALID_ARG, "n_cnt must be >= 0 (0 when kept_cnt is NULL)");
@@ -505,8 +512,46 @@ dr_status dr_proxy_error(const void* o_ref, const void* o_test, int64_t n, const
   p.n_cnt = kept_cnt ? n_cnt : 0;
   p.partial = static_cast<double*>(ws);
   p.out = out;
+  p.with_loss = with_loss ? 1 : 0;
+  p.total_blocks = total_blocks;
+  p.alpha = alpha;
+  p.target = target;
   const hipError_t e = dr::launch_proxy_error(p, stream);
   if (e != hipSuccess) return hip_fail(e, "proxy error kernels");
+  return ok();
+}
+
+dr_status dr_proxy_error(const void* o_ref, const void* o_test, int64_t n, const int32_t* kept_cnt, int64_t n_cnt,
+                         double* out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return proxy_impl(o_ref, o_test, n, kept_cnt, n_cnt, false, 0, 0.0, 0.0, out, ws, ws_bytes, stream);
+}
+
+dr_status dr_proxy_loss(const void* o_ref, const void* o_test, int64_t n, const int32_t* kept_cnt, int64_t n_cnt,
+                        int64_t total_blocks, double alpha, double target, double* out, void* ws, size_t ws_bytes,
+                        hipStream_t stream) {
+  if (total_blocks < 1) return fail(DR_ERR_INVALID_ARG, "total_blocks must be >= 1");
+  if (!isfinite(alpha) || alpha < 0.0) return fail(DR_ERR_INVALID_ARG, "alpha must be finite and >= 0");
+  if (!isfinite(target)) return fail(DR_ERR_INVALID_ARG, "target must be finite");
+  return proxy_impl(o_ref, o_test, n, kept_cnt, n_cnt, true, total_blocks, alpha, target, out, ws, ws_bytes, stream);
+}
+
+dr_status dr_set_wait_limit(int64_t polls) {
+  if (polls < 0 || polls > (int64_t)0x7fffffff) return fail(DR_ERR_INVALID_ARG, "polls must be in [0, 2^31)");
+  g_wait_limit.store(polls == 0 ? dr::kDefaultSpinLimit : (int)polls, std::memory_order_relaxed);
+  return ok();
+}
+
+dr_status dr_wait_report(hipStream_t stream, uint32_t* flags) {
+  if (!flags) return fail(DR_ERR_INVALID_ARG, "flags is NULL");
+  unsigned a = 0, t = 0;
+  hipError_t e = dr::take_wait_flags_attn(&a, stream);
+  if (e != hipSuccess) return hip_fail(e, "reading the attention wait flags");
+  e = dr::take_wait_flags_token(&t, stream);
+  if (e != hipSuccess) return hip_fail(e, "reading the token-selection wait flags");
+  *flags = a | t;
+  if (*flags)
+    return fail(DR_ERR_WAIT, "a bounded wait gave up (flags 0x%x): outputs of the ring kernels since the last report "
+                             "are not valid", *flags);
   return ok();
 }
 
@@ -631,6 +676,7 @@ const char* dr_status_string(dr_status s) {
     case DR_ERR_UNSUPPORTED: return "unsupported configuration";
     case DR_ERR_CAPACITY: return "insufficient capacity";
     case DR_ERR_HIP: return "HIP error";
+    case DR_ERR_WAIT: return "bounded wait gave up";
   }
   return "unknown status";
 }

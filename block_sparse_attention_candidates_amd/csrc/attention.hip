@@ -21,7 +21,9 @@
 // loader refills a slot only after every compute wavefront has moved past the
 // unit it held. Compute wavefronts therefore run out of phase with each other,
 // and the two on a SIMD overlap one's MFMA with the other's softmax. Waits are
-// bounded (a wave gives up after ~2^26 polls; the protocol never needs that).
+// bounded (a wave gives up after p.spin_limit polls, 2^26 by default; the
+// protocol never needs that) and a wave that gives up sets a bit of
+// g_attn_wait_flags, which the host reads back (take_wait_flags_attn).
 //
 // Per compute wavefront and 32-key unit (v_mfma_f32_32x32x16_bf16):
 //   S^T = K Q^T : A = K rows read from LDS (16 B per lane), B = the wave's Q
@@ -74,7 +76,6 @@ constexpr int kLdsBytes = 160 * 1024;        // LDS per workgroup on gfx950
 static_assert(kConsumers == 8, "the loaders read the 8 progress entries as two int4");
 constexpr int kUnit = 32;
 constexpr float kRescaleLog2 = 8.0f;         // rescale only past 2^8 growth
-constexpr int kSpinLimit = 1 << 26;
 constexpr int kDone = 0x3fffffff;
 
 template <int D, int NS>
@@ -114,6 +115,9 @@ __device__ inline float sum_halves(float v) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 __device__ inline int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// Bits of the waits that gave up since the host last read them (kWaitAttn*).
+__device__ unsigned int g_attn_wait_flags;
 
 struct Shared {
   int prog[kConsumers];        // next unit each compute wave may read (16-byte aligned)
@@ -283,6 +287,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
       }
     };
     int k = 0;
+    bool gave_up = false;
     for (int u = L; u < n_units; u += kLoaders, ++k) {
       if (k >= kInflight) {
         wait_vmcnt<2 * G::NLOAD * (kInflight - 1)>();
@@ -301,7 +306,11 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
         const int mn = uniform(min(min(min(a[0], a[1]), min(a[2], a[3])), min(min(b[0], b[1]), min(b[2], b[3]))));
         const bool free_slot = mn >= u - kSlots + 1 &&
                                (u < kSlots || uniform(ld_relaxed(&sh->ready[u % kSlots])) == u - kSlots);
-        if (free_slot || ++spins > kSpinLimit) break;
+        if (free_slot) break;
+        if (++spins > p.spin_limit) {
+          gave_up = true;
+          break;
+        }
         __builtin_amdgcn_s_sleep(1);
       }
       compiler_fence();
@@ -314,6 +323,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
     wait_vmcnt<0>();
     const int first = max(L, L + kLoaders * (k - kInflight));
     for (int u = first; u < n_units; u += kLoaders) publish(u);
+    if (gave_up && lane == 0) atomicOr(&g_attn_wait_flags, kWaitAttnLoader);
     return;
   }
 
@@ -435,11 +445,18 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
     }
   };
 
+  bool gave_up = false;
   auto consume = [&](int u, int key0) {
     compiler_fence();
     st_relaxed(&sh->prog[wave], u);
     int spins = 0;
-    while (ld_relaxed(&sh->ready[u % kSlots]) != u && ++spins <= kSpinLimit) __builtin_amdgcn_s_sleep(1);
+    while (ld_relaxed(&sh->ready[u % kSlots]) != u) {
+      if (++spins > p.spin_limit) {
+        gave_up = true;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
     compiler_fence();
     compute(ring + (u % kSlots) * G::SLOT, key0);
   };
@@ -471,6 +488,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
   }
   compiler_fence();
   st_relaxed(&sh->prog[wave], kDone);
+  if (gave_up && lane == 0) atomicOr(&g_attn_wait_flags, kWaitAttnCompute);
 
   // ---------------- epilogue ----------------
   const float l_tot = sum_halves(l_run);
@@ -531,6 +549,20 @@ hipError_t launch_sparse_attn(const AttnParams& p, int D, int Bs, hipStream_t st
   if (D == 128 && Bs == 128) return launch_one<128, 128, true>(p, stream);
   if (D == 64 && Bs == 128) return launch_one<64, 128, true>(p, stream);
   return hipErrorInvalidValue;
+}
+
+hipError_t take_wait_flags_attn(unsigned* flags, hipStream_t stream) {
+  unsigned v = 0;
+  hipError_t e = hipMemcpyFromSymbolAsync(&v, HIP_SYMBOL(g_attn_wait_flags), sizeof v, 0, hipMemcpyDeviceToHost,
+                                          stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e == hipSuccess && v != 0) {
+    static const unsigned zero = 0;
+    e = hipMemcpyToSymbolAsync(HIP_SYMBOL(g_attn_wait_flags), &zero, sizeof zero, 0, hipMemcpyHostToDevice, stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  }
+  *flags = v;
+  return e;
 }
 
 hipError_t launch_dense_attn(const AttnParams& p, int D, hipStream_t stream) {

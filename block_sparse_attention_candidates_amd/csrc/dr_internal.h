@@ -212,6 +212,18 @@ inline QGroup make_qgroup(int Nf, int Nt, int Bs, int Sb) {
   return q;
 }
 
+// Bounded waits of the ring protocols: every wait polls at most spin_limit
+// times (kDefaultSpinLimit unless a caller lowered it for a test of this
+// report). A wave whose wait gives up ORs its bit into its file's flag word in
+// device memory (a vector-memory atomic) and goes on, so every kernel still
+// exits; the host reads and clears the words with take_wait_flags_*().
+constexpr int kDefaultSpinLimit = 1 << 26;
+constexpr unsigned kWaitAttnLoader = 1u;    // attention loader: slot refilled before it was free
+constexpr unsigned kWaitAttnCompute = 2u;   // attention compute wave: unit read before it was published
+constexpr unsigned kWaitToken = 4u;         // token selector: key block read before it was published
+hipError_t take_wait_flags_attn(unsigned* flags, hipStream_t stream);
+hipError_t take_wait_flags_token(unsigned* flags, hipStream_t stream);
+
 struct AttnParams {
   const uint16_t* q;
   const uint16_t* k;
@@ -226,6 +238,7 @@ struct AttnParams {
   int S, Sb, BH;
   int n_tiles;        // query-row tiles per (b, h) (dense) / grid width (sparse)
   float scale_log2;   // softmax_scale * log2(e)
+  int spin_limit;     // polls before a bounded wait gives up (>= 1)
 };
 
 struct GroupCostParams {
@@ -263,6 +276,7 @@ struct TokParams {
   int FR;              // query frames a workgroup can span
   double gamma, lambda, theta_c, theta_m, tau_near, tau_far, eps;
   float scale;         // 1 / (sqrt(d_k) * H_f)
+  int spin_limit;      // polls before a bounded wait gives up (>= 1)
   // workspace
   TokStat* part;       // [B][n_wg][kTokSplit][FR][Nf] workgroup partials
   float* thr;          // [B][Nf][Nf] threshold in score units (+inf: no t > 1 pair)
@@ -327,7 +341,13 @@ struct ProxyParams {
   const int32_t* kept_cnt;
   long long n_cnt;
   double* partial;        // [kProxyPartials][3]
-  double* out;            // [3]
+  double* out;            // [3], or [6] with the loss terms
+  // Eq. 22 terms (with_loss != 0): out[3] = out[0] / out[1] (normalised
+  // error), out[4] = 1 - out[2] / total_blocks (sparsity), out[5] = out[3] +
+  // alpha * max(0, target - out[4])
+  int with_loss;
+  long long total_blocks;
+  double alpha, target;
 };
 hipError_t launch_proxy_error(const ProxyParams& p, hipStream_t stream);
 hipError_t launch_token_select(const TokParams& p, int B, int D, int Bs, int Hf, hipStream_t stream);

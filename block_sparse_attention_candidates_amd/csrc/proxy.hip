@@ -9,7 +9,9 @@
 // every bf16 element is read once with 16-byte loads. Each thread sums a fixed
 // grid-strided set of elements in float64, workgroups reduce in a fixed tree
 // order into one partial each, and a single workgroup adds the partials in
-// order, so the result is bit-reproducible.
+// order, so the result is bit-reproducible. With the loss requested, the same
+// workgroup also forms Eq. 22 from the three sums: the normalised error, the
+// sparsity 1 - (kept block pairs) / (all block pairs) and the penalised loss.
 #include "dr_internal.h"
 
 namespace dr {
@@ -94,6 +96,15 @@ __global__ __launch_bounds__(kThreads) void final_kernel(ProxyParams p) {
     p.out[0] = d2;
     p.out[1] = r2;
     p.out[2] = cnt;
+    if (p.with_loss) {
+      // Eq. 22: normalised squared error plus the sparsity shortfall penalty
+      const double nmse = d2 / r2;
+      const double sparsity = 1.0 - cnt / (double)p.total_blocks;
+      const double shortfall = p.target - sparsity;
+      p.out[3] = nmse;
+      p.out[4] = sparsity;
+      p.out[5] = nmse + p.alpha * (shortfall > 0.0 ? shortfall : 0.0);
+    }
   }
 }
 

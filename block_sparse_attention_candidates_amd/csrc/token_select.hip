@@ -8,7 +8,8 @@
 //   stats:    a workgroup of 8 wavefronts owns 256 query tokens (8 / 4 query
 //             blocks); it walks the union of their candidate key blocks in
 //             ascending order, staging each key block of the H_f fused heads in
-//             LDS (double-buffered, XOR-swizzled rows), and every wave whose
+//             an LDS ring (XOR-swizzled rows, claim-based loading, see
+//             ring_service), and every wave whose
 //             query block has the key block as a candidate computes its 32x32
 //             token tiles of s = (1/H_f) sum_h Q^h K^h^T / sqrt(d_k) (Eq. 9) with
 //             v_mfma_f32_32x32x16_bf16. Token pairs of P(i, j) with t > 1 feed
@@ -48,11 +49,14 @@ constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
 constexpr int kRows = kWaves * 32;      // query tokens per workgroup
 constexpr int kRingMax = 16;            // ring depth limit (key blocks)
-constexpr int kSpinLimit = 1 << 26;     // bound of every wait
 constexpr int kDone = 0x3fffffff;       // progress of a wave that reads no more blocks
 
 typedef int intx4 __attribute__((ext_vector_type(4)));
 #define DR_LDS __attribute__((address_space(3)))
+
+// Set (kWaitToken) by a wave whose bounded ring wait gave up; read and cleared
+// by the host (take_wait_flags_token).
+__device__ unsigned int g_tok_wait_flags;
 __device__ __forceinline__ int ld_relaxed(const int* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
@@ -397,7 +401,11 @@ __device__ __forceinline__ void ring_wait(const TokParams& p, int b, const Lds<D
   st_relaxed(&L.prog[wave], j);
   ring_service<D, BS, HF>(p, b, L, n, pending, lane);
   int spins = 0;
-  while (ld_relaxed(&L.ready[j % G::NB]) != j && ++spins <= kSpinLimit) {
+  while (ld_relaxed(&L.ready[j % G::NB]) != j) {
+    if (++spins > p.spin_limit) {
+      if (lane == 0) atomicOr(&g_tok_wait_flags, kWaitToken);
+      break;
+    }
     ring_service<D, BS, HF>(p, b, L, n, pending, lane);
     __builtin_amdgcn_s_sleep(1);
   }
@@ -1115,6 +1123,20 @@ __global__ __launch_bounds__(256) void flag_compact_kernel(FlagCompact p) {
 hipError_t launch_flag_compact(const FlagCompact& c, int B, hipStream_t stream) {
   hipLaunchKernelGGL(flag_compact_kernel, dim3((unsigned)((c.Sb + 3) / 4), (unsigned)B), dim3(256), 0, stream, c);
   return hipGetLastError();
+}
+
+hipError_t take_wait_flags_token(unsigned* flags, hipStream_t stream) {
+  unsigned v = 0;
+  hipError_t e = hipMemcpyFromSymbolAsync(&v, HIP_SYMBOL(g_tok_wait_flags), sizeof v, 0, hipMemcpyDeviceToHost,
+                                          stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e == hipSuccess && v != 0) {
+    static const unsigned zero = 0;
+    e = hipMemcpyToSymbolAsync(HIP_SYMBOL(g_tok_wait_flags), &zero, sizeof zero, 0, hipMemcpyHostToDevice, stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  }
+  *flags = v;
+  return e;
 }
 
 hipError_t launch_token_select(const TokParams& p, int B, int D, int Bs, int Hf, hipStream_t stream) {

@@ -30,8 +30,11 @@
  *    tokens [a*B_s, min((a+1)*B_s, S)). S_b = ceil(S / B_s). Tokens >= S are
  *    padding: never attended, never pooled, never written.
  *  - All device buffers are allocated by the caller. The library allocates
- *    nothing and keeps no state across calls except a thread-local error
- *    message.
+ *    nothing. State kept across calls: a thread-local error message, the
+ *    process-wide poll limit of the bounded waits (dr_set_wait_limit) and, on
+ *    each device, a word of flags of waits that gave up (dr_wait_report).
+ *  - Tensor inputs (q, k, v) must hold finite values; NaN or infinity in q or k
+ *    makes the outputs of the calls that read them unspecified.
  *  - Calls are asynchronous on the given HIP stream (NULL = default stream);
  *    inputs must stay valid until the stream passes the call. Only
  *    dr_build_candidates synchronises (to report the candidate count).
@@ -58,7 +61,8 @@ typedef enum dr_status {
   DR_ERR_INVALID_ARG = 1, /* null pointer, non-positive size, value out of range */
   DR_ERR_UNSUPPORTED = 2, /* valid but not built: head_dim / block_size / size limits */
   DR_ERR_CAPACITY = 3,    /* output capacity below the required size */
-  DR_ERR_HIP = 4          /* a HIP launch or runtime call failed */
+  DR_ERR_HIP = 4,         /* a HIP launch or runtime call failed */
+  DR_ERR_WAIT = 5         /* dr_wait_report: a bounded wait of a ring kernel gave up */
 } dr_status;
 
 /* Radial candidate configuration ([DR] §3.1; parameter vector x of §3.4 / C.4). */
@@ -309,6 +313,41 @@ dr_status dr_attn(const dr_dims* dims, int32_t seq_len, const void* q, const voi
 #define DR_PROXY_WS_BYTES 24576
 dr_status dr_proxy_error(const void* o_ref, const void* o_test, int64_t n, const int32_t* kept_cnt, int64_t n_cnt,
                          double* out, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* The proxy-task objective of [DR] App. C.4 Eq. 22 in one call: the sums of
+ * dr_proxy_error in out[0..2], then
+ *   out[3] = out[0] / out[1]                          normalised error
+ *   out[4] = 1 - out[2] / total_blocks                sparsity (total_blocks =
+ *                                                     B * H * S_b^2, all block pairs)
+ *   out[5] = out[3] + alpha * max(0, target - out[4]) the loss ([DR]: alpha = 10,
+ *                                                     target = 0.8)
+ * out: device, 6 doubles; total_blocks >= 1; alpha finite and >= 0; target
+ * finite. out[1] = 0 (an all-zero o_ref) gives the IEEE quotient (inf or NaN).
+ * Other arguments as dr_proxy_error. */
+dr_status dr_proxy_loss(const void* o_ref, const void* o_test, int64_t n, const int32_t* kept_cnt, int64_t n_cnt,
+                        int64_t total_blocks, double alpha, double target, double* out, void* ws, size_t ws_bytes,
+                        hipStream_t stream);
+
+/* Bounded waits. The kernels of dr_sparse_attn, dr_sparse_attn_grouped,
+ * dr_attn and dr_token_select pass data between wavefronts through LDS rings
+ * ([DR] §3.3: each kept tile is streamed once per workgroup); every wait in
+ * them polls a bounded number of times. A wave whose wait gives up (the
+ * protocol never needs it) sets a flag on its device and goes on, so the
+ * kernel still exits, but the outputs of that call are not valid.
+ *
+ * dr_wait_report: synchronises `stream`, then reads and clears the flags of
+ * the current device: bit 0 (1) an attention loader refilled a slot before it
+ * was free, bit 1 (2) an attention compute wave read a unit before it was
+ * published, bit 2 (4) a token-selection wave read a key block before it was
+ * published. Stores them in *flags (host) and returns DR_ERR_WAIT if any is
+ * set, else DR_OK. Calls still running on other streams may set flags later.
+ *
+ * dr_set_wait_limit: the number of polls after which every bounded wait of
+ * later calls (on any device, any thread) gives up; 0 restores the default
+ * 2^26 (seconds of waiting). For tests of this report: a tiny limit makes
+ * waits give up on purpose while every kernel still exits normally. */
+dr_status dr_wait_report(hipStream_t stream, uint32_t* flags);
+dr_status dr_set_wait_limit(int64_t polls);
 
 /* Static description of a status code. */
 const char* dr_status_string(dr_status status);

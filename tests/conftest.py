@@ -21,3 +21,18 @@ def dynrad_lib():
         from block_sparse_attention_candidates_amd import build
         build.build()
     return _lib.lib()
+
+
+@pytest.fixture(autouse=True)
+def _no_wait_gave_up(request):
+    """After every GPU test: no bounded wait of a ring kernel gave up
+    (dr_wait_report reads and clears the device's flags; raises if any)."""
+    yield
+    if request.node.get_closest_marker("gpu") is None:
+        return
+    import torch
+    if not torch.cuda.is_available():
+        return
+    import block_sparse_attention_candidates_amd as dr
+    dr.set_wait_limit(0)
+    assert dr.wait_report() == 0

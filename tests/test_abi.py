@@ -212,6 +212,29 @@ def test_proxy_error_validation(dynrad_lib):
     assert pe(t=ctypes.c_void_p(8200)) == L.DR_ERR_INVALID_ARG   # not 16-byte aligned
     assert pe(ws_bytes=L.PROXY_WS_BYTES - 8) == L.DR_ERR_CAPACITY
 
+    def pl(total=100, alpha=10.0, target=0.8, **kw):
+        a = dict(r=A, t=B, n=100, cnt=None, n_cnt=0, out=A, ws=B, ws_bytes=L.PROXY_WS_BYTES) | kw
+        return dynrad_lib.dr_proxy_loss(a["r"], a["t"], a["n"], a["cnt"], a["n_cnt"], total, alpha, target, a["out"],
+                                        a["ws"], a["ws_bytes"], None)
+    assert pl(total=0) == L.DR_ERR_INVALID_ARG
+    assert pl(alpha=-1.0) == L.DR_ERR_INVALID_ARG
+    assert pl(alpha=float("inf")) == L.DR_ERR_INVALID_ARG
+    assert pl(target=float("nan")) == L.DR_ERR_INVALID_ARG
+    assert pl(r=None) == L.DR_ERR_INVALID_ARG
+    assert pl(ws_bytes=16) == L.DR_ERR_CAPACITY
+
+
+def test_wait_limit_and_report_validation(dynrad_lib):
+    """dr_set_wait_limit accepts [0, 2^31); dr_wait_report rejects a NULL
+    flags pointer before any HIP call."""
+    from block_sparse_attention_candidates_amd import _lib as L
+    assert dynrad_lib.dr_set_wait_limit(-1) == L.DR_ERR_INVALID_ARG
+    assert dynrad_lib.dr_set_wait_limit(1 << 31) == L.DR_ERR_INVALID_ARG
+    assert dynrad_lib.dr_set_wait_limit(5) == L.DR_OK
+    assert dynrad_lib.dr_set_wait_limit(0) == L.DR_OK
+    assert dynrad_lib.dr_wait_report(None, None) == L.DR_ERR_INVALID_ARG
+    assert dynrad_lib.dr_status_string(L.DR_ERR_WAIT) == b"bounded wait gave up"
+
 
 @pytest.mark.parametrize("layout", [(21, 3600, 32), (21, 1560, 32), (33, 3600, 64), (9, 33, 128), (6, 200, 64),
                                     (4, 64, 32), (1, 1000, 32), (13, 31, 32), (5, 300, 128)])

@@ -1,7 +1,7 @@
 """GPU parity of the proxy-task evaluator ([DR] App. C.2 Eq. 20, C.4 Eq. 22):
 dr_proxy_error's sums against float64 NumPy, and the penalised loss of whole
-masks (dr_attn + dr_sparse_attn on the drift inputs with a random probe)
-against the oracle's probe form on the same inputs and masks."""
+masks (dr_attn + dr_sparse_attn on the drift inputs with a random probe, then
+dr_proxy_loss) against the oracle's probe form on the same inputs and masks."""
 import numpy as np
 import pytest
 
@@ -57,7 +57,11 @@ def _check(res, ora_nmse, ora_sparsity, label):
     # error sum by a few percent of the signal at these error levels
     assert res["nmse"] == pytest.approx(ora_nmse, rel=0.05, abs=2e-4)
     assert res["sparsity"] == pytest.approx(ora_sparsity, abs=1e-12)
-    assert res["loss"] == pytest.approx(res["nmse"] + 10.0 * max(0.0, 0.8 - res["sparsity"]), rel=1e-12)
+    # the library's Eq. 22 (dr_proxy_loss) on its own terms equals the oracle's formula
+    assert res["nmse"] == res["err_sum"] / res["ref_sum"]
+    assert res["loss"] == pytest.approx(O.proxy_loss(res["nmse"], res["sparsity"]), rel=1e-12, abs=1e-15)
+    # and the loss as a whole is the oracle's loss within the error tolerance above
+    assert res["loss"] == pytest.approx(O.proxy_loss(ora_nmse, ora_sparsity), rel=0.05, abs=2e-4)
 
 
 @pytest.mark.parametrize("regime", ["low", "mid", "high"])
