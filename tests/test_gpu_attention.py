@@ -19,7 +19,7 @@ pytestmark = pytest.mark.gpu
 CASES = [
     ("tiny", "static", 0.5, 1.0), ("tiny", "dynamic", 1.0, 0.8),
     ("wan13b_480p", "static", 0.2, 1.0), ("wan13b_480p", "dynamic", 1.0, 0.8),
-    ("wan14b_480p", "dynamic", 1.0, 0.8),
+    ("wan14b_480p", "dynamic", 1.0, 0.8), ("wan14b_480p", "static", 0.2, 1.0),
     ("wan14b_720p", "static", 0.15, 1.0), ("wan14b_720p", "dynamic", 1.0, 0.8),
     ("hunyuan_720p", "dynamic", 1.0, 0.85), ("hunyuan_720p", "static", 0.1, 1.0),
 ]
@@ -68,7 +68,7 @@ def test_sparse_attention_parity(name, mode, ratio, tau):
         G.log(f"   head {h}: own mask rel-L2 {r1[0]:.2e} max {r1[1]:.2e}; oracle mask {r2[0]:.2e} {r2[1]:.2e}")
 
 
-@pytest.mark.parametrize("name", ["tiny", "wan13b_480p", "wan14b_720p", "hunyuan_720p"])
+@pytest.mark.parametrize("name", ["tiny", "wan13b_480p", "wan14b_480p", "wan14b_720p", "hunyuan_720p"])
 def test_dense_attention_parity(name):
     G.log(f"[dense] {name}")
     w = workloads.get_workload(name)
@@ -185,8 +185,8 @@ def test_attention_special_cases_and_determinism():
     # ratio = 1 keeps every candidate: same as the oracle over the full candidate rows
     kept = G.dr().score_select(q, k, cand, mode="static", ratio=1.0)
     out1 = G.dr().sparse_attn(q, k, v, cand, kept)
-    out2 = G.dr().sparse_attn(q, k, v, cand, kept)
-    assert torch.equal(out1, out2)            # bitwise reproducible
+    for _ in range(3):                        # bitwise reproducible
+        assert torch.equal(G.dr().sparse_attn(q, k, v, cand, kept), out1)
     # constant V -> constant output
     vc = torch.full_like(v, 1.5)
     oc = G.to_np(G.dr().sparse_attn(q, k, vc, cand, kept))
