@@ -50,7 +50,7 @@ def parse():
     ap.add_argument("--seed", type=int, default=2024, help="sampling seed of --mode decay-static")
     ap.add_argument("--block-size", type=int, default=None, help="override the workload's block size (32, 64, 128)")
     ap.add_argument("--stage-iters", type=int, default=20)
-    ap.add_argument("--dense-iters", type=int, default=3)
+    ap.add_argument("--dense-iters", type=int, default=20)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-groups", action="store_true",
@@ -87,41 +87,68 @@ def traffic_record(workload, mode):
     return rec
 
 
+def host_info():
+    """Threads the oracle's BLAS uses, CPUs this process may run on, CPU model."""
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        blas = 1
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return int(blas), len(os.sched_getaffinity(0)), model
+
+
 def cpu_baseline(w, mode, ratio, tau, n_blocks):
     """The CPU oracle, untuned, on a bounded sample: one head, n_blocks query
     blocks spread over the sequence; every step of the path for those blocks
-    (candidate rows, pooling, scores, selection, attention)."""
+    (candidate rows, pooling, scores, selection, attention), each timed."""
     import workloads
     from oracle import dynrad_oracle as O
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:
-        cores = 1
+    cores, host_cpus, model = host_info()
     if mode == "token":
-        return cpu_baseline_token(w, tau, cores)
-    if mode == "decay-static":
-        return cpu_baseline_decay_static(w, tau, cores)
-    q, k, v = (x.astype(np.float64) for x in workloads.head_qkv(w, 0, 0))
-    Sb = w.num_blocks
-    blocks = np.unique(np.linspace(0, Sb - 1, n_blocks).astype(int))
-    t0 = time.perf_counter()
-    table = O.distance_table(w.num_frames, w.tokens_per_frame, w.block_size, w.gamma, w.lam)
-    qbar, kbar = O.pool_blocks(q, w.block_size), O.pool_blocks(k, w.block_size)
-    kept = {}
-    for a in blocks:
-        cols = O.candidate_row(int(a), w.num_frames, w.tokens_per_frame, w.block_size, w.gamma, w.lam,
-                               w.theta_c, w.theta_m, table=table)
-        s = (kbar[cols] @ qbar[a]) / math.sqrt(w.head_dim)
-        kept[int(a)] = O.select_row(s, cols, mode, ratio=ratio, tau=tau)
-    klist = [kept.get(a, np.zeros(0, dtype=np.int64)) for a in range(Sb)]
-    O.sparse_attention_rows(q, k, v, w.block_size, klist, [int(a) for a in blocks])
-    dt = time.perf_counter() - t0
-    flops = 4.0 * w.block_size ** 2 * w.head_dim * sum(len(kept[int(a)]) for a in blocks)
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-            "seconds": round(dt, 3),
-            "sample": f"{w.name} head 0, {len(blocks)} of {Sb} query blocks (evenly spaced), all stages "
-                      f"(candidate rows, pooling, scores, {mode} selection, attention), float64 NumPy"}
+        res = cpu_baseline_token(w, tau, cores)
+    elif mode == "decay-static":
+        res = cpu_baseline_decay_static(w, tau, cores)
+    else:
+        q, k, v = (x.astype(np.float64) for x in workloads.head_qkv(w, 0, 0))
+        Sb = w.num_blocks
+        blocks = np.unique(np.linspace(0, Sb - 1, n_blocks).astype(int))
+        t0 = time.perf_counter()
+        table = O.distance_table(w.num_frames, w.tokens_per_frame, w.block_size, w.gamma, w.lam)
+        rows = {int(a): O.candidate_row(int(a), w.num_frames, w.tokens_per_frame, w.block_size, w.gamma, w.lam,
+                                        w.theta_c, w.theta_m, table=table) for a in blocks}
+        t1 = time.perf_counter()
+        qbar, kbar = O.pool_blocks(q, w.block_size), O.pool_blocks(k, w.block_size)
+        t2 = time.perf_counter()
+        kept = {}
+        for a in blocks:
+            cols = rows[int(a)]
+            s = (kbar[cols] @ qbar[a]) / math.sqrt(w.head_dim)
+            kept[int(a)] = O.select_row(s, cols, mode, ratio=ratio, tau=tau)
+        t3 = time.perf_counter()
+        klist = [kept.get(a, np.zeros(0, dtype=np.int64)) for a in range(Sb)]
+        O.sparse_attention_rows(q, k, v, w.block_size, klist, [int(a) for a in blocks])
+        t4 = time.perf_counter()
+        dt = t4 - t0
+        flops = 4.0 * w.block_size ** 2 * w.head_dim * sum(len(kept[int(a)]) for a in blocks)
+        res = {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+               "seconds": round(dt, 3),
+               "stage_ms": {"candidate_rows": round((t1 - t0) * 1e3, 2), "pooling": round((t2 - t1) * 1e3, 2),
+                            "scores_selection": round((t3 - t2) * 1e3, 2), "attention": round((t4 - t3) * 1e3, 2)},
+               "sample": f"{w.name} head 0, {len(blocks)} of {Sb} query blocks (evenly spaced), all stages "
+                         f"(candidate rows, pooling of the whole head, scores, {mode} selection, attention), "
+                         f"float64 NumPy"}
+    res["host_cpus"] = host_cpus
+    res["cpu_model"] = model
+    return res
 
 
 def cpu_baseline_token(w, taus, cores):
@@ -140,16 +167,21 @@ def cpu_baseline_token(w, taus, cores):
                      if a * Bs // Nt == f and ((a + 1) * Bs - 1) // Nt == f})
     t0 = time.perf_counter()
     sub = O.token_frame_stats(qh, kh, Nf, Nt, Bs, w.gamma, w.lam, taus[0], taus[1], query_frames=frames)
+    t1 = time.perf_counter()
     kept = O.token_select_rows(qh, kh, blocks, Nf, Nt, Bs, w.gamma, w.lam, taus[0], taus[1], w.theta_c, w.theta_m,
                                stats=sub)
+    t2 = time.perf_counter()
     klist = [np.zeros(0, dtype=np.int64)] * w.num_blocks
     for a, ks in zip(blocks, kept):
         klist[a] = ks
     O.sparse_attention_rows(qh[0], kh[0], v0, Bs, klist, blocks)
-    dt = time.perf_counter() - t0
+    t3 = time.perf_counter()
+    dt = t3 - t0
     flops = 4.0 * Bs ** 2 * w.head_dim * sum(len(x) for x in kept)
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
             "seconds": round(dt, 3),
+            "stage_ms": {"frame_pair_statistics": round((t1 - t0) * 1e3, 2),
+                         "token_selection": round((t2 - t1) * 1e3, 2), "attention": round((t3 - t2) * 1e3, 2)},
             "sample": f"{w.name}: the {len(blocks)} query blocks inside frames {frames}, all stages (statistics "
                       f"of those frames' frame pairs, token-level selection on heads 0-1, attention on head 0), "
                       f"float64 NumPy"}
@@ -170,16 +202,21 @@ def cpu_baseline_decay_static(w, rho_seed, cores, n_blocks=16):
     blocks = [inside[int(x)] for x in np.unique(np.linspace(0, len(inside) - 1, n_blocks).astype(int))]
     t0 = time.perf_counter()
     th = O.static_frame_thresholds(Nf, Nt, Bs, w.gamma, w.lam, rn, rf, seed, query_frames=[f])
+    t1 = time.perf_counter()
     kept = O.static_select_rows(blocks, Nf, Nt, Bs, w.gamma, w.lam, rn, rf, seed, w.theta_c, w.theta_m,
                                 thresholds=th)
+    t2 = time.perf_counter()
     klist = [np.zeros(0, dtype=np.int64)] * w.num_blocks
     for a, ks in zip(blocks, kept):
         klist[a] = ks
     O.sparse_attention_rows(q, k, v, Bs, klist, blocks)
-    dt = time.perf_counter() - t0
+    t3 = time.perf_counter()
+    dt = t3 - t0
     flops = 4.0 * Bs ** 2 * w.head_dim * sum(len(x) for x in kept)
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
             "seconds": round(dt, 3),
+            "stage_ms": {"sample_cuts": round((t1 - t0) * 1e3, 2), "decay_static_selection": round((t2 - t1) * 1e3, 2),
+                         "attention": round((t3 - t2) * 1e3, 2)},
             "sample": f"{w.name}: {len(blocks)} query blocks inside frame {f}, all stages (sample cuts of that "
                       f"frame's {len(th)} sampled frame pairs, decay-state static selection, attention on head 0), "
                       f"float64 NumPy"}
