@@ -10,11 +10,17 @@
 // together on one XCD, where the KV blocks their unions share hit in its L2.
 //
 // Setup (the only workgroup barriers): the kept lists of the workgroup's
-// query blocks are ORed into per-block LDS bitmaps; their union is the
-// sequence of KV blocks the workgroup streams, cut into 32-key units.
+// query blocks are ORed into per-block LDS bitmaps; their union is the set of
+// KV blocks the workgroup streams, cut into 32-key units. The stream visits
+// the union in round-robin order over the query blocks by rank in their kept
+// lists (block c at key min over (slot s, rank i) of QB * i + s), so every
+// compute wave meets its own blocks evenly along the stream and the waves,
+// coupled through the ring, wait less for each other than in key order. The
+// order is a function of the group's kept lists only: outputs are bitwise
+// reproducible.
 //
 // Streaming without barriers: the loaders copy units from HBM/L2 straight into
-// an LDS ring (8 or more slots) with direct-to-LDS loads (16 B per lane, no registers),
+// an LDS ring (6 or more slots) with direct-to-LDS loads (16 B per lane, no registers),
 // each keeping one unit in flight, and publish a slot once its loads have
 // landed. Each compute wavefront walks only the units of the KV blocks its own
 // query block kept, announces its position, waits for the slot, computes. A
@@ -30,10 +36,12 @@
 //                 fragment in registers; lane l holds the 16 scores of query
 //                 row l%32 for keys 8*(i/4) + 4*(l/32) + i%4.
 //   softmax     : float32, exp2 with the scale folded into one FMA; the row max
-//                 is shared by the two lane halves with one shuffle; the
-//                 output is rescaled only when a row max grows by more than
-//                 2^8 (probabilities stay <= 256, exact after the final 1/l);
-//                 padding keys get probability 0.
+//                 (three-input maxima) is shared by the two lane halves with
+//                 one shuffle; the output is rescaled only when a row max grows
+//                 by more than 2^8 (probabilities stay <= 256, exact after the
+//                 final 1/l); padding keys get probability 0; the row sum adds
+//                 the bf16 probabilities the PV product uses, two per
+//                 v_dot2c_f32_bf16.
 //   O^T += V^T P^T: B = the lane's own probabilities as bf16; A = V^T obtained
 //                 from row-major V in LDS with the gfx950 transposing LDS read
 //                 (ds_read_b64_tr_b16: a 16-lane group turns four 4-element
@@ -56,6 +64,7 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x4_v __attribute__((__vector_size__(4 * sizeof(__bf16))));
 #define DR_LDS __attribute__((address_space(3)))
 
@@ -123,7 +132,8 @@ struct Shared {
   int prog[kConsumers];        // next unit each compute wave may read (16-byte aligned)
   int ready[kMaxSlots];        // unit index held by each slot (-1: none)
   int n_units;
-  int pad[3];
+  int tmax;                    // bound of the stream-order keys (setup)
+  int pad[2];
 };
 
 template <int D, int BS, bool SPARSE, int NS>
@@ -163,25 +173,37 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
     else return row0 / BS + s;
   };
   const int nword = (p.Sb + 31) >> 5;
-  unsigned int* uword = bits + QB * nword;        // union of the query blocks' bitmaps
+  unsigned int* uword = bits + QB * nword;        // union of the query blocks' key bitmaps
   int* wpre = reinterpret_cast<int*>(uword + nword);  // exclusive prefix popcounts
+  uint16_t* stream = reinterpret_cast<uint16_t*>(wpre + nword);  // key block of each union step
 
   // ---------------- setup ----------------
   if (tid < kSlots) sh->ready[tid] = -1;
   if (tid < kConsumers) sh->prog[tid] = 0;
   if constexpr (SPARSE) {
+    // kept list of group slot s, its length clamped to the candidate row
+    auto kept_of = [&](int s, int& cnt) -> const int32_t* {
+      const int qb = qblock(s);
+      cnt = 0;
+      if (qb < 0 || qb >= p.Sb) return nullptr;
+      cnt = min(p.kept_cnt[(long long)bh * p.Sb + qb], p.row_ptr[qb + 1] - p.row_ptr[qb]);
+      return p.kept_col + (long long)bh * p.nnz + p.row_ptr[qb];
+    };
+    // union step (position among the union's key blocks) of key block c
+    auto union_index = [&](int c) -> int {
+      return wpre[c >> 5] + __popc(uword[c >> 5] & ((1u << (c & 31)) - 1u));
+    };
     for (int i = tid; i < QB * nword; i += kThreads) bits[i] = 0;
+    if (tid == 0) sh->tmax = 0;
     __syncthreads();
     if (wave < QB) {
-      const int qb = qblock(wave);
-      if (qb >= 0 && qb < p.Sb) {
-        const int32_t* kl = p.kept_col + (long long)bh * p.nnz + p.row_ptr[qb];
-        const int cnt = p.kept_cnt[(long long)bh * p.Sb + qb];
-        for (int i = lane; i < cnt; i += 64) {
-          const int c = kl[i];
-          if (c >= 0 && c < p.Sb) atomicOr(&bits[wave * nword + (c >> 5)], 1u << (c & 31));
-        }
+      int cnt;
+      const int32_t* kl = kept_of(wave, cnt);
+      for (int i = lane; i < cnt; i += 64) {
+        const int c = kl[i];
+        if (c >= 0 && c < p.Sb) atomicOr(&bits[wave * nword + (c >> 5)], 1u << (c & 31));
       }
+      if (lane == 0) atomicMax(&sh->tmax, QB * cnt);
     }
     __syncthreads();
     for (int wi = tid; wi < nword; wi += kThreads) {
@@ -190,21 +212,80 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
       uword[wi] = u;
     }
     __syncthreads();
-    if (wave == 0) {
+    // exclusive prefix popcounts of a bitmap (one wavefront); returns the total
+    auto prefix = [&](const unsigned int* words, int* pre, int n) -> int {
       int run = 0;
-      for (int w0 = 0; w0 < nword; w0 += 64) {
+      for (int w0 = 0; w0 < n; w0 += 64) {
         const int wi = w0 + lane;
-        const int c = wi < nword ? __popc(uword[wi]) : 0;
+        const int c = wi < n ? __popc(words[wi]) : 0;
         int incl = c;
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
           const int o = __shfl_up(incl, off);
           if (lane >= off) incl += o;
         }
-        if (wi < nword) wpre[wi] = run + incl - c;
+        if (wi < n) pre[wi] = run + incl - c;
         run += __shfl(incl, 63);
       }
-      if (lane == 0) sh->n_units = run * UPB;
+      return run;
+    };
+    if (wave == 0) {
+      const int U = prefix(uword, wpre, nword);
+      if (lane == 0) sh->n_units = U * UPB;
+    }
+    __syncthreads();
+    // Stream order: the union's key blocks in round-robin order over the group
+    // slots by rank in their kept lists. Block c gets the key t(c) = min over
+    // the slots s keeping it at rank i of QB * i + s; steps ascend in t. Each
+    // slot then meets its i-th kept block no later than round i of the stream,
+    // so its work is spread evenly over the stream, whatever the key order of
+    // its list. Setup scratch lives in the ring (unused until streaming).
+    const int U = sh->n_units / UPB;
+    const int T = sh->tmax;                        // keys lie in [0, T)
+    const int tw = (T + 31) >> 5;
+    unsigned int* tmin = reinterpret_cast<unsigned int*>(ring);      // [U] key of each union step
+    unsigned int* tbit = tmin + U;                                    // [tw] keys in use
+    int* tpre = reinterpret_cast<int*>(tbit + tw);                    // [tw] their prefix counts
+    for (int i = tid; i < U; i += kThreads) tmin[i] = 0xffffffffu;
+    for (int i = tid; i < tw; i += kThreads) tbit[i] = 0;
+    __syncthreads();
+    if (wave < QB) {
+      int cnt;
+      const int32_t* kl = kept_of(wave, cnt);
+      for (int i = lane; i < cnt; i += 64) {
+        const int c = kl[i];
+        if (c >= 0 && c < p.Sb) atomicMin(&tmin[union_index(c)], (unsigned)(QB * i + wave));
+      }
+    }
+    __syncthreads();
+    for (int i = tid; i < U; i += kThreads) {
+      const unsigned int t = tmin[i];
+      atomicOr(&tbit[t >> 5], 1u << (t & 31));
+    }
+    for (int i = tid; i < QB * nword; i += kThreads) bits[i] = 0;   // become step bitmaps
+    __syncthreads();
+    if (wave == 0) prefix(tbit, tpre, tw);
+    __syncthreads();
+    auto step_of = [&](unsigned int t) -> int { return tpre[t >> 5] + __popc(tbit[t >> 5] & ((1u << (t & 31)) - 1u)); };
+    for (int wi = tid; wi < nword; wi += kThreads) {
+      unsigned int m = uword[wi];
+      int ui = wpre[wi];
+      while (m) {
+        const int b = __ffs(m) - 1;
+        m &= m - 1;
+        stream[step_of(tmin[ui++])] = (uint16_t)(wi * 32 + b);
+      }
+    }
+    if (wave < QB) {
+      int cnt;
+      const int32_t* kl = kept_of(wave, cnt);
+      for (int i = lane; i < cnt; i += 64) {
+        const int c = kl[i];
+        if (c >= 0 && c < p.Sb) {
+          const int j = step_of(tmin[union_index(c)]);
+          atomicOr(&bits[wave * nword + (j >> 5)], 1u << (j & 31));
+        }
+      }
     }
   } else {
     if (tid == 0) sh->n_units = (p.S + kUnit - 1) / kUnit;
@@ -217,25 +298,10 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
     const int L = wave - kConsumers;
     const uint16_t* __restrict__ Kg = p.k + base;
     const uint16_t* __restrict__ Vg = p.v + base;
-    // cursor over the union (sparse): block of union step j
-    int cur_wi = 0, cur_step = 0;
-    unsigned int cur_bits = SPARSE ? uword[0] : 0u;
+    // key block of union step j
     auto block_of_step = [&](int j) -> int {
-      if constexpr (!SPARSE) {
-        return j;
-      } else {
-        while (true) {
-          const int n = __popc(cur_bits);
-          if (j < cur_step + n) {
-            unsigned int m = cur_bits;
-            for (int t = cur_step; t < j; ++t) m &= m - 1;
-            return cur_wi * 32 + __ffs(m) - 1;
-          }
-          cur_step += n;
-          ++cur_wi;
-          cur_bits = uword[cur_wi];
-        }
-      }
+      if constexpr (!SPARSE) return j;
+      else return (int)stream[j];
     };
     auto publish = [&](int u) {
       compiler_fence();
@@ -347,6 +413,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
   floatx16 oacc[D / 32];
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) oacc[dt] = floatx16{};
+  const bf16x2 kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
   const float c = p.scale_log2;
   const bool c_pos = c >= 0.f;
   const float c_abs = fabsf(c);
@@ -394,9 +461,11 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
     const bool ragged = key0 + kUnit > p.S;
     float mx;
     if (c_pos && !ragged) {
-      mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-#pragma unroll
-      for (int i = 4; i < 16; i += 4) mx = fmaxf(mx, fmaxf(fmaxf(s[i], s[i + 1]), fmaxf(s[i + 2], s[i + 3])));
+      // three-input maxima: 16 values in 8 instructions
+      const float m0 = fmaxf(fmaxf(s[0], s[1]), s[2]), m1 = fmaxf(fmaxf(s[3], s[4]), s[5]);
+      const float m2 = fmaxf(fmaxf(s[6], s[7]), s[8]), m3 = fmaxf(fmaxf(s[9], s[10]), s[11]);
+      const float m4 = fmaxf(fmaxf(s[12], s[13]), s[14]);
+      mx = fmaxf(fmaxf(fmaxf(m0, m1), m2), fmaxf(fmaxf(m3, m4), s[15]));
     } else {
       // element i holds key key0 + 4*half + 8*(i/4) + i%4: valid iff below lim
       const int lim = p.S - key0 - 4 * half;
@@ -425,16 +494,22 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
       for (int i = 0; i < 16; ++i)
         if (8 * (i >> 2) + (i & 3) >= lim) x[i] = 0.f;
     }
-    float psum = 0.f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) psum += x[i];
-    l_run += psum;
     bf16x8 pb[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const floatx8 f = {x[8 * j], x[8 * j + 1], x[8 * j + 2], x[8 * j + 3],
                          x[8 * j + 4], x[8 * j + 5], x[8 * j + 6], x[8 * j + 7]};
       pb[j] = __builtin_convertvector(f, bf16x8);
+    }
+    // row sum of the probabilities as the PV product uses them (bf16), two per
+    // v_dot2c_f32_bf16 with float32 accumulation
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bf16x2 pair = {pb[j][2 * i], pb[j][2 * i + 1]};
+        l_run = __builtin_amdgcn_fdot2_f32_bf16(pair, kOnes2, l_run, false);
+      }
     }
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt) {
@@ -463,17 +538,16 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
 
   if (wrow0 < p.S) {
     if constexpr (SPARSE) {
+      // this query block's union steps, in stream order
       const unsigned int* mine = bits + (wave / WPQ) * nword;
       for (int wi = 0; wi < nword; ++wi) {
-        unsigned int m = mine[wi];
-        if (!m) continue;
-        const unsigned int uw = uword[wi];
-        const int wp = wpre[wi];
+        // wave-uniform words: the walk runs on the scalar unit
+        unsigned int m = (unsigned)uniform((int)mine[wi]);
         while (m) {
           const int b = __ffs(m) - 1;
           m &= m - 1;
-          const int j = wp + __popc(uw & ((1u << b) - 1u));
-          const int cblk = wi * 32 + b;
+          const int j = wi * 32 + b;
+          const int cblk = uniform((int)stream[j]);
 #pragma unroll
           for (int q = 0; q < UPB; ++q) {
             const int key0 = cblk * BS + q * kUnit;
@@ -514,16 +588,19 @@ size_t lds_bytes(const AttnParams& p) {
   size_t lds = Geo<D, NS>::RING + sizeof(Shared);
   if (SPARSE) {
     const int nword = (p.Sb + 31) / 32;
-    lds += (size_t)(kRows / BS) * nword * 4 + (size_t)nword * 8;
+    lds += (size_t)(kRows / BS) * nword * 4 + (size_t)nword * 8 + (((size_t)p.Sb * 2 + 15) & ~(size_t)15);
   }
   return lds;
 }
 
 // Ring depth: 9 slots of 32 keys at D = 128 (16 at D = 64) when the sparse
-// bitmaps leave room for them, else 8.
+// bitmaps and stream table leave room for them, else 6 (12). The shallow ring
+// also holds the setup scratch of the largest layouts (S_b = 16384: 64 KB of
+// step keys and 32 KB of key bitmaps).
 template <int D, int BS, bool SPARSE>
 hipError_t launch_one(const AttnParams& p, hipStream_t stream) {
   constexpr int DEEP = D == 128 ? 9 : 16;
+  constexpr int SHALLOW = D == 128 ? 6 : 12;
   // sparse: the widest grouping in use; a workgroup past its mode's group
   // count exits at once
   int gx = p.n_tiles;
@@ -531,11 +608,13 @@ hipError_t launch_one(const AttnParams& p, hipStream_t stream) {
     for (int m = 1; m < kGroupModes; ++m) gx = max(gx, group_count(p.grp, m));
   const dim3 grid((unsigned)gx, (unsigned)p.BH);
   const size_t deep = lds_bytes<D, BS, SPARSE, DEEP>(p);
-  const size_t base = lds_bytes<D, BS, SPARSE, 8>(p);
+  const size_t shallow = lds_bytes<D, BS, SPARSE, SHALLOW>(p);
   if (deep <= (size_t)kLdsBytes)
     hipLaunchKernelGGL((attn_kernel<D, BS, SPARSE, DEEP>), grid, dim3(kThreads), deep, stream, p);
+  else if (shallow <= (size_t)kLdsBytes)
+    hipLaunchKernelGGL((attn_kernel<D, BS, SPARSE, SHALLOW>), grid, dim3(kThreads), shallow, stream, p);
   else
-    hipLaunchKernelGGL((attn_kernel<D, BS, SPARSE, 8>), grid, dim3(kThreads), base, stream, p);
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

@@ -240,18 +240,22 @@ dr_status dr_static_select(const dr_dims* dims, const dr_radial_cfg* cfg, const 
  * float32, bf16 products into float32 accumulators, bf16 output.
  * Kept lists use the layout of dr_score_select (any source: a host-built mask
  * uploaded in that layout works). Entries outside [0, S_b) are ignored and
- * duplicates count once; a row with no kept block outputs zeros.
+ * duplicates count once; a row with no kept block outputs zeros; a kept count
+ * above the row's candidate count is read as the candidate count.
  * q, k, v, out: bf16 [B, H, S, D] device; out must not alias the inputs. */
 dr_status dr_sparse_attn(const dr_dims* dims, const dr_radial_cfg* cfg, const void* q,
                          const void* k, const void* v, const int32_t* row_ptr, int64_t nnz,
                          const int32_t* kept_col, const int32_t* kept_cnt, float softmax_scale,
                          void* out, hipStream_t stream);
 
-/* Query-block grouping of the sparse attention (scheduling only: the output of
- * dr_sparse_attn_grouped is bit-identical to dr_sparse_attn's for every mode).
- * One workgroup computes a group of Q = 256 / B_s query blocks and reads the
- * union of their kept lists ([DR] §3.3: each kept block pair is one tile), so
- * groups whose kept lists overlap read fewer key/value bytes. Modes:
+/* Query-block grouping of the sparse attention (scheduling only). One
+ * workgroup computes a group of Q = 256 / B_s query blocks and reads the union
+ * of their kept lists ([DR] §3.3: each kept block pair is one tile), so groups
+ * whose kept lists overlap read fewer key/value bytes. The workgroup streams
+ * that union in an order set by all of its query blocks (round robin over
+ * their kept lists by rank), so a grouping changes the order in which a query
+ * block's kept blocks are accumulated: outputs of different groupings agree to
+ * float32 rounding, and each is bitwise reproducible. Modes:
  *   0: consecutive blocks Q g .. Q g + Q - 1 (the grouping of dr_sparse_attn);
  *   1, 2: blocks in rows, one per frame (row f = blocks [floor(f N_t / B_s),
  *      floor((f + 1) N_t / B_s)), the last row up to S_b); a group is F
@@ -283,7 +287,8 @@ dr_status dr_query_groups(const dr_dims* dims, const dr_radial_cfg* cfg, const i
 
 /* dr_sparse_attn with the query blocks of (b, h) grouped by mode
  * group_mode[b * H + h] (device int32 [B * H], non-NULL; a value that is not a
- * mode with groups at this B_s means mode 0). Same results as dr_sparse_attn. */
+ * mode with groups at this B_s means mode 0). Same results as dr_sparse_attn up
+ * to the order of accumulation. */
 dr_status dr_sparse_attn_grouped(const dr_dims* dims, const dr_radial_cfg* cfg, const void* q,
                                  const void* k, const void* v, const int32_t* row_ptr, int64_t nnz,
                                  const int32_t* kept_col, const int32_t* kept_cnt,

@@ -167,11 +167,14 @@ def test_sparse_attention_empty_rows_and_bad_entries():
         bad = G.dr().Kept(col.view(-1), cnt.view(-1))
         out2 = G.to_np(G.dr().sparse_attn(q, k, v, cand, bad))
         np.testing.assert_array_equal(out2[0, 0, a * 32:(a + 1) * 32], out[0, 0, a * 32:(a + 1) * 32])
-        # the same under every query grouping and the chosen one (bad entries ignored there too)
+        # the same under every query grouping and the chosen one (bad entries ignored there too;
+        # the grouping changes only the accumulation order)
         for modes in [torch.full((B * H,), m, dtype=torch.int32, device="cuda") for m in range(3)] + \
                      [G.dr().query_groups(q, cand, bad)]:
             out3 = G.to_np(G.dr().sparse_attn(q, k, v, cand, bad, groups=modes))
-            np.testing.assert_array_equal(out3, out2)
+            assert G.rel_l2(out3.ravel(), out2.ravel()) <= G.REL_L2 and np.abs(out3 - out2).max() <= 2 * G.MAX_ABS
+            good = G.to_np(G.dr().sparse_attn(q, k, v, cand, kept, groups=modes))
+            np.testing.assert_array_equal(out3[0, 0, a * 32:(a + 1) * 32], good[0, 0, a * 32:(a + 1) * 32])
 
 
 def test_attention_special_cases_and_determinism():

@@ -1,12 +1,15 @@
 """Query-block grouping of the sparse attention on the GPU.
 
-dr_sparse_attn_grouped must give bit-identical outputs to dr_sparse_attn for
-every grouping mode (the grouping only changes which workgroup computes a
-query block), including mixed modes per (b, h) and out-of-range mode values;
-dr_query_groups must pick, per (b, h), the mode whose groups' kept-list unions
-have the smallest estimated total size (groups 0, 4, 8, ... measured, the sum
-scaled to the mode's group count; ties to the lower mode), recomputed here on
-the host from the kept lists and the host group tables."""
+The grouping changes which workgroup computes a query block and so the order
+in which its kept blocks are accumulated (a workgroup streams its union in an
+order that depends on all of its query blocks). dr_sparse_attn_grouped must
+therefore agree with dr_sparse_attn within the attention tolerances (and with
+the oracle on sampled rows), for every grouping mode, mixed modes per (b, h)
+and out-of-range mode values, and be bitwise reproducible for a given
+grouping. dr_query_groups must pick, per (b, h), the mode whose groups'
+kept-list unions have the smallest estimated total size (groups 0, 4, 8, ...
+measured, the sum scaled to the mode's group count; ties to the lower mode),
+recomputed here on the host from the kept lists and the host group tables."""
 import numpy as np
 import pytest
 
@@ -62,18 +65,30 @@ def _expected_modes(tot, counts):
     return np.array(out)
 
 
+def _same_within_tolerance(out, ref, what):
+    """Two GPU outputs that each meet the oracle bar (rel-L2 1e-2, max-abs
+    2e-2) differ by at most twice the max-abs bar: bf16 outputs of magnitude 4
+    to 8 round to steps of 2^-5, so one rounding step apart is 0.031."""
+    a, b = G.to_np(out).ravel(), G.to_np(ref).ravel()
+    assert np.isfinite(a).all(), f"{what}: non-finite output"
+    r, m = G.rel_l2(a, b), float(np.abs(a - b).max())
+    assert r <= G.REL_L2 and m <= 2 * G.MAX_ABS, f"{what}: rel-L2 {r:.3g} max-abs {m:.3g}"
+
+
 def _check(q, k, v, cand, kept, B, H, label):
     import torch
     ref = G.dr().sparse_attn(q, k, v, cand, kept)
+    assert torch.equal(G.dr().sparse_attn(q, k, v, cand, kept), ref), f"{label}: not reproducible"
     variants = {f"mode {m}": torch.full((B * H,), m, dtype=torch.int32, device="cuda") for m in range(3)}
     variants["mixed"] = (torch.arange(B * H, dtype=torch.int32, device="cuda") % 3).to(torch.int32)
     variants["out of range"] = torch.tensor([7, -1, 3] * (B * H), dtype=torch.int32, device="cuda")[:B * H]
     for name, modes in variants.items():
         out = G.dr().sparse_attn(q, k, v, cand, kept, groups=modes)
-        assert torch.equal(out, ref), f"{label}: {name} differs from the consecutive grouping"
+        _same_within_tolerance(out, ref, f"{label}: {name} vs the consecutive grouping")
+        assert torch.equal(G.dr().sparse_attn(q, k, v, cand, kept, groups=modes), out), f"{label}: {name} not reproducible"
     chosen = G.dr().query_groups(q, cand, kept)
     out = G.dr().sparse_attn(q, k, v, cand, kept, groups=chosen)
-    assert torch.equal(out, ref), f"{label}: chosen grouping differs"
+    _same_within_tolerance(out, ref, f"{label}: chosen grouping")
     tot, counts = _host_union_totals(kept, cand, B, H)
     exp = _expected_modes(tot, counts)
     got = chosen.cpu().numpy()
@@ -111,7 +126,8 @@ def test_grouping_random_masks(B, H, Nf, Nt, D, Bs):
 
 def test_grouping_choice_full_size_static():
     """wan14b_720p with the static 15% selection: the choice on every head
-    (host union totals on three heads), and the grouped output bit-identical."""
+    (host union totals on three heads), and the grouped output within the
+    attention tolerances of the consecutive one and of the oracle."""
     import torch
     G.log("[groups] wan14b_720p static")
     name = "wan14b_720p"
@@ -122,8 +138,18 @@ def test_grouping_choice_full_size_static():
     chosen = G.dr().query_groups(q, cand, kept)
     ref = G.dr().sparse_attn(q, k, v, cand, kept)
     out = G.dr().sparse_attn(q, k, v, cand, kept, groups=chosen)
-    assert torch.equal(out, ref)
+    _same_within_tolerance(out, ref, "wan14b_720p static: chosen grouping")
     rp, _ = G.host_csr(cand)
+    # sampled rows of the grouped output against the oracle on the GPU's own mask
+    from oracle import dynrad_oracle as O
+    o = G.to_np(out[0])
+    for h in (0, w.heads - 1):
+        qh, kh, vh = G.head_f64(name, 0, h)
+        blocks = G.sample_blocks(cand.num_blocks, 12, seed=77 + h)
+        rows = np.concatenate([np.arange(a * w.block_size, min((a + 1) * w.block_size, w.seq_len)) for a in blocks])
+        ref_o = O.sparse_attention_rows(qh, kh, vh, w.block_size, G.kept_lists(kept, rp, cand.nnz, cand.num_blocks, h),
+                                        blocks)
+        G.check_close(o[h][rows], ref_o, f"grouped head {h} vs oracle")
     tables = [G.dr().group_table(cand, m) for m in range(3)]
     got = chosen.cpu().numpy()
     for h in (0, w.heads // 2, w.heads - 1):
