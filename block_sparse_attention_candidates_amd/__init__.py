@@ -27,8 +27,9 @@ from . import _lib as _L
 from ._lib import Dims, DynradError, RadialCfg, SelectCfg, check, lib
 
 __all__ = ["radial_cfg", "num_blocks", "distance_table", "Candidates", "Kept", "build_candidates",
-           "score_select", "token_select", "static_select", "query_groups", "group_table", "sparse_attn", "attn",
-           "proxy_error", "proxy_loss", "DynradError", "kept_from_lists", "wait_report", "set_wait_limit"]
+           "score_select", "token_select", "static_select", "query_groups", "query_groups_noalloc", "group_table",
+           "sparse_attn", "attn", "proxy_error", "proxy_loss", "DynradError", "kept_from_lists", "wait_report",
+           "set_wait_limit"]
 
 
 def radial_cfg(num_frames: int, tokens_per_frame: int, block_size: int, gamma: float, lam: float,
@@ -215,6 +216,21 @@ def query_groups(q, cand: Candidates, kept: Kept, workspace=None):
     check(lib().dr_query_groups(ctypes.byref(dims), ctypes.byref(cand.cfg), cand.row_ptr.data_ptr(), cand.nnz,
                                 kept.kept_col.data_ptr(), kept.kept_cnt.data_ptr(), modes.data_ptr(),
                                 workspace.data_ptr(), workspace.numel(), _stream(q.device)))
+    return modes
+
+
+def query_groups_noalloc(q, cand: Candidates, kept: Kept, out=None):
+    """query_groups without a workspace (dr_query_groups_noalloc: the library's
+    per-GPU scratch array). `out`: an int32 tensor of B * H modes to fill, or
+    None (then one is allocated here, by torch, outside the library)."""
+    torch = _torch()
+    dims = _dims(tuple(q.shape))
+    modes = out if out is not None else torch.empty(dims.batch * dims.heads, dtype=torch.int32, device=q.device)
+    if modes.dtype != torch.int32 or modes.numel() != dims.batch * dims.heads or not modes.is_contiguous():
+        raise ValueError("out must be a contiguous int32 tensor of B * H modes")
+    check(lib().dr_query_groups_noalloc(ctypes.byref(dims), ctypes.byref(cand.cfg), cand.row_ptr.data_ptr(), cand.nnz,
+                                        kept.kept_col.data_ptr(), kept.kept_cnt.data_ptr(), modes.data_ptr(),
+                                        _stream(q.device)))
     return modes
 
 

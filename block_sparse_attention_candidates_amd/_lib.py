@@ -93,6 +93,8 @@ def lib() -> ctypes.CDLL:
         "dr_query_groups_workspace": (c_int32, [P(Dims), P(c_size_t)]),
         "dr_query_groups": (c_int32, [P(Dims), P(RadialCfg), c_void_p, c_int64, c_void_p, c_void_p, c_void_p,
                                       c_void_p, c_size_t, c_void_p]),
+        "dr_query_groups_noalloc": (c_int32, [P(Dims), P(RadialCfg), c_void_p, c_int64, c_void_p, c_void_p,
+                                              c_void_p, c_void_p]),
         "dr_attn": (c_int32, [P(Dims), c_int32, c_void_p, c_void_p, c_void_p, c_float, c_void_p, c_void_p]),
         "dr_status_string": (ctypes.c_char_p, [c_int32]),
         "dr_last_error": (ctypes.c_char_p, []),

@@ -623,19 +623,31 @@ dr_status dr_query_groups_workspace(const dr_dims* dims, size_t* bytes) {
   return ok();
 }
 
-dr_status dr_query_groups(const dr_dims* dims, const dr_radial_cfg* cfg, const int32_t* row_ptr, int64_t nnz,
-                          const int32_t* kept_col, const int32_t* kept_cnt, int32_t* group_mode, void* ws,
-                          size_t ws_bytes, hipStream_t stream) {
+static dr_status query_groups_impl(const dr_dims* dims, const dr_radial_cfg* cfg, const int32_t* row_ptr,
+                                   int64_t nnz, const int32_t* kept_col, const int32_t* kept_cnt, int32_t* group_mode,
+                                   void* ws, size_t ws_bytes, bool library_scratch, hipStream_t stream) {
   Layout L;
   dr_status st = check_radial(cfg, &L);
   if (st != DR_OK) return st;
   if ((st = check_dims(dims)) != DR_OK) return st;
   if ((st = check_nnz(nnz, L.Sb, dims)) != DR_OK) return st;
-  if (!row_ptr || !kept_col || !kept_cnt || !group_mode || !ws)
-    return fail(DR_ERR_INVALID_ARG, "row_ptr, kept_col, kept_cnt, group_mode and ws must be non-NULL");
-  const size_t need = align256((size_t)dims->batch * dims->heads * dr::kGroupModes * sizeof(uint32_t));
-  if (ws_bytes < need) return fail(DR_ERR_CAPACITY, "workspace of %zu bytes below the %zu required", ws_bytes, need);
+  if (!row_ptr || !kept_col || !kept_cnt || !group_mode)
+    return fail(DR_ERR_INVALID_ARG, "row_ptr, kept_col, kept_cnt and group_mode must be non-NULL");
   if ((long long)dims->batch * dims->heads > 65535) return fail(DR_ERR_UNSUPPORTED, "batch * heads above 65535");
+  if (library_scratch) {
+    if ((long long)dims->batch * dims->heads > dr::kGroupScratchBH)
+      return fail(DR_ERR_CAPACITY, "batch * heads = %lld above the %d the library's scratch holds",
+                  (long long)dims->batch * dims->heads, dr::kGroupScratchBH);
+    uint32_t* scratch = nullptr;
+    const hipError_t e = dr::group_scratch(&scratch);
+    if (e != hipSuccess) return hip_fail(e, "address of the grouping scratch on the current device");
+    ws = scratch;
+  } else {
+    if (!ws) return fail(DR_ERR_INVALID_ARG, "ws must be non-NULL");
+    const size_t need = align256((size_t)dims->batch * dims->heads * dr::kGroupModes * sizeof(uint32_t));
+    if (ws_bytes < need)
+      return fail(DR_ERR_CAPACITY, "workspace of %zu bytes below the %zu required", ws_bytes, need);
+  }
   dr::GroupCostParams p;
   p.row_ptr = row_ptr;
   p.kept_col = kept_col;
@@ -650,6 +662,18 @@ dr_status dr_query_groups(const dr_dims* dims, const dr_radial_cfg* cfg, const i
   const hipError_t e = dr::launch_group_choice(p, stream);
   if (e != hipSuccess) return hip_fail(e, "query grouping kernels");
   return ok();
+}
+
+dr_status dr_query_groups(const dr_dims* dims, const dr_radial_cfg* cfg, const int32_t* row_ptr, int64_t nnz,
+                          const int32_t* kept_col, const int32_t* kept_cnt, int32_t* group_mode, void* ws,
+                          size_t ws_bytes, hipStream_t stream) {
+  return query_groups_impl(dims, cfg, row_ptr, nnz, kept_col, kept_cnt, group_mode, ws, ws_bytes, false, stream);
+}
+
+dr_status dr_query_groups_noalloc(const dr_dims* dims, const dr_radial_cfg* cfg, const int32_t* row_ptr,
+                                  int64_t nnz, const int32_t* kept_col, const int32_t* kept_cnt, int32_t* group_mode,
+                                  hipStream_t stream) {
+  return query_groups_impl(dims, cfg, row_ptr, nnz, kept_col, kept_cnt, group_mode, nullptr, 0, true, stream);
 }
 
 dr_status dr_attn(const dr_dims* dims, int32_t seq_len, const void* q, const void* k, const void* v,

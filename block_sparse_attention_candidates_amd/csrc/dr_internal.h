@@ -363,5 +363,9 @@ hipError_t launch_select(const SelectParams& p, int B, hipStream_t stream);
 hipError_t launch_sparse_attn(const AttnParams& p, int D, int Bs, hipStream_t stream);
 hipError_t launch_dense_attn(const AttnParams& p, int D, hipStream_t stream);
 hipError_t launch_group_choice(const GroupCostParams& p, hipStream_t stream);
+// Library-held totals of dr_query_groups_noalloc: up to kGroupScratchBH (b, h)
+// pairs; the device address of the current device's array.
+constexpr int kGroupScratchBH = 65535;
+hipError_t group_scratch(uint32_t** out);
 
 }  // namespace dr

@@ -8,9 +8,14 @@
 // kGroupSample-th group of a (b, h) are summed and scaled to the mode's group
 // count; the mode with the smallest estimate (ties: the lower mode) is
 // written. Integer work (the comparison cross-multiplied), deterministic. The
-// outputs of the attention do not depend on the grouping, only its memory
-// traffic does.
+// grouping sets the attention's memory traffic; its outputs agree under every
+// grouping up to the order of accumulation.
+//
+// The same kernels also run on a library-held scratch array instead of a
+// caller workspace (group_scratch), for callers that cannot allocate.
 #include "dr_internal.h"
+
+#include <mutex>
 
 namespace dr {
 namespace {
@@ -46,7 +51,7 @@ __global__ __launch_bounds__(kThreads) void union_kernel(GroupCostParams p) {
     const int qb = group_block(p.grp, mode, g, lane);
     if (qb >= 0) {
       start = p.row_ptr[qb];
-      cnt = p.kept_cnt[(long long)bh * p.grp.Sb + qb];
+      cnt = min(p.kept_cnt[(long long)bh * p.grp.Sb + qb], p.row_ptr[qb + 1] - start);
     }
   }
   const int32_t* base = p.kept_col + (long long)bh * p.nnz;
@@ -91,7 +96,33 @@ __global__ __launch_bounds__(kThreads) void choose_kernel(GroupCostParams p) {
   p.group_mode[bh] = best;
 }
 
+// Union totals of every (b, h) and mode for the entry point that allocates
+// nothing: one array per GPU for the life of the process. Calls on one GPU
+// share it, so calls that overlap on one GPU race.
+__device__ __align__(256) uint32_t g_group_scratch[kGroupScratchBH * kGroupModes];
+
 }  // namespace
+
+hipError_t group_scratch(uint32_t** out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static uint32_t* ptr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptr[dev]) {
+    // the array's device address on the current device (the host-side name is
+    // only a stand-in, never a device address)
+    void* a = nullptr;
+    e = hipGetSymbolAddress(&a, HIP_SYMBOL(g_group_scratch));
+    if (e != hipSuccess) return e;
+    ptr[dev] = static_cast<uint32_t*>(a);
+  }
+  *out = ptr[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_group_choice(const GroupCostParams& p, hipStream_t stream) {
   const int n = p.BH * kGroupModes;

@@ -285,6 +285,20 @@ dr_status dr_query_groups(const dr_dims* dims, const dr_radial_cfg* cfg, const i
                           int64_t nnz, const int32_t* kept_col, const int32_t* kept_cnt,
                           int32_t* group_mode, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* dr_query_groups for callers that cannot allocate (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same
+ * computation and outputs, with the union totals held in a scratch array the
+ * library keeps in each GPU's memory for the life of the process (12 bytes per
+ * (b, h), 768 KiB per GPU for the limit B * H <= 65535; its device address is
+ * taken once per device, on the first call with that device current). It
+ * allocates nothing and calls no allocating routine. Every call on a GPU uses
+ * that GPU's one array: calls that overlap on one GPU (other streams, other
+ * threads) race and must not be issued; each call clears what it uses before
+ * use. `stream` must belong to the current device. */
+dr_status dr_query_groups_noalloc(const dr_dims* dims, const dr_radial_cfg* cfg, const int32_t* row_ptr,
+                                  int64_t nnz, const int32_t* kept_col, const int32_t* kept_cnt,
+                                  int32_t* group_mode, hipStream_t stream);
+
 /* dr_sparse_attn with the query blocks of (b, h) grouped by mode
  * group_mode[b * H + h] (device int32 [B * H], non-NULL; a value that is not a
  * mode with groups at this B_s means mode 0). Same results as dr_sparse_attn up

@@ -224,6 +224,24 @@ def test_proxy_error_validation(dynrad_lib):
     assert pl(ws_bytes=16) == L.DR_ERR_CAPACITY
 
 
+def test_query_groups_noalloc_validation(dynrad_lib):
+    """dr_query_groups_noalloc checks its arguments before any HIP call,
+    including the (b, h) limit of the library's scratch array."""
+    import block_sparse_attention_candidates_amd as dr
+    from block_sparse_attention_candidates_amd import _lib as L
+    cfg = dr.radial_cfg(4, 64, 32, 1.0, 2.0)
+    P = ctypes.c_void_p(4096)
+
+    def call(B=1, H=2, nnz=64, rp=P, kc=P, kn=P, gm=P):
+        dims = L.Dims(B, H, 64, 0)
+        return dynrad_lib.dr_query_groups_noalloc(ctypes.byref(dims), ctypes.byref(cfg), rp, nnz, kc, kn, gm, None)
+    assert call(rp=None) == L.DR_ERR_INVALID_ARG
+    assert call(gm=None) == L.DR_ERR_INVALID_ARG
+    assert call(nnz=0) == L.DR_ERR_INVALID_ARG
+    assert call(B=256, H=256) == L.DR_ERR_UNSUPPORTED          # 65536 (b, h) pairs
+    assert b"65535" in dynrad_lib.dr_last_error()
+
+
 def test_wait_limit_and_report_validation(dynrad_lib):
     """dr_set_wait_limit accepts [0, 2^31); dr_wait_report rejects a NULL
     flags pointer before any HIP call."""
