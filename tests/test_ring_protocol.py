@@ -41,11 +41,17 @@ class Violation(AssertionError):
 
 
 def run_schedule(n_units, needs, n_loaders, inflight, n_slots, rng, publish_rule=True, early_publish=False,
-                 early_progress=False, max_steps=200000):
+                 early_progress=False, lag=False, lag_flush=True, max_steps=200000):
     """One random execution. needs[w]: ascending units compute wave w reads.
-    The last three switches plant protocol mistakes: no publish check before
-    slot reuse; a vmcnt count one too high (a unit published before its copies
-    land); a wave announcing its next unit before its read has finished."""
+    publish_rule, early_publish and early_progress plant protocol mistakes: no
+    publish check before slot reuse; a vmcnt count one too high (a unit
+    published before its copies land); a wave announcing its next unit before
+    its read has finished. lag: each wave reads a unit in two parts, the
+    second (the V tile of the lagged PV product) during its next unit's turn;
+    while it waits for that next unit its progress word still names the
+    pending unit, unless the two lie more than n_slots - 1 apart, when it first
+    finishes the pending read (lag_flush; False plants the mistake of always
+    holding it)."""
     W = len(needs)
     ready = [-1] * n_slots
     prog = [0] * W
@@ -62,6 +68,7 @@ def run_schedule(n_units, needs, n_loaders, inflight, n_slots, rng, publish_rule
     C_i = [0] * W                      # index into needs[w]
     C_phase = ["announce"] * W
     read_log = [[] for _ in range(W)]
+    pend = [None] * W                  # lag: unit whose second part is still to be read
 
     def publish(l, u):
         ready[u % n_slots] = u
@@ -126,6 +133,11 @@ def run_schedule(n_units, needs, n_loaders, inflight, n_slots, rng, publish_rule
         landed[s] = u
         return True
 
+    def check_landed(w, u):
+        s = u % n_slots
+        if writing[s] is not None or landed[s] != u:
+            raise Violation(f"wave {w} reads unit {u} from slot {s}: landed {landed[s]}, in flight {writing[s]}")
+
     def compute_step(w):
         ph = C_phase[w]
         i = C_i[w]
@@ -133,27 +145,51 @@ def run_schedule(n_units, needs, n_loaders, inflight, n_slots, rng, publish_rule
             return False
         if ph == "announce":
             if i >= len(needs[w]):
+                if pend[w] is not None:     # the last pending read
+                    C_phase[w] = "flush_end"
+                    return True
                 prog[w] = DONE
                 C_phase[w] = "done"
                 return True
-            prog[w] = needs[w][i]
+            u = needs[w][i]
+            if pend[w] is not None and lag_flush and u - pend[w] > n_slots - 1:
+                C_phase[w] = "flush"
+                return True
+            prog[w] = pend[w] if pend[w] is not None else u
             C_phase[w] = "wait"
+            return True
+        if ph in ("flush", "flush_end"):
+            # the pending unit's second read, then release it
+            pu = pend[w]
+            check_landed(w, pu)
+            pend[w] = None
+            C_phase[w] = "announce" if ph == "flush" else "announce"
             return True
         u = needs[w][i]
         s = u % n_slots
         if ph == "wait":
             if ready[s] != u:
                 return False
-            if writing[s] is not None or landed[s] != u:
-                raise Violation(f"wave {w} reads unit {u} from slot {s}: landed {landed[s]}, in flight {writing[s]}")
+            check_landed(w, u)
             readers[s][w] = u
+            if pend[w] is not None:
+                readers[pend[w] % n_slots][w] = pend[w]
             C_phase[w] = "read"
             if early_progress:
                 prog[w] = needs[w][i + 1] if i + 1 < len(needs[w]) else DONE
             return True
         if ph == "read":
+            # this unit's first part and the pending unit's second part are read;
+            # the pending unit's reads have finished before the progress store
             del readers[s][w]
+            if pend[w] is not None:
+                pu = pend[w]
+                check_landed(w, pu)
+                del readers[pu % n_slots][w]
             read_log[w].append(u)
+            if lag:
+                pend[w] = u
+                prog[w] = u
             C_i[w] = i + 1
             C_phase[w] = "announce"
             return True
@@ -244,6 +280,40 @@ def test_ring_protocol_without_publish_rule_fails():
         needs = random_needs(rng, n, 8, 0.05)
         try:
             run_schedule(n, needs, 4, 1, 9, rng, publish_rule=False)
+        except Violation:
+            found = True
+            break
+    assert found
+
+
+@pytest.mark.parametrize("loaders,inflight,slots", [(4, 1, 9), (4, 1, 6), (4, 1, 8)])
+def test_ring_protocol_lagged_pv(loaders, inflight, slots):
+    """A variant of the protocol that was timed and not adopted (no gain for
+    the dense kernel, slower sparse launches): the PV product of a unit lags
+    one unit behind, so a wave keeps its previous unit claimed (progress word
+    = that unit) while it waits for the next one, and finishes the previous
+    unit first when the two are more than slots - 1 apart. No slot is
+    refilled under a pending read, and no schedule deadlocks."""
+    rng = np.random.default_rng(1000 + slots)
+    for trial in range(150):
+        n = int(rng.integers(1, 41))
+        density = float(rng.choice([0.05, 0.2, 0.5, 1.0]))
+        needs = random_needs(rng, n, 8, density)
+        run_schedule(n, needs, loaders, inflight, slots, rng, lag=True)
+
+
+def test_ring_protocol_lag_without_flush_deadlocks():
+    """Holding the pending unit while waiting for a unit more than slots - 1
+    further on deadlocks: that unit's slot still holds a unit between the two,
+    which the loaders may not replace while the wave's progress word names the
+    pending unit. The model finds it."""
+    rng = np.random.default_rng(11)
+    found = False
+    for trial in range(400):
+        n = int(rng.integers(20, 41))
+        needs = random_needs(rng, n, 8, 0.1)
+        try:
+            run_schedule(n, needs, 4, 1, 9, rng, lag=True, lag_flush=False)
         except Violation:
             found = True
             break
