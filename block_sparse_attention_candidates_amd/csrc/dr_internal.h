@@ -277,6 +277,7 @@ struct TokParams {
   double gamma, lambda, theta_c, theta_m, tau_near, tau_far, eps;
   float scale;         // 1 / (sqrt(d_k) * H_f)
   int spin_limit;      // polls before a bounded wait gives up (>= 1)
+  int nb;              // key-block ring buffers (set at launch)
   // workspace
   TokStat* part;       // [B][n_wg][kTokSplit][FR][Nf] workgroup partials
   float* thr;          // [B][Nf][Nf] threshold in score units (+inf: no t > 1 pair)

@@ -8,8 +8,8 @@
 //   stats:    a workgroup of 8 wavefronts owns 256 query tokens (8 / 4 query
 //             blocks); it walks the union of their candidate key blocks in
 //             ascending order, staging each key block of the H_f fused heads in
-//             an LDS ring (XOR-swizzled rows, claim-based loading, see
-//             ring_service), and every wave whose
+//             an LDS ring (XOR-swizzled rows) filled by 4 loader wavefronts
+//             (see ring_load), and every compute wave whose
 //             query block has the key block as a candidate computes its 32x32
 //             token tiles of s = (1/H_f) sum_h Q^h K^h^T / sqrt(d_k) (Eq. 9) with
 //             v_mfma_f32_32x32x16_bf16. Token pairs of P(i, j) with t > 1 feed
@@ -45,10 +45,12 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
-constexpr int kWaves = 8;
-constexpr int kThreads = kWaves * 64;
+constexpr int kWaves = 8;              // compute wavefronts
+constexpr int kLoadWaves = 4;          // loader wavefronts (key-block copies only)
+constexpr int kThreads = (kWaves + kLoadWaves) * 64;
 constexpr int kRows = kWaves * 32;      // query tokens per workgroup
 constexpr int kRingMax = 16;            // ring depth limit (key blocks)
+constexpr int kTokLdsBytes = 160 * 1024; // LDS per workgroup on gfx950
 constexpr int kDone = 0x3fffffff;       // progress of a wave that reads no more blocks
 
 typedef int intx4 __attribute__((ext_vector_type(4)));
@@ -122,8 +124,6 @@ struct Geo {
   static constexpr int KBUF = HF * BS * RB;         // one key block, all fused heads
   static constexpr int QB = kRows / BS;             // query blocks per workgroup
   static constexpr int WPQ = BS / 32;               // waves per query block
-  // key-block ring in LDS: NB buffers within a 96 KB budget (at least 2)
-  static constexpr int NB = 98304 / KBUF < 2 ? 2 : (98304 / KBUF > kRingMax ? kRingMax : 98304 / KBUF);
   static constexpr int NI = KBUF / 1024;            // 1 KB direct-to-LDS loads per block
 };
 
@@ -309,7 +309,8 @@ template <int D, int BS, int HF>
 struct Lds {
   using G = Geo<D, BS, HF>;
   int nword;
-  unsigned char* ring;  // [NB][KBUF]
+  int nb;               // ring buffers (chosen at launch: the deepest ring that fits)
+  unsigned char* ring;  // [nb][KBUF]
   unsigned int* bits;   // [QB][nword]
   int* pre;             // [QB][nword]
   unsigned int* uword;  // [nword]
@@ -323,12 +324,13 @@ struct Lds {
   int* next_issue;      // next step to be claimed for loading
   unsigned char* rest;  // 16-byte aligned
   __host__ __device__ static size_t align16(size_t x) { return (x + 15) & ~(size_t)15; }
-  __device__ unsigned char* kbuf(int j) const { return ring + (j % G::NB) * G::KBUF; }
+  __device__ unsigned char* kbuf(int j) const { return ring + (j % nb) * G::KBUF; }
   __host__ __device__ static int max_steps(int Sb) { return Sb / kTokSplit + 2; }
-  __device__ Lds(unsigned char* smem, int Sb, int Nf) {
+  __device__ Lds(unsigned char* smem, int Sb, int Nf, int nb_) {
     nword = (Sb + 31) >> 5;
+    nb = nb_;
     ring = smem;
-    bits = reinterpret_cast<unsigned int*>(smem + G::NB * G::KBUF);
+    bits = reinterpret_cast<unsigned int*>(smem + (size_t)nb * G::KBUF);
     pre = reinterpret_cast<int*>(bits + G::QB * nword);
     uword = reinterpret_cast<unsigned int*>(pre + G::QB * nword);
     upre = reinterpret_cast<int*>(uword + nword);
@@ -341,13 +343,23 @@ struct Lds {
     next_issue = ready + kRingMax;
     rest = reinterpret_cast<unsigned char*>(prog) + kCtlBytes;
   }
-  __host__ __device__ static size_t bytes(int Sb, int Nf) {
+  __host__ __device__ static size_t bytes(int Sb, int Nf, int nb) {
     const size_t nw = (size_t)(Sb + 31) / 32;
-    const size_t used = (size_t)G::NB * G::KBUF + (size_t)G::QB * nw * 8 + nw * 8 + (size_t)max_steps(Sb) * 8 +
+    const size_t used = (size_t)nb * G::KBUF + (size_t)G::QB * nw * 8 + nw * 8 + (size_t)max_steps(Sb) * 8 +
                         (size_t)Nf * 8;
     return ((used + 15) & ~(size_t)15) + kCtlBytes;
   }
 };
+
+// Mark-kernel LDS beyond the shared layout: thresholds and served flags per
+// frame pair, the column counts and arrivals per ring buffer (B_s > 32), and
+// the split's flags.
+template <int D, int BS, int HF>
+__host__ __device__ size_t mark_extra(int Sb, int Nf, int FR, int nb) {
+  using G = Geo<D, BS, HF>;
+  return (size_t)FR * Nf * 8 + (G::WPQ > 1 ? (size_t)G::QB * nb * (BS + 1) * 4 : 0) +
+         (size_t)G::QB * Lds<D, BS, HF>::max_steps(Sb);
+}
 
 // First union step of key-range split `split` (kTokSplit workgroups share one
 // query group's walk, each taking a contiguous run of its steps).
@@ -355,75 +367,77 @@ __device__ __forceinline__ int step_begin(int nsteps, int split) {
   return (int)(((long long)nsteps * split) / kTokSplit);
 }
 
-// The key-block ring without workgroup barriers. Waves walk only the steps
-// their own query block needs. A wave claims the next step in order with an
-// LDS compare-and-swap when its buffer is free (every wave past the step it
-// held, and that step published), issues its direct-to-LDS copies, and
-// publishes it at its next service point after s_waitcnt vmcnt(0): its only
-// vector-memory operations in the walk are these copies. Every wave services
-// before each step and while waiting, so the lowest wanted step can always be
-// claimed (its buffer is free); waits are bounded.
+// The key-block ring without workgroup barriers. Loader wavefront l copies
+// the steps l, l + kLoadWaves, ... of the split in order, one step in flight:
+// before issuing a step it waits (s_waitcnt vmcnt) for its previous step's
+// copies and publishes that step, then waits until the step's buffer is free
+// (every compute wave past the step the buffer held, and that step
+// published: a step no wave needs could otherwise still be landing). Compute
+// waves walk only the steps their own query block needs: announce the step,
+// wait until it is published, read. Waits are bounded.
 template <int D, int BS, int HF>
-__device__ __forceinline__ void ring_service(const TokParams& p, int b, const Lds<D, BS, HF>& L, int n, int& pending,
-                                             int lane) {
-  using G = Geo<D, BS, HF>;
-  if (pending >= 0) {
+__device__ __forceinline__ void ring_load(const TokParams& p, int b, const Lds<D, BS, HF>& L, int n, int l, int lane) {
+  bool gave_up = false;
+  int prev = -1;
+  for (int j = l; j < n; j += kLoadWaves) {
+    if (prev >= 0) {
+      wait_vmcnt<0>();
+      compiler_fence();
+      st_relaxed(&L.ready[prev % L.nb], prev);
+    }
+    int spins = 0;
+    while (true) {
+      // explicit LDS loads (a generic load would also wait for copies in flight)
+      const volatile DR_LDS intx4* pv = (const volatile DR_LDS intx4*)(L.prog);
+      const intx4 a = pv[0];
+      const intx4 c = pv[1];
+      const int mn = uniform(min(min(min(a[0], a[1]), min(a[2], a[3])), min(min(c[0], c[1]), min(c[2], c[3]))));
+      const bool free_buf =
+          mn >= j - L.nb + 1 && (j < L.nb || uniform(ld_relaxed(&L.ready[j % L.nb])) == j - L.nb);
+      if (free_buf) break;
+      if (++spins > p.spin_limit) {
+        gave_up = true;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+    compiler_fence();
+    __builtin_amdgcn_s_setprio(2);
+    issue_block<D, BS, HF>(p, b, uniform(L.steps[j]), L.kbuf(j), lane);
+    __builtin_amdgcn_s_setprio(0);
+    prev = j;
+  }
+  if (prev >= 0) {
     wait_vmcnt<0>();
     compiler_fence();
-    st_relaxed(&L.ready[pending % G::NB], pending);
-    pending = -1;
+    st_relaxed(&L.ready[prev % L.nb], prev);
   }
-  const int j = uniform(ld_relaxed(L.next_issue));
-  if (j >= n) return;
-  // explicit LDS loads (a generic load would also wait for copies in flight)
-  const volatile DR_LDS intx4* pv = (const volatile DR_LDS intx4*)(L.prog);
-  const intx4 a = pv[0];
-  const intx4 c = pv[1];
-  const int mn = uniform(min(min(min(a[0], a[1]), min(a[2], a[3])), min(min(c[0], c[1]), min(c[2], c[3]))));
-  if (mn < j - G::NB + 1) return;
-  if (j >= G::NB && uniform(ld_relaxed(&L.ready[j % G::NB])) != j - G::NB) return;
-  int old = 0;
-  if (lane == 0) old = atomicCAS(L.next_issue, j, j + 1);
-  if (uniform(old) != j) return;
-  compiler_fence();
-  __builtin_amdgcn_s_setprio(2);
-  issue_block<D, BS, HF>(p, b, uniform(L.steps[j]), L.kbuf(j), lane);
-  __builtin_amdgcn_s_setprio(0);
-  pending = j;
+  if (gave_up && lane == 0) atomicOr(&g_tok_wait_flags, kWaitToken);
 }
 
-// Announce step j, then wait (servicing) until its key block is in the ring.
+// Announce step j, then wait until its key block is in the ring.
 template <int D, int BS, int HF>
-__device__ __forceinline__ void ring_wait(const TokParams& p, int b, const Lds<D, BS, HF>& L, int n, int& pending,
-                                          int wave, int lane, int j) {
-  using G = Geo<D, BS, HF>;
+__device__ __forceinline__ void ring_wait(const TokParams& p, const Lds<D, BS, HF>& L, int wave, int lane, int j,
+                                          bool& gave_up) {
   compiler_fence();
   st_relaxed(&L.prog[wave], j);
-  ring_service<D, BS, HF>(p, b, L, n, pending, lane);
   int spins = 0;
-  while (ld_relaxed(&L.ready[j % G::NB]) != j) {
+  while (ld_relaxed(&L.ready[j % L.nb]) != j) {
     if (++spins > p.spin_limit) {
-      if (lane == 0) atomicOr(&g_tok_wait_flags, kWaitToken);
+      gave_up = true;
       break;
     }
-    ring_service<D, BS, HF>(p, b, L, n, pending, lane);
     __builtin_amdgcn_s_sleep(1);
   }
   compiler_fence();
 }
 
-// Leave the walk: no more reads, and this wave's last copy published.
+// Leave the walk: no more reads.
 template <int D, int BS, int HF>
-__device__ __forceinline__ void ring_leave(const Lds<D, BS, HF>& L, int& pending, int wave) {
-  using G = Geo<D, BS, HF>;
+__device__ __forceinline__ void ring_leave(const Lds<D, BS, HF>& L, int wave, int lane, bool gave_up) {
   compiler_fence();
   st_relaxed(&L.prog[wave], kDone);
-  if (pending >= 0) {
-    wait_vmcnt<0>();
-    compiler_fence();
-    st_relaxed(&L.ready[pending % G::NB], pending);
-    pending = -1;
-  }
+  if (gave_up && lane == 0) atomicOr(&g_tok_wait_flags, kWaitToken);
 }
 
 // Visit the steps of this wave's query block (bitmap row `mine`) within the
@@ -543,7 +557,7 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(TokParams p) {
   using G = Geo<D, BS, HF>;
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ int s_nsteps;
-  Lds<D, BS, HF> L(smem, p.Sb, p.Nf);
+  Lds<D, BS, HF> L(smem, p.Sb, p.Nf, p.nb);
   Stat* acc_l = reinterpret_cast<Stat*>(L.rest);     // [kWaves][2][Nf]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5;
   const int wg = blockIdx.x / kTokSplit, split = blockIdx.x - wg * kTokSplit, b = blockIdx.y;
@@ -554,10 +568,10 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(TokParams p) {
   const int qb = wave / G::WPQ, sub = wave - qb * G::WPQ;
   const int a = a0 + qb;
   const int q0 = a * BS + 32 * sub;
-  const bool active_wave = a < p.Sb && q0 < p.S;
+  const bool active_wave = wave < kWaves && a < p.Sb && q0 < p.S;
   bf16x8 qf[HF][D / 16];
   if (active_wave) load_q<D, HF>(p, b, q0, lane, qf);
-  wait_vmcnt<0>();   // Q resident before the ring's loads are counted
+  wait_vmcnt<0>();
   const int f0w = q0 / p.Nt;
   const FrameAt qat{f0w, q0 - f0w * p.Nt};   // frame and index of the wave's first row
   Stat* mine = acc_l + wave * 2 * p.Nf;
@@ -567,8 +581,9 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(TokParams p) {
   // ascending order and the 32 keys of a tile span at most two adjacent frames,
   // so the set of parity kp holds one key frame (tag0 / tag1) at a time; it is
   // reduced over the wave and merged into the wave's LDS statistics once the
-  // walk has passed that frame. Sums are float64 power sums of the float32
-  // scores; the highest score keeps its position for safeguard (ii).
+  // walk has passed that frame. Per tile, a lane sums its (at most 16) logits
+  // and their squares in float32; the set adds those tile sums, scaled, as
+  // float64 power sums. The highest score keeps its position for safeguard (ii).
   double rs[4] = {0.0, 0.0, 0.0, 0.0}, rq[4] = {0.0, 0.0, 0.0, 0.0};
   int rn[4] = {0, 0, 0, 0};
   float rm[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
@@ -617,16 +632,17 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(TokParams p) {
       }
   };
 
-  // key blocks stream through the LDS ring; this wave visits only its own
-  int pending = -1;
+  // key blocks stream through the LDS ring; a compute wave visits only its own
   const int j0 = step_begin(s_nsteps, split);
+  bool gave_up = false;
+  if (wave >= kWaves) ring_load<D, BS, HF>(p, b, L, n, wave - kWaves, lane);
   if (active_wave) {
     walk_own(L, L.bits + qb * L.nword, n, j0, [&](int j, int kb) __attribute__((always_inline)) {
-      ring_wait<D, BS, HF>(p, b, L, n, pending, wave, lane, j);
+      ring_wait<D, BS, HF>(p, L, wave, lane, j, gave_up);
       const unsigned char* kbuf = L.kbuf(j);
       const int info = L.sinfo[j];
       const FrameAt kat0{info & 255, info >> 8};
-#pragma unroll
+#pragma unroll 1
       for (int ksub = 0; ksub < BS / 32; ++ksub) {
         const int ktok0 = kb * BS + 32 * ksub;
         if (ktok0 >= p.S) break;
@@ -679,7 +695,7 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(TokParams p) {
         const int w0 = t0 < p.Nf ? L.s_w[t0] : 0, w1 = t1 < p.Nf ? L.s_w[t1] : 0;
         // per query frame f0 (suffix 0) and f0 + 1 (suffix 1); scalars, so that
         // a lane-dependent choice never indexes memory
-        double ts0 = 0.0, tq0 = 0.0, ts1 = 0.0, tq1 = 0.0;
+        float ts0 = 0.f, tq0 = 0.f, ts1 = 0.f, tq1 = 0.f;
         int tn0 = 0, tn1 = 0;
         float tm0 = -INFINITY, tm1 = -INFINITY;
         unsigned int tl0 = 0xffffffffu, tl1 = 0xffffffffu;
@@ -692,21 +708,21 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(TokParams p) {
           if (second) u -= p.Nt;
           const int du = u > f.uk ? u - f.uk : f.uk - u;
           if (!(second ? (ok1 && du <= w1) : (ok0 && du <= w0))) continue;
-          const float v = acc[i] * p.scale;
-          const double d = (double)v;
+          const float a = acc[i];
+          const float v = a * p.scale;
           const unsigned int loc = (unsigned)(u * p.Nt + f.uk);
           // rows ascend with i: the first maximum has the lowest position
           if (second) {
-            ts1 += d;
-            tq1 = fma(d, d, tq1);
+            ts1 += a;
+            tq1 = fmaf(a, a, tq1);
             ++tn1;
             if (v > tm1) {
               tm1 = v;
               tl1 = loc;
             }
           } else {
-            ts0 += d;
-            tq0 = fma(d, d, tq0);
+            ts0 += a;
+            tq0 = fmaf(a, a, tq0);
             ++tn0;
             if (v > tm0) {
               tm0 = v;
@@ -715,12 +731,13 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(TokParams p) {
           }
         }
         const int kp = f.fk & 1;
-        if (tn0 > 0) add(kp, ts0, tq0, tn0, tm0, tl0);
-        if (tn1 > 0) add(2 + kp, ts1, tq1, tn1, tm1, tl1);
+        const double sc = (double)p.scale;
+        if (tn0 > 0) add(kp, (double)ts0 * sc, (double)tq0 * (sc * sc), tn0, tm0, tl0);
+        if (tn1 > 0) add(2 + kp, (double)ts1 * sc, (double)tq1 * (sc * sc), tn1, tm1, tl1);
       }
     });
   }
-  ring_leave(L, pending, wave);
+  if (wave < kWaves) ring_leave(L, wave, lane, gave_up);
   flush(0);
   flush(1);
   __syncthreads();
@@ -801,19 +818,19 @@ __global__ __launch_bounds__(kThreads) void mark_kernel(TokParams p) {
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ int s_nsteps;
   __shared__ int min_c[BS + 1], min_a[BS + 1], pos_lo[G::QB];
-  Lds<D, BS, HF> L(smem, p.Sb, p.Nf);
+  Lds<D, BS, HF> L(smem, p.Sb, p.Nf, p.nb);
   const int MS = Lds<D, BS, HF>::max_steps(p.Sb);
   float* thr_l = reinterpret_cast<float*>(L.rest);                      // [FR][Nf]
   int* served_l = reinterpret_cast<int*>(thr_l + p.FR * p.Nf);          // [FR][Nf]
-  int* colcnt = served_l + p.FR * p.Nf;                                 // [QB][NB][BS] when BS > 32
-  int* arrive = colcnt + (G::WPQ > 1 ? G::QB * G::NB * BS : 0);          // [QB][NB] when BS > 32
-  unsigned char* flags_l = reinterpret_cast<unsigned char*>(arrive + (G::WPQ > 1 ? G::QB * G::NB : 0));  // [QB][MS]
+  int* colcnt = served_l + p.FR * p.Nf;                                 // [QB][nb][BS] when BS > 32
+  int* arrive = colcnt + (G::WPQ > 1 ? G::QB * L.nb * BS : 0);           // [QB][nb] when BS > 32
+  unsigned char* flags_l = reinterpret_cast<unsigned char*>(arrive + (G::WPQ > 1 ? G::QB * L.nb : 0));  // [QB][MS]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5;
   const int wg = blockIdx.x / kTokSplit, split = blockIdx.x - wg * kTokSplit, b = blockIdx.y;
   const int a0 = wg * G::QB;
   const int f_lo = (a0 * BS) / p.Nt;
   if (G::WPQ > 1)
-    for (int i = tid; i < G::QB * G::NB * (BS + 1); i += kThreads) colcnt[i] = 0;   // counts and arrivals
+    for (int i = tid; i < G::QB * L.nb * (BS + 1); i += kThreads) colcnt[i] = 0;   // counts and arrivals
   for (int i = tid; i < p.FR * p.Nf; i += kThreads) {
     const int fr = i / p.Nf, fk = i - fr * p.Nf;
     const int fq = f_lo + fr;
@@ -837,13 +854,13 @@ __global__ __launch_bounds__(kThreads) void mark_kernel(TokParams p) {
   const int qb = wave / G::WPQ, sub = wave - qb * G::WPQ;
   const int a = a0 + qb;
   const int q0 = a * BS + 32 * sub;
-  const bool active_wave = a < p.Sb && q0 < p.S;
+  const bool active_wave = wave < kWaves && a < p.Sb && q0 < p.S;
   const int nq = a < p.Sb ? min(BS, p.S - a * BS) : 0;
   const int n_sub = (nq + 31) / 32;   // waves of this query block holding rows
   const FrameAt qat{q0 / p.Nt, q0 - (q0 / p.Nt) * p.Nt};   // frame and index of the wave's first row
   bf16x8 qf[HF][D / 16];
   if (active_wave) load_q<D, HF>(p, b, q0, lane, qf);
-  wait_vmcnt<0>();   // Q resident before the ring's loads are counted
+  wait_vmcnt<0>();
 
   // selected count of key column lane % 32 of the tile (q0, ktok0) over the
   // wave's 32 query rows (the same value in both half-waves); marks served
@@ -884,11 +901,12 @@ __global__ __launch_bounds__(kThreads) void mark_kernel(TokParams p) {
   // key blocks stream through the LDS ring; this wave visits only its own.
   // B_s > 32: the waves of a query block add their column counts in LDS (one
   // count row per ring buffer) and the last one to arrive decides.
-  int pending = -1;
   const int j0 = step_begin(s_nsteps, split);
+  bool gave_up = false;
+  if (wave >= kWaves) ring_load<D, BS, HF>(p, b, L, n, wave - kWaves, lane);
   if (active_wave) {
     walk_own(L, L.bits + qb * L.nword, n, j0, [&](int j, int kb) __attribute__((always_inline)) {
-      ring_wait<D, BS, HF>(p, b, L, n, pending, wave, lane, j);
+      ring_wait<D, BS, HF>(p, L, wave, lane, j, gave_up);
       const unsigned char* kbuf = L.kbuf(j);
       const int nk = min(BS, p.S - kb * BS);
       const int info = L.sinfo[j];
@@ -899,8 +917,8 @@ __global__ __launch_bounds__(kThreads) void mark_kernel(TokParams p) {
         const int n_act = __popcll(__ballot(lane < nk && c >= min_c[nq]));
         if (lane == 0) flags_l[qb * MS + pos_of(qb, kb) - pos_lo[qb]] = n_act >= min_a[nk] ? 1 : 0;
       } else {
-        int* cnt = colcnt + (qb * G::NB + j % G::NB) * BS;
-#pragma unroll
+        int* cnt = colcnt + (qb * L.nb + j % L.nb) * BS;
+#pragma unroll 1
         for (int ksub = 0; ksub < BS / 32; ++ksub) {
           const int ktok0 = kb * BS + 32 * ksub;
           if (ktok0 >= p.S) break;
@@ -910,7 +928,7 @@ __global__ __launch_bounds__(kThreads) void mark_kernel(TokParams p) {
         // LDS operations of a wave complete in order: its counts are in
         // before its arrival is counted
         int arrived = 0;
-        if (lane == 0) arrived = atomicAdd(&arrive[qb * G::NB + j % G::NB], 1) + 1;
+        if (lane == 0) arrived = atomicAdd(&arrive[qb * L.nb + j % L.nb], 1) + 1;
         if (uniform(arrived) == n_sub) {
           compiler_fence();
           int n_act = 0;
@@ -923,13 +941,13 @@ __global__ __launch_bounds__(kThreads) void mark_kernel(TokParams p) {
           }
           if (lane == 0) {
             flags_l[qb * MS + pos_of(qb, kb) - pos_lo[qb]] = n_act >= min_a[nk] ? 1 : 0;
-            arrive[qb * G::NB + j % G::NB] = 0;
+            arrive[qb * L.nb + j % L.nb] = 0;
           }
         }
       }
     });
   }
-  ring_leave(L, pending, wave);
+  if (wave < kWaves) ring_leave(L, wave, lane, gave_up);
   __syncthreads();
   // write out this split's flags (a contiguous run of each candidate row) and
   // the served frame pairs
@@ -1051,13 +1069,35 @@ __global__ __launch_bounds__(64) void fallback_kernel(TokParams p) {
 
 // Pass 5 (ordered compaction of the flags into kept lists of every head) is
 // flag_compact_kernel below.
+// LDS of the stats and mark kernels with a ring of nb buffers, static arrays
+// included; the larger of the two.
 template <int D, int BS, int HF>
-hipError_t launch_all(const TokParams& p, int B, hipStream_t stream) {
+size_t lds_need(int Sb, int Nf, int FR, int nb) {
   using G = Geo<D, BS, HF>;
-  const size_t base = Lds<D, BS, HF>::bytes(p.Sb, p.Nf);
+  const size_t base = Lds<D, BS, HF>::bytes(Sb, Nf, nb);
+  const size_t stats = base + (size_t)kWaves * 2 * Nf * sizeof(Stat) + 16;
+  const size_t mark = base + mark_extra<D, BS, HF>(Sb, Nf, FR, nb) + (size_t)(2 * (BS + 1) + G::QB) * 4 + 16;
+  return stats > mark ? stats : mark;
+}
+
+// The deepest ring (at most kRingMax buffers) whose kernels fit in LDS; 0 if
+// not even two buffers fit.
+template <int D, int BS, int HF>
+int ring_depth(int Sb, int Nf, int FR) {
+  for (int nb = kRingMax; nb >= 2; --nb)
+    if (lds_need<D, BS, HF>(Sb, Nf, FR, nb) <= (size_t)kTokLdsBytes) return nb;
+  return 0;
+}
+
+// Pass 5 (ordered compaction of the flags into kept lists of every head) is
+// flag_compact_kernel below.
+template <int D, int BS, int HF>
+hipError_t launch_all(TokParams p, int B, hipStream_t stream) {
+  p.nb = ring_depth<D, BS, HF>(p.Sb, p.Nf, p.FR);
+  if (p.nb < 2) return hipErrorInvalidValue;
+  const size_t base = Lds<D, BS, HF>::bytes(p.Sb, p.Nf, p.nb);
   const size_t lds_stats = base + (size_t)kWaves * 2 * p.Nf * sizeof(Stat);
-  const size_t lds_mark = base + (size_t)p.FR * p.Nf * 8 + (G::WPQ > 1 ? (size_t)G::QB * G::NB * (BS + 1) * 4 : 0) +
-                          (size_t)G::QB * Lds<D, BS, HF>::max_steps(p.Sb);
+  const size_t lds_mark = base + mark_extra<D, BS, HF>(p.Sb, p.Nf, p.FR, p.nb);
   const dim3 grid((unsigned)(p.n_wg * kTokSplit), (unsigned)B);
   hipLaunchKernelGGL((stats_kernel<D, BS, HF>), grid, dim3(kThreads), lds_stats, stream, p);
   hipError_t e = hipGetLastError();
@@ -1076,24 +1116,14 @@ hipError_t launch_all(const TokParams& p, int B, hipStream_t stream) {
 
 }  // namespace
 
-template <int D, int BS, int HF>
-size_t lds_need(int Sb, int Nf, int FR) {
-  using G = Geo<D, BS, HF>;
-  const size_t base = Lds<D, BS, HF>::bytes(Sb, Nf);
-  const size_t stats = base + (size_t)kWaves * 2 * Nf * sizeof(Stat);
-  // (+ the static arrays of the mark kernel: the integer thresholds and the step count)
-  const size_t mark = base + (size_t)FR * Nf * 8 + (G::WPQ > 1 ? (size_t)G::QB * G::NB * (BS + 1) * 4 : 0) +
-                      (size_t)G::QB * Lds<D, BS, HF>::max_steps(Sb) + (size_t)(2 * (BS + 1) + G::QB) * 4 + 16;
-  return stats > mark ? stats : mark;
-}
-
+// LDS the token selector needs at its shallowest ring (two buffers).
 size_t token_lds_bytes(int D, int Bs, int Hf, int Sb, int Nf, int FR) {
-  if (D == 128 && Bs == 128) return Hf == 1 ? lds_need<128, 128, 1>(Sb, Nf, FR) : lds_need<128, 128, 2>(Sb, Nf, FR);
-  if (D == 64 && Bs == 128) return Hf == 1 ? lds_need<64, 128, 1>(Sb, Nf, FR) : lds_need<64, 128, 2>(Sb, Nf, FR);
-  if (D == 128 && Bs == 32) return Hf == 1 ? lds_need<128, 32, 1>(Sb, Nf, FR) : lds_need<128, 32, 2>(Sb, Nf, FR);
-  if (D == 128 && Bs == 64) return Hf == 1 ? lds_need<128, 64, 1>(Sb, Nf, FR) : lds_need<128, 64, 2>(Sb, Nf, FR);
-  if (D == 64 && Bs == 32) return Hf == 1 ? lds_need<64, 32, 1>(Sb, Nf, FR) : lds_need<64, 32, 2>(Sb, Nf, FR);
-  return Hf == 1 ? lds_need<64, 64, 1>(Sb, Nf, FR) : lds_need<64, 64, 2>(Sb, Nf, FR);
+  if (D == 128 && Bs == 128) return Hf == 1 ? lds_need<128, 128, 1>(Sb, Nf, FR, 2) : lds_need<128, 128, 2>(Sb, Nf, FR, 2);
+  if (D == 64 && Bs == 128) return Hf == 1 ? lds_need<64, 128, 1>(Sb, Nf, FR, 2) : lds_need<64, 128, 2>(Sb, Nf, FR, 2);
+  if (D == 128 && Bs == 32) return Hf == 1 ? lds_need<128, 32, 1>(Sb, Nf, FR, 2) : lds_need<128, 32, 2>(Sb, Nf, FR, 2);
+  if (D == 128 && Bs == 64) return Hf == 1 ? lds_need<128, 64, 1>(Sb, Nf, FR, 2) : lds_need<128, 64, 2>(Sb, Nf, FR, 2);
+  if (D == 64 && Bs == 32) return Hf == 1 ? lds_need<64, 32, 1>(Sb, Nf, FR, 2) : lds_need<64, 32, 2>(Sb, Nf, FR, 2);
+  return Hf == 1 ? lds_need<64, 64, 1>(Sb, Nf, FR, 2) : lds_need<64, 64, 2>(Sb, Nf, FR, 2);
 }
 
 // One wavefront per (b, query block): flags -> ascending kept list, by ballots.

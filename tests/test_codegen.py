@@ -1,10 +1,14 @@
 """Checks on the gfx950 code the compiler generates for the HIP sources (host
 only: hipcc cross-compiles, nothing runs on a GPU).
 
-* No kernel spills to scratch memory: the ring protocols of the attention and
-  token-selection kernels count their own vector-memory operations with
-  explicit s_waitcnt vmcnt, and a scratch reload would add loads they do not
-  count (and the compiler's waits for it would drain their copies in flight).
+* No attention kernel (nor any other kernel outside the token selector) spills
+  to scratch memory: the attention loaders may count their own vector-memory
+  operations with a nonzero s_waitcnt vmcnt, and a scratch reload would add
+  loads they do not count (and the compiler's waits for it would drain their
+  copies in flight). The token selector's compute wavefronts issue no copies
+  and its loader wavefronts wait for all their copies (vmcnt(0)) before
+  publishing, so a spill there costs time only; its source is checked to hold
+  no counted wait.
 * M0 is touched only by the direct-to-LDS copy helpers: the compiler is not
   told that their inline asm writes M0 (a reserved register), so no compiler-
   generated instruction may keep a value in M0. Every instruction that names
@@ -69,8 +73,17 @@ def _instructions(asm):
     return out
 
 
+# sources whose ring waits are all vmcnt(0), so that scratch use is harmless
+UNCOUNTED_WAITS = {"token_select.hip"}
+
+
 @pytest.mark.parametrize("src", HIP_SOURCES)
 def test_no_scratch(device_asm, src):
+    if src in UNCOUNTED_WAITS:
+        text = open(os.path.join(build.PKG, "csrc", src)).read()
+        waits = re.findall(r"wait_vmcnt<([^>]*)>", text)
+        assert waits and all(w.strip() == "0" for w in waits), f"{src}: counted vmcnt waits {waits}"
+        return
     spilling = [n for n, size in _kernels(device_asm[src]) if size != 0]
     assert not spilling, f"{src}: kernels using scratch: {spilling}"
 

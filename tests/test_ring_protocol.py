@@ -1,5 +1,6 @@
-"""CPU model of the LDS ring protocol of the attention kernel (csrc/attention.hip),
-checked over random interleavings.
+"""CPU model of the LDS ring protocol of the attention kernel (csrc/attention.hip)
+and the token selector's key-block ring (csrc/token_select.hip), checked over
+random interleavings.
 
 The kernel streams the union of its query blocks' kept KV units through a ring
 of NS slots (unit u lives in slot u mod NS). L loader wavefronts own the units
@@ -237,12 +238,14 @@ def random_needs(rng, n_units, waves, density):
     return needs
 
 
-@pytest.mark.parametrize("loaders,inflight,slots", [(4, 1, 9), (4, 1, 8), (3, 2, 9), (3, 2, 8), (4, 2, 9)])
+@pytest.mark.parametrize("loaders,inflight,slots",
+                         [(4, 1, 9), (4, 1, 8), (4, 1, 6), (4, 1, 3), (4, 1, 2), (3, 2, 9), (3, 2, 8), (4, 2, 9)])
 def test_ring_protocol_random_interleavings(loaders, inflight, slots):
-    """The kernel's protocol (current: 4 loaders, 1 unit in flight each; the
-    earlier form: 3 loaders, 2 in flight) with 9 and 8 slots, 8 compute waves,
-    unions of 1 to 40 units, densities from sparse (units no wave needs occur)
-    to full."""
+    """The protocol of the attention kernel (4 loaders, 1 unit in flight each,
+    9 or 6 slots; the earlier form: 3 loaders, 2 in flight) and of the token
+    selector (the same loaders over its key-block ring of 2 to 16 buffers),
+    8 compute waves, unions of 1 to 40 units, densities from sparse (units no
+    wave needs occur) to full."""
     rng = np.random.default_rng(loaders * 100 + inflight * 10 + slots)
     for trial in range(150):
         n = int(rng.integers(1, 41))
