@@ -7,7 +7,10 @@ One step = one pass of the whole hot path over one batch of synthetic input
 already resident in HBM: candidate build (asynchronous form), block mean
 pooling + scoring + selection, the choice of query-block grouping, and
 block-sparse flash attention. The dense
-kernel is timed separately as the speedup denominator. Prints one JSON line.
+kernel is timed separately as the speedup denominator. Per-stage times come
+from HIP events on the launch stream: stage_ms is the mean over
+--stage-iters launches (the roofline uses it), stage_ms_median the median of
+the per-launch times. Prints one JSON line.
 
 --mode decay-static: the paper's content-free static-ratio selector (Eq. 8);
 its mask depends on no tensor, so it is built once (timed separately as
@@ -49,8 +52,8 @@ def parse():
                     help="Table 2 preset (dynamic rows for --mode token, static rows for --mode decay-static)")
     ap.add_argument("--seed", type=int, default=2024, help="sampling seed of --mode decay-static")
     ap.add_argument("--block-size", type=int, default=None, help="override the workload's block size (32, 64, 128)")
-    ap.add_argument("--stage-iters", type=int, default=20)
-    ap.add_argument("--dense-iters", type=int, default=20)
+    ap.add_argument("--stage-iters", type=int, default=100, help="timed launches per stage (mean and median)")
+    ap.add_argument("--dense-iters", type=int, default=50, help="timed launches of the dense kernel")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-groups", action="store_true",
@@ -61,17 +64,21 @@ def parse():
     return ap.parse_args()
 
 
-def event_ms(fn, iters, torch):
+def event_ms(fn, iters, torch, medians=None, name=None):
     """Average ms per call from HIP events on the current stream (the stream
-    the library launches on)."""
-    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    the library launches on): the first launch's start to the last one's end,
+    over iters. With `medians`, also the median of the per-launch times,
+    stored under `name`."""
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(iters + 1)]
     torch.cuda.synchronize()
-    s.record()
-    for _ in range(iters):
+    ev[0].record()
+    for i in range(iters):
         fn()
-    e.record()
-    e.synchronize()
-    return s.elapsed_time(e) / iters
+        ev[i + 1].record()
+    ev[-1].synchronize()
+    if medians is not None:
+        medians[name] = round(float(np.median([ev[i].elapsed_time(ev[i + 1]) for i in range(iters)])), 4)
+    return ev[0].elapsed_time(ev[-1]) / iters
 
 
 def traffic_record(workload, mode):
@@ -355,10 +362,12 @@ def main():
     ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
 
     # per-stage HIP-event timing on the launch stream
-    ms_cand = event_ms(step_candidates, args.stage_iters, torch) if ms_mask is None else None
-    ms_sel = event_ms(step_select, args.stage_iters, torch) if ms_mask is None else None
-    ms_groups = event_ms(step_groups, args.stage_iters, torch) if not args.no_groups else None
-    ms_attn = event_ms(step_attn, args.stage_iters, torch)
+    med = {}
+    sel_name = "token_select" if args.mode == "token" else "score_select"
+    ms_cand = event_ms(step_candidates, args.stage_iters, torch, med, "build_candidates") if ms_mask is None else None
+    ms_sel = event_ms(step_select, args.stage_iters, torch, med, sel_name) if ms_mask is None else None
+    ms_groups = event_ms(step_groups, args.stage_iters, torch, med, "query_groups") if not args.no_groups else None
+    ms_attn = event_ms(step_attn, args.stage_iters, torch, med, "sparse_attn")
     modes_used = np.bincount(gmodes.cpu().numpy(), minlength=3).tolist() if not args.no_groups else None
     kept_total = int(kept_cnt.sum().item())
     Sb = cand.num_blocks
@@ -368,7 +377,7 @@ def main():
     if not args.no_dense:
         dense_out = torch.empty_like(q)
         dr.attn(q, k, v, out=dense_out)
-        ms_dense = event_ms(lambda: dr.attn(q, k, v, out=dense_out), args.dense_iters, torch)
+        ms_dense = event_ms(lambda: dr.attn(q, k, v, out=dense_out), args.dense_iters, torch, med, "dense_attn")
     dense_flops = 4.0 * w.batch * w.heads * w.seq_len ** 2 * w.head_dim
     value = flops / (ms_step * 1e-3) / 1e12
     achieved = flops / (ms_attn * 1e-3) / 1e12
@@ -395,6 +404,7 @@ def main():
                       ("token_select" if args.mode == "token" else "score_select"): round(ms_sel, 4)}) |
                     ({"query_groups": round(ms_groups, 4)} if ms_groups is not None else {}) |
                     {"sparse_attn": round(ms_attn, 4), "dense_attn": round(ms_dense, 3) if ms_dense else None},
+        "stage_ms_median": med,
         "query_grouping": ({"heads_per_mode": modes_used} if modes_used is not None else "consecutive"),
         "dense_tflops": round(dense_flops / (ms_dense * 1e-3) / 1e12, 2) if ms_dense else None,
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
