@@ -6,7 +6,8 @@
 One step = one pass of the whole hot path over one batch of synthetic input
 already resident in HBM: candidate build (asynchronous form), block mean
 pooling + scoring + selection, the choice of query-block grouping, and
-block-sparse flash attention. The dense
+block-sparse flash attention (--graph: the step's launches replayed from a
+HIP graph). The dense
 kernel is timed separately as the speedup denominator. Per-stage times come
 from HIP events on the launch stream: stage_ms is the mean over
 --stage-iters launches (the roofline uses it), stage_ms_median the median of
@@ -55,6 +56,8 @@ def parse():
     ap.add_argument("--stage-iters", type=int, default=100, help="timed launches per stage (mean and median)")
     ap.add_argument("--dense-iters", type=int, default=50, help="timed launches of the dense kernel")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--graph", action="store_true",
+                    help="time replays of the step's HIP graph instead of eager launches")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-groups", action="store_true",
                     help="consecutive query blocks per attention workgroup (skip dr_query_groups)")
@@ -352,12 +355,33 @@ def main():
         step_groups()
         step_attn()
 
+    # --graph: the step's launches recorded once in a HIP graph and replayed
+    # (no host launch overhead per kernel; measured no faster than eager
+    # launches, which the GPU never waits for); eager if capture fails.
+    run_step, launch = step, "eager"
+    if args.graph:
+        try:
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                step()
+            torch.cuda.current_stream().wait_stream(side)
+            torch.cuda.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                step()
+            torch.cuda.synchronize()
+            run_step, launch = graph.replay, "hip_graph"
+        except Exception as exc:   # noqa: BLE001 - report and time the eager launches
+            print(f"# graph capture failed ({exc}); timing eager launches", file=sys.stderr, flush=True)
+            torch.cuda.synchronize()
+
     for _ in range(args.warmup):
-        step()
+        run_step()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        step()
+        run_step()
     torch.cuda.synchronize()
     ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
 
@@ -393,7 +417,7 @@ def main():
                    "theta_c": w.theta_c, "theta_m": w.theta_m,
                    "batch": w.batch, "heads": w.heads,
                    "seq_len": w.seq_len, "head_dim": w.head_dim, "block_size": w.block_size, "gamma": w.gamma,
-                   "lambda": w.lam, "parallelism": "single-gpu"},
+                   "lambda": w.lam, "parallelism": "single-gpu", "launch": launch},
         "sparsity": round(sparsity, 4),
         "candidate_density": round(cand.nnz / Sb ** 2, 4),
         "kept_blocks": kept_total,
