@@ -351,13 +351,13 @@ struct Lds {
   }
 };
 
-// Mark-kernel LDS beyond the shared layout: thresholds and served flags per
-// frame pair, the column counts and arrivals per ring buffer (B_s > 32), and
+// Mark-kernel LDS beyond the shared layout: thresholds (score and logit
+// units) and served flags per frame pair, the column counts and arrivals per ring buffer (B_s > 32), and
 // the split's flags.
 template <int D, int BS, int HF>
 __host__ __device__ size_t mark_extra(int Sb, int Nf, int FR, int nb) {
   using G = Geo<D, BS, HF>;
-  return (size_t)FR * Nf * 8 + (G::WPQ > 1 ? (size_t)G::QB * nb * (BS + 1) * 4 : 0) +
+  return (size_t)FR * Nf * 12 + (G::WPQ > 1 ? (size_t)G::QB * nb * (BS + 1) * 4 : 0) +
          (size_t)G::QB * Lds<D, BS, HF>::max_steps(Sb);
 }
 
@@ -802,6 +802,21 @@ __global__ __launch_bounds__(256) void reduce_kernel(TokParams p) {
   p.served[o] = 0;
 }
 
+// The smallest float a with fl(a * scale) >= thr (scale > 0): rounding is
+// monotone, so for every float x, x >= a exactly when fl(x * scale) >= thr.
+// thr / scale lies within two ulps of it; +-inf map to themselves.
+__device__ __forceinline__ float logit_threshold(float thr, float scale) {
+  if (__builtin_isinf(thr)) return thr;
+  float a = thr / scale;
+  for (int it = 0; it < 4; ++it) {
+    const float d = nextafterf(a, -INFINITY);
+    if (d * scale >= thr) a = d;
+    else break;
+  }
+  for (int it = 0; it < 4 && !(a * scale >= thr); ++it) a = nextafterf(a, INFINITY);
+  return a;
+}
+
 // Decision of one block pair from per-key-token selected counts.
 __device__ __forceinline__ bool block_kept(const TokParams& p, const int* cnt, int nq, int nk) {
   int act = 0;
@@ -822,7 +837,8 @@ __global__ __launch_bounds__(kThreads) void mark_kernel(TokParams p) {
   const int MS = Lds<D, BS, HF>::max_steps(p.Sb);
   float* thr_l = reinterpret_cast<float*>(L.rest);                      // [FR][Nf]
   int* served_l = reinterpret_cast<int*>(thr_l + p.FR * p.Nf);          // [FR][Nf]
-  int* colcnt = served_l + p.FR * p.Nf;                                 // [QB][nb][BS] when BS > 32
+  float* thra_l = reinterpret_cast<float*>(served_l + p.FR * p.Nf);    // [FR][Nf] in logit units
+  int* colcnt = reinterpret_cast<int*>(thra_l + p.FR * p.Nf);           // [QB][nb][BS] when BS > 32
   int* arrive = colcnt + (G::WPQ > 1 ? G::QB * L.nb * BS : 0);           // [QB][nb] when BS > 32
   unsigned char* flags_l = reinterpret_cast<unsigned char*>(arrive + (G::WPQ > 1 ? G::QB * L.nb : 0));  // [QB][MS]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5;
@@ -834,7 +850,9 @@ __global__ __launch_bounds__(kThreads) void mark_kernel(TokParams p) {
   for (int i = tid; i < p.FR * p.Nf; i += kThreads) {
     const int fr = i / p.Nf, fk = i - fr * p.Nf;
     const int fq = f_lo + fr;
-    thr_l[i] = fq < p.Nf ? p.thr[(size_t)b * p.Nf * p.Nf + (size_t)fq * p.Nf + fk] : INFINITY;
+    const float thr = fq < p.Nf ? p.thr[(size_t)b * p.Nf * p.Nf + (size_t)fq * p.Nf + fk] : INFINITY;
+    thr_l[i] = thr;
+    thra_l[i] = logit_threshold(thr, p.scale);
     served_l[i] = 0;
   }
   for (int n = 1 + tid; n <= BS; n += kThreads) {
@@ -872,11 +890,15 @@ __global__ __launch_bounds__(kThreads) void mark_kernel(TokParams p) {
     const floatx16 acc = tile_scores<D, BS, HF>(qf, kbuf, ksub, lane);
     unsigned sel = 0;
     if (ti.cls == kAllScored) {
-      const float thr = thr_l[(ti.fq - f_lo) * p.Nf + ti.fk];
+      // selected iff logit >= the frame pair's logit threshold: the sign bit
+      // of their difference counts the rest (x - y is +0 when x = y)
+      const float ta = thra_l[(ti.fq - f_lo) * p.Nf + ti.fk];
+      int below = 0;
 #pragma unroll
-      for (int i = 0; i < 16; ++i)
-        if (acc[i] * p.scale >= thr) sel |= 1u << i;
-      if (__ballot(sel != 0u) != 0ull && lane == 0) served_l[(ti.fq - f_lo) * p.Nf + ti.fk] = 1;
+      for (int i = 0; i < 16; ++i) below += (int)(__float_as_uint(acc[i] - ta) >> 31);
+      const int c = 16 - below;
+      if (__ballot(c != 0) != 0ull && lane == 0) served_l[(ti.fq - f_lo) * p.Nf + ti.fk] = 1;
+      return c + __shfl_xor(c, 32);
     } else {
       const TileFrames f = tile_frames_at(p, qat, kat, ktok0, lane);
       const float thr0 = f.kvalid ? thr_l[(f.f0 - f_lo) * p.Nf + f.fk] : INFINITY;
