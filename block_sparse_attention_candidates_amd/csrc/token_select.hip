@@ -300,10 +300,10 @@ __device__ __forceinline__ void select_bits(const TokParams& p, const floatx16& 
   }
 }
 
-// LDS layout shared by the stats and mark kernels: key staging (2 buffers),
-// per-query-block candidate bitmaps and their CSR word prefixes, the union
+// LDS layout shared by the stats and mark kernels: the key-block ring (nb
+// buffers, chosen at launch), per-query-block candidate bitmaps and their CSR word prefixes, the union
 // bitmap, and the per-distance table; then kernel-specific areas.
-constexpr int kCtlBytes = 128;   // ring control: prog[8], ready[16], next_issue, padding
+constexpr int kCtlBytes = 128;   // ring control: prog[8], ready[16], padding
 
 template <int D, int BS, int HF>
 struct Lds {
@@ -321,7 +321,6 @@ struct Lds {
   int* s_ret;           // [Nf] 1 iff t mod sf(t) = 0 (Eq. 6)
   int* prog;            // [kWaves] ring step each wave may still read (kDone: none)
   int* ready;           // [kRingMax] step held by each ring buffer (-1: none)
-  int* next_issue;      // next step to be claimed for loading
   unsigned char* rest;  // 16-byte aligned
   __host__ __device__ static size_t align16(size_t x) { return (x + 15) & ~(size_t)15; }
   __device__ unsigned char* kbuf(int j) const { return ring + (j % nb) * G::KBUF; }
@@ -340,7 +339,6 @@ struct Lds {
     s_ret = s_w + Nf;
     prog = reinterpret_cast<int*>(smem + align16((size_t)(reinterpret_cast<unsigned char*>(s_ret + Nf) - smem)));
     ready = prog + kWaves;
-    next_issue = ready + kRingMax;
     rest = reinterpret_cast<unsigned char*>(prog) + kCtlBytes;
   }
   __host__ __device__ static size_t bytes(int Sb, int Nf, int nb) {
@@ -483,7 +481,6 @@ __device__ __forceinline__ int setup(const TokParams& p, Lds<D, BS, HF>& L, int 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if (tid < kWaves) L.prog[tid] = 0;
   if (tid < kRingMax) L.ready[tid] = -1;
-  if (tid == 0) *L.next_issue = 0;
   for (int t = tid; t < p.Nf; t += kThreads) {
     int w, sf;
     table_entry(t, p.Nt, BS, p.L0, p.gamma, p.lambda, &w, &sf);
