@@ -423,6 +423,9 @@ def main():
         "kept_blocks": kept_total,
         "speedup_vs_dense": round(ms_dense / ms_step, 3) if ms_dense else None,
         "speedup_vs_dense_attention_only": round(ms_dense / ms_attn, 3) if ms_dense else None,
+        # selection + attention, the candidate set counted as a cached setup cost
+        "speedup_vs_dense_select_attn": (round(ms_dense / (ms_sel + ms_attn), 3)
+                                         if ms_dense and ms_sel is not None else None),
         "stage_ms": ({"mask_build": round(ms_mask, 4)} if ms_mask is not None else
                      {"build_candidates": round(ms_cand, 4),
                       ("token_select" if args.mode == "token" else "score_select"): round(ms_sel, 4)}) |
