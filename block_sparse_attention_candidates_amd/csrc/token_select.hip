@@ -129,22 +129,35 @@ struct Geo {
 
 // Fused-head logits of one 32x32 token tile: A = this wave's Q rows (registers),
 // B = 32 staged keys (key sub-block ksub of the staged block). Lane l gets key
-// column l%32 and query rows 8*(i/4) + 4*(l/32) + i%4.
+// column l%32 and query rows 8*(i/4) + 4*(l/32) + i%4. The key operands are
+// read two products ahead, in an order the scheduler may not change: left to
+// itself, under the register limit of three waves per SIMD, it waits for each
+// read right before its product (wan14b_720p + "mid" 4.84 -> 4.73 ms per
+// selection; three ahead spill more and gain nothing).
 template <int D, int BS, int HF>
 __device__ __forceinline__ floatx16 tile_scores(const bf16x8 (&qf)[HF][D / 16], const unsigned char* kbuf, int ksub,
                                        int lane) {
   using G = Geo<D, BS, HF>;
+  constexpr int NK = HF * (D / 16);      // products per tile
+  constexpr int PF = 2;                  // key operands in flight
   floatx16 acc = {};
   const int key = 32 * ksub + (lane & 31), half = lane >> 5;
-#pragma unroll
-  for (int h = 0; h < HF; ++h) {
+  auto operand = [&](int i) -> bf16x8 {
+    const int h = i / (D / 16), kk = i - h * (D / 16);
     const unsigned char* row = kbuf + (h * BS + key) * G::RB;
+    const int ch = (2 * kk + half) ^ swz<D>(key);
+    return *reinterpret_cast<const bf16x8*>(row + ch * 16);
+  };
+  bf16x8 kb[PF];
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
-      const int ch = (2 * kk + half) ^ swz<D>(key);
-      const bf16x8 kb = *reinterpret_cast<const bf16x8*>(row + ch * 16);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[h][kk], kb, acc, 0, 0, 0);
-    }
+  for (int i = 0; i < PF; ++i) kb[i] = operand(i);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = 0; i < NK; ++i) {
+    const int h = i / (D / 16), kk = i - h * (D / 16);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[h][kk], kb[i % PF], acc, 0, 0, 0);
+    if (i + PF < NK) kb[i % PF] = operand(i + PF);
+    __builtin_amdgcn_sched_barrier(0);
   }
   return acc;
 }
