@@ -126,8 +126,9 @@ WsLayout ws_layout(const dr_dims* d, int Sb, const dr_select_cfg* s, long long n
 }
 
 struct TokWs {
-  size_t part, thr, fmax, fn, served, flags, total;
+  size_t part, thr, fmax, fn, served, flags, colsum, und, total;
   int n_wg, FR;
+  bool decide;   // B_s = 32: column sums and the decision pass
 };
 
 TokWs tok_ws(const dr_dims* d, const dr_radial_cfg* c, int Sb, long long S, long long nnz) {
@@ -149,6 +150,11 @@ TokWs tok_ws(const dr_dims* d, const dr_radial_cfg* c, int Sb, long long S, long
   off = align256(off + fpairs * sizeof(int));
   w.flags = off;
   off = align256(off + (size_t)d->batch * nnz);
+  w.decide = c->block_size == 32;
+  w.colsum = off;
+  if (w.decide) off = align256(off + (size_t)d->batch * nnz * 32 * 2 * sizeof(float));
+  w.und = off;
+  if (w.decide) off = align256(off + (size_t)d->batch * nnz);
   w.total = off;
   (void)Sb;
   return w;
@@ -398,6 +404,8 @@ dr_status dr_token_select(const dr_dims* dims, const dr_radial_cfg* cfg, const d
   p.fn = reinterpret_cast<double*>(wsb + w.fn);
   p.served = reinterpret_cast<int*>(wsb + w.served);
   p.flags = wsb + w.flags;
+  p.colsum = w.decide ? reinterpret_cast<float*>(wsb + w.colsum) : nullptr;
+  p.und = w.decide ? wsb + w.und : nullptr;
   const hipError_t e = dr::launch_token_select(p, dims->batch, dims->head_dim, cfg->block_size, tok->fused_heads,
                                                stream);
   if (e != hipSuccess) return hip_fail(e, "token selection kernels");

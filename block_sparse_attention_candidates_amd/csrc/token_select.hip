@@ -42,6 +42,7 @@ namespace dr {
 namespace {
 
 typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef float floatx2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
@@ -52,6 +53,7 @@ constexpr int kRows = kWaves * 32;      // query tokens per workgroup
 constexpr int kRingMax = 16;            // ring depth limit (key blocks)
 constexpr int kTokLdsBytes = 160 * 1024; // LDS per workgroup on gfx950
 constexpr int kDone = 0x3fffffff;       // progress of a wave that reads no more blocks
+constexpr int kOpenChunk = 16;          // candidate entries per wavefront of mark_open_kernel
 
 typedef int intx4 __attribute__((ext_vector_type(4)));
 #define DR_LDS __attribute__((address_space(3)))
@@ -68,6 +70,14 @@ __device__ __forceinline__ void st_relaxed(int* p, int v) {
 __device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
 
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// Sum of a value over lanes l and l ^ 32, the same float in both:
+// v_permlane32_swap(v, v) gives the low half's value in one result and the
+// high half's in the other.
+__device__ __forceinline__ float sum_halves(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 // order-preserving unsigned key of a float
 __device__ __forceinline__ unsigned int fkey(float s) {
@@ -251,7 +261,7 @@ __device__ __forceinline__ int row_of(int i, int half) { return 8 * (i >> 2) + 4
 // frame and one key frame, away from the sequence end, has one frame distance
 // t for all its pairs; then its pairs are all or none in P(i, j) unless the
 // window edge cuts it. Computed in scalar registers.
-enum TileClass { kGeneral = 0, kNone = 1, kAllNear = 2, kAllScored = 3 };
+enum TileClass { kGeneral = 0, kNone = 1, kAllNear = 2, kAllScored = 3, kCutNear = 4, kCutScored = 5 };
 struct TileInfo {
   int cls, fq, fk;
 };
@@ -273,6 +283,7 @@ __device__ __forceinline__ TileInfo classify(const TokParams& p, int q0, FrameAt
   const int dmin = max(0, max(uk - (uq + 31), uq - (uk + 31)));      // smallest
   if (dmin > w) ti.cls = kNone;
   else if (dmax <= w) ti.cls = t <= 1 ? kAllNear : kAllScored;
+  else ti.cls = t <= 1 ? kCutNear : kCutScored;   // the window edge cuts the tile
   return ti;
 }
 
@@ -585,6 +596,15 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(TokParams p) {
   const int f0w = q0 / p.Nt;
   const FrameAt qat{f0w, q0 - f0w * p.Nt};   // frame and index of the wave's first row
   Stat* mine = acc_l + wave * 2 * p.Nf;
+  // B_s = 32: candidate entry of the wave's current step. The walk visits the
+  // wave's candidates in ascending key order, one entry after another, from
+  // the first at or after the split's first step.
+  int entry = 0;
+  if (BS == 32 && active_wave && n > 0) {
+    const int kb = L.steps[0], wi = kb >> 5;
+    entry = uniform(p.row_ptr[a] + L.pre[qb * L.nword + wi] +
+                    __popc(L.bits[qb * L.nword + wi] & ((1u << (kb & 31)) - 1u)));
+  }
 
   // Per-lane running statistics, four sets: query frame f0w + fo (the wave's
   // 32 rows span at most two frames) x key frame parity kp. Keys are walked in
@@ -648,6 +668,7 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(TokParams p) {
   if (wave >= kWaves) ring_load<D, BS, HF>(p, b, L, n, wave - kWaves, lane);
   if (active_wave) {
     walk_own(L, L.bits + qb * L.nword, n, j0, [&](int j, int kb) __attribute__((always_inline)) {
+      const int ent = entry++;
       ring_wait<D, BS, HF>(p, L, wave, lane, j, gave_up);
       const unsigned char* kbuf = L.kbuf(j);
       const int info = L.sinfo[j];
@@ -678,6 +699,9 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(TokParams p) {
             tq = fmaf(acc[i], acc[i], tq);
             m = fmaxf(m, acc[i]);
           }
+          // the tile's key-column sums for the decision pass (B_s = 32): lanes
+          // l and l ^ 32 hold the two 16-row halves of column l % 32
+          const float cs = sum_halves(ts), cq = sum_halves(tq);
           const float ms = m * p.scale;
           const float cur = x == 0 ? rm[0] : (x == 1 ? rm[1] : (x == 2 ? rm[2] : rm[3]));
           unsigned int loc = 0xffffffffu;
@@ -692,6 +716,13 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(TokParams p) {
           }
           const double sc = (double)p.scale;
           add(x, (double)ts * sc, (double)tq * (sc * sc), 16, ms, loc);
+          if constexpr (BS == 32) {
+            // stored after the set update: the spill reloads there wait for
+            // every memory operation in flight, this store included
+            compiler_fence();
+            floatx2* o = reinterpret_cast<floatx2*>(p.colsum) + ((size_t)b * p.nnz + (size_t)ent) * 32;
+            if (lane < 32) o[lane] = floatx2{cs, cq};
+          }
           continue;
         }
         // general tile: pairs split by query frame f0 + fo and the lane's key frame
@@ -744,6 +775,16 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(TokParams p) {
         const double sc = (double)p.scale;
         if (tn0 > 0) add(kp, (double)ts0 * sc, (double)tq0 * (sc * sc), tn0, tm0, tl0);
         if (tn1 > 0) add(2 + kp, (double)ts1 * sc, (double)tq1 * (sc * sc), tn1, tm1, tl1);
+        if constexpr (BS == 32) {
+          if (ti.cls == kCutScored) {
+            // a tile inside one frame pair cut by the window: its key columns'
+            // in-window sums for the decision pass (after the set update, as above)
+            const float cs = sum_halves(ts0), cq = sum_halves(tq0);
+            compiler_fence();
+            floatx2* o = reinterpret_cast<floatx2*>(p.colsum) + ((size_t)b * p.nnz + (size_t)ent) * 32;
+            if (lane < 32) o[lane] = floatx2{cs, cq};
+          }
+        }
       }
     });
   }
@@ -809,7 +850,10 @@ __global__ __launch_bounds__(256) void reduce_kernel(TokParams p) {
   p.thr[o] = thr;
   p.fmax[o] = t.mx;
   p.fn[o] = t.n;
-  p.served[o] = 0;
+  // served iff some pair of P(i, j) reaches the threshold, i.e. iff its
+  // highest score does (the same float32 scores the mark pass compares; fkey
+  // preserves order)
+  p.served[o] = t.n > 0.0 && (unsigned int)(t.mx >> 32) >= fkey(thr) ? 1 : 0;
 }
 
 // The smallest float a with fl(a * scale) >= thr (scale > 0): rounding is
@@ -832,6 +876,197 @@ __device__ __forceinline__ bool block_kept(const TokParams& p, const int* cnt, i
   int act = 0;
   for (int c = 0; c < nk; ++c) act += ((double)cnt[c] / (double)nq) > p.theta_c ? 1 : 0;
   return ((double)act / (double)nk) > p.theta_m;
+}
+
+// ---------------------------------------------------------------------------
+// Pass 3a (B_s = 32): candidate entries whose flag follows without their
+// logits. For a tile inside one frame pair, a key column's selected count is
+// known outright when the pair has t <= 1 (its in-window rows, or all 32, or
+// none). For t > 1, Cantelli's inequality bounds the count of the column's n
+// in-window logits at or above the logit threshold T: at most n v / (v + d^2)
+// of them lie d or more above their mean (v: population variance), and as many
+// at most d or more below it. Mean and variance come from the statistics pass's float32
+// column sums, widened by their rounding bounds (a float32 sum of n terms is
+// within (n + 1) u sum |x| of the exact one, a fused sum of squares within
+// (n + 1) u sum x^2; 20 u is taken), so a column fixed as active (count >=
+// the theta_c count) or inactive is so for its logits, and the flag is fixed
+// once enough columns are. Exact: a fixed flag is the flag the mark pass would
+// compute. The other entries (und = 1) are left to the mark pass.
+// One workgroup per (b, query block), one half-wave per entry (lane = column).
+// ---------------------------------------------------------------------------
+template <int D, int BS, int HF>
+__global__ __launch_bounds__(256) void decide_kernel(TokParams p) {
+  static_assert(BS == 32, "one 32x32 tile per block pair");
+  __shared__ int s_w[kMaxTokenFrames], s_ret[kMaxTokenFrames];
+  __shared__ float s_thra[kMaxTokenFrames];   // logit threshold against key frame fk
+  const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5, col = lane & 31;
+  const int a = blockIdx.x, b = blockIdx.y;
+  const int q0 = a * 32;
+  const FrameAt qat{q0 / p.Nt, q0 - (q0 / p.Nt) * p.Nt};
+  for (int t = tid; t < p.Nf; t += 256) {
+    int w, sf;
+    table_entry(t, p.Nt, BS, p.L0, p.gamma, p.lambda, &w, &sf);
+    s_w[t] = w < p.Nt ? w : p.Nt;
+    s_ret[t] = t % sf == 0 ? 1 : 0;
+    s_thra[t] = logit_threshold(p.thr[((size_t)b * p.Nf + qat.f) * p.Nf + t], p.scale);
+  }
+  __syncthreads();
+  const int min_c = min_count(32, p.theta_c), min_a = min_count(32, p.theta_m);
+  const int e0 = p.row_ptr[a], e1 = p.row_ptr[a + 1];
+  const size_t eb = (size_t)b * p.nnz;
+  const unsigned long long halfmask = half ? 0xffffffff00000000ull : 0xffffffffull;
+  for (int e = e0 + (tid >> 5); e - (tid >> 5) < e1; e += 8) {
+    const bool valid = e < e1;
+    int cls = kGeneral, fk = 0, dt = 0;
+    FrameAt kat{0, 0};
+    if (valid) {
+      const int k0 = p.cols[e] * 32;
+      kat = FrameAt{k0 / p.Nt, k0 - (k0 / p.Nt) * p.Nt};
+      const TileInfo ti = classify(p, q0, qat, k0, kat, s_w, s_ret);
+      cls = ti.cls;
+      fk = ti.fk;
+      dt = ti.fq > ti.fk ? ti.fq - ti.fk : ti.fk - ti.fq;
+    }
+    bool act = false, inact = false;
+    if (cls == kNone || cls == kAllNear || cls == kCutNear) {
+      // selected count of the column: none, all 32 rows, or its in-window rows
+      int c = cls == kNone ? 0 : 32;
+      if (cls == kCutNear) {
+        const int v = kat.u + col, w = s_w[dt];
+        c = max(0, min(qat.u + 31, v + w) - max(qat.u, v - w) + 1);
+      }
+      act = c >= min_c;
+      inact = !act;
+    } else if (cls == kAllScored || cls == kCutScored) {
+      // the column's n logits in P(i, j) (all 32 rows, or its in-window rows)
+      int nin = 32;
+      if (cls == kCutScored) {
+        const int v = kat.u + col, w = s_w[dt];
+        nin = max(0, min(qat.u + 31, v + w) - max(qat.u, v - w) + 1);
+      }
+      if (nin == 0) {
+        act = 0 >= min_c;
+        inact = !act;
+      } else {
+        const float* cs = p.colsum + ((eb + (size_t)e) * 32 + col) * 2;
+        const double n = (double)nin, u = 0x1p-24;
+        const double S1 = cs[0], Q = cs[1], T = s_thra[fk];
+        const double Qhi = Q * (1.0 + 20.0 * u);                 // >= the exact sum of squares
+        const double e1s = 20.0 * u * sqrt(n * Qhi);               // >= |S1 - the exact sum|
+        const double sa = fmax(0.0, fabs(S1) - e1s);
+        const double var = fmax(0.0, Qhi - sa * sa / n) / n;      // >= the population variance
+        const double A = n * T - S1;                               // n (T - mean), within e1s
+        if (__builtin_isfinite(T) && A - e1s > 0.0) {
+          const double d = (A - e1s) / n;                          // <= T - mean
+          inact = n * var / (var + d * d) * (1.0 + 1e-12) < (double)min_c;
+        } else if (__builtin_isfinite(T) && -A - e1s > 0.0) {
+          const double d = (-A - e1s) / n;                         // <= mean - T
+          act = (n - n * var / (var + d * d)) * (1.0 - 1e-12) > (double)(min_c - 1);
+        }
+      }
+    }
+    const int n_act = __popcll(__ballot(act) & halfmask), n_in = __popcll(__ballot(inact) & halfmask);
+    const bool decided = cls != kGeneral && (n_act >= min_a || 32 - n_in < min_a);
+    if (valid && col == 0) {
+      if (decided) p.flags[eb + e] = n_act >= min_a ? 1 : 0;
+      p.und[eb + e] = decided ? 0 : 1;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Pass 3b (B_s = 32): the entries the decision pass left open, decided as the
+// mark pass below decides them. Few stay open (3.6% at wan14b_720p + "mid":
+// tiles cut by a frame or window edge, every entry of a query block that
+// straddles two frames), so there is no staging ring: one wavefront per
+// kOpenChunk consecutive candidate entries (rows with many open entries are
+// spread over many wavefronts) loads its query block's fragments and reads
+// each open entry's key fragments straight from memory. Served frame pairs
+// are already final (reduce kernel).
+// ---------------------------------------------------------------------------
+template <int D, int HF>
+__global__ __launch_bounds__(256) void mark_open_kernel(TokParams p) {
+  constexpr int BS = 32;
+  __shared__ int s_w[kMaxTokenFrames], s_ret[kMaxTokenFrames];
+  const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5, wave = tid >> 6;
+  const int b = blockIdx.y;
+  for (int t = tid; t < p.Nf; t += 256) {
+    int w, sf;
+    table_entry(t, p.Nt, BS, p.L0, p.gamma, p.lambda, &w, &sf);
+    s_w[t] = w < p.Nt ? w : p.Nt;
+    s_ret[t] = t % sf == 0 ? 1 : 0;
+  }
+  __syncthreads();
+  // this wave's kOpenChunk consecutive candidate entries
+  const long long c0 = ((long long)blockIdx.x * 4 + wave) * kOpenChunk;
+  if (c0 >= p.nnz) return;
+  const size_t eb = (size_t)b * p.nnz;
+  unsigned long long open = __ballot(lane < kOpenChunk && c0 + lane < p.nnz && p.und[eb + c0 + lane] != 0);
+  if (!open) return;
+  // query block holding entry c0: the last a with row_ptr[a] <= c0
+  int lo = 0, hi = p.Sb - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (uniform(p.row_ptr[mid]) <= c0) lo = mid;
+    else hi = mid - 1;
+  }
+  int a = lo, a_end = uniform(p.row_ptr[a + 1]);
+  const float* thr = p.thr + (size_t)b * p.Nf * p.Nf;
+  bf16x8 qf[HF][D / 16];
+  int a_loaded = -1;
+  while (open) {
+    const long long e = c0 + __ffsll(open) - 1;
+    open &= open - 1;
+    while (e >= a_end) {
+      ++a;
+      a_end = uniform(p.row_ptr[a + 1]);
+    }
+    const int q0 = a * BS;
+    if (a != a_loaded) {
+      load_q<D, HF>(p, b, q0, lane, qf);
+      a_loaded = a;
+    }
+    const int nq = min(BS, p.S - q0);
+    const FrameAt qat{q0 / p.Nt, q0 - (q0 / p.Nt) * p.Nt};
+    const int k0 = uniform(p.cols[e]) * BS;
+    const FrameAt kat{k0 / p.Nt, k0 - (k0 / p.Nt) * p.Nt};
+    const int nk = min(BS, p.S - k0);
+    const TileInfo ti = classify(p, q0, qat, k0, kat, s_w, s_ret);
+    int c = ti.cls == kAllNear ? 32 : 0;
+    if (ti.cls != kNone && ti.cls != kAllNear) {
+      // key fragments of every fused head (rows past S read the last token;
+      // those columns are outside P)
+      const int key = min(k0 + (lane & 31), p.S - 1);
+      floatx16 acc = {};
+#pragma unroll
+      for (int h = 0; h < HF; ++h) {
+        const uint16_t* row = p.k + ((size_t)(b * p.H + h) * p.S + key) * D;
+        bf16x8 kf[D / 16];
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk)
+          kf[kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(row + (2 * kk + half) * 8));
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[h][kk], kf[kk], acc, 0, 0, 0);
+      }
+      if (ti.cls == kAllScored) {
+        const float ta = logit_threshold(thr[ti.fq * p.Nf + ti.fk], p.scale);
+        int below = 0;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) below += (int)(__float_as_uint(acc[i] - ta) >> 31);
+        c = 16 - below;
+      } else {
+        const TileFrames f = tile_frames_at(p, qat, kat, k0, lane);
+        const float thr0 = f.kvalid ? thr[f.f0 * p.Nf + f.fk] : INFINITY;
+        const float thr1 = (f.kvalid && f.f0 + 1 < p.Nf) ? thr[(f.f0 + 1) * p.Nf + f.fk] : INFINITY;
+        unsigned sel, inP2;
+        select_bits(p, acc, f, q0, half, s_w, s_ret, thr0, thr1, sel, inP2);
+        c = __popc(sel);
+      }
+      c += __shfl_xor(c, 32);
+    }
+    const int n_act = __popcll(__ballot(lane < nk && c >= min_count(nq, p.theta_c)));
+    if (lane == 0) p.flags[eb + e] = n_act >= min_count(nk, p.theta_m) ? 1 : 0;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1137,7 +1372,16 @@ hipError_t launch_all(TokParams p, int B, hipStream_t stream) {
   hipLaunchKernelGGL(reduce_kernel, dim3((unsigned)((p.Nf * p.Nf + 255) / 256), (unsigned)B), dim3(256), 0, stream,
                      p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL((mark_kernel<D, BS, HF>), grid, dim3(kThreads), lds_mark, stream, p);
+  if constexpr (BS == 32) {
+    if (!p.colsum || !p.und) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((decide_kernel<D, BS, HF>), dim3((unsigned)p.Sb, (unsigned)B), dim3(256), 0, stream, p);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const long long chunks = (p.nnz + kOpenChunk - 1) / kOpenChunk;
+    hipLaunchKernelGGL((mark_open_kernel<D, HF>), dim3((unsigned)((chunks + 3) / 4), (unsigned)B), dim3(256), 0,
+                       stream, p);
+  } else {
+    hipLaunchKernelGGL((mark_kernel<D, BS, HF>), grid, dim3(kThreads), lds_mark, stream, p);
+  }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL((fallback_kernel<D, BS, HF>), dim3((unsigned)(p.Nf * p.Nf), (unsigned)B), dim3(64), 0, stream,
                      p);

@@ -152,7 +152,12 @@ def test_token_select_validation(dynrad_lib):
     assert dynrad_lib.dr_token_select_workspace(ctypes.byref(dims), ctypes.byref(cfg), ctypes.byref(tok), 64,
                                                 ctypes.byref(size)) == L.DR_OK
     # partials: 1 workgroup x 4 key-range splits x FR (255 // 64 + 2 = 5) x N_f 4 x 32 B = 2560;
-    # thr 64 B -> 256; maxima 128 B -> 256; counts 128 B -> 256; served 64 B -> 256; flags 64 B -> 256
+    # thr 64 B -> 256; maxima 128 B -> 256; counts 128 B -> 256; served 64 B -> 256; flags 64 B -> 256;
+    # B_s = 32: column sums 64 entries x 32 columns x 8 B = 16384; undecided marks 64 B -> 256
+    assert size.value == 2560 + 5 * 256 + 16384 + 256
+    cfg64 = _cfg(4, 64, 64, 1.0, 2.0)           # B_s = 64: no column sums
+    assert dynrad_lib.dr_token_select_workspace(ctypes.byref(dims), ctypes.byref(cfg64), ctypes.byref(tok), 16,
+                                                ctypes.byref(size)) == L.DR_OK
     assert size.value == 2560 + 5 * 256
 
     def ts(d=dims, c=cfg, t=tok, nnz=64, ws_bytes=1 << 20, q=FAKE):
