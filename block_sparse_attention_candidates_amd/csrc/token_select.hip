@@ -287,6 +287,13 @@ __device__ __forceinline__ TileInfo classify(const TokParams& p, int q0, FrameAt
   return ti;
 }
 
+// A general tile whose 32 query rows lie in one frame, away from the sequence
+// end: only its keys cross a frame boundary, so each key column lies in one
+// frame pair.
+__device__ __forceinline__ bool key_straddle(const TokParams& p, int q0, FrameAt q, int k0, const TileInfo& ti) {
+  return ti.cls == kGeneral && q0 + 31 < p.S && k0 + 31 < p.S && q.u + 31 < p.Nt;
+}
+
 // Selection bits (one per element i) of a tile under the thresholds of the
 // frame pairs involved; inP bits mark the candidate pairs of P with t > 1.
 // thr0 / thr1: thresholds (score units) for query frame f0 / f0 + 1 against
@@ -776,9 +783,11 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(TokParams p) {
         if (tn0 > 0) add(kp, (double)ts0 * sc, (double)tq0 * (sc * sc), tn0, tm0, tl0);
         if (tn1 > 0) add(2 + kp, (double)ts1 * sc, (double)tq1 * (sc * sc), tn1, tm1, tl1);
         if constexpr (BS == 32) {
-          if (ti.cls == kCutScored) {
-            // a tile inside one frame pair cut by the window: its key columns'
-            // in-window sums for the decision pass (after the set update, as above)
+          if (ti.cls == kCutScored || key_straddle(p, q0, qat, ktok0, ti)) {
+            // the rows lie in one query frame and each key column in one frame
+            // pair (a tile cut by the window, or whose keys cross a frame
+            // boundary): the columns' in-P sums for the decision pass (after
+            // the set update, as above)
             const float cs = sum_halves(ts0), cq = sum_halves(tq0);
             compiler_fence();
             floatx2* o = reinterpret_cast<floatx2*>(p.colsum) + ((size_t)b * p.nnz + (size_t)ent) * 32;
@@ -880,18 +889,21 @@ __device__ __forceinline__ bool block_kept(const TokParams& p, const int* cnt, i
 
 // ---------------------------------------------------------------------------
 // Pass 3a (B_s = 32): candidate entries whose flag follows without their
-// logits. For a tile inside one frame pair, a key column's selected count is
-// known outright when the pair has t <= 1 (its in-window rows, or all 32, or
-// none). For t > 1, Cantelli's inequality bounds the count of the column's n
-// in-window logits at or above the logit threshold T: at most n v / (v + d^2)
-// of them lie d or more above their mean (v: population variance), and as many
-// at most d or more below it. Mean and variance come from the statistics pass's float32
+// logits. When a tile's 32 query rows lie in one frame (and it stays clear of
+// the sequence end), each key column lies in one frame pair (also when the
+// keys cross a frame boundary), and its selected count is known outright if
+// that pair has t <= 1 (its in-window rows) or no pair in P (none). For t > 1,
+// Cantelli's inequality bounds the count of the column's n in-window logits
+// at or above the logit threshold T: at most n v / (v + d^2) of them lie d or
+// more above their mean (v: population variance), and as many at most d or
+// more below it. Mean and variance come from the statistics pass's float32
 // column sums, widened by their rounding bounds (a float32 sum of n terms is
 // within (n + 1) u sum |x| of the exact one, a fused sum of squares within
 // (n + 1) u sum x^2; 20 u is taken), so a column fixed as active (count >=
 // the theta_c count) or inactive is so for its logits, and the flag is fixed
 // once enough columns are. Exact: a fixed flag is the flag the mark pass would
-// compute. The other entries (und = 1) are left to the mark pass.
+// compute. The other entries (und = 1: query rows crossing a frame boundary,
+// the sequence end, columns the bound leaves open) go to mark_open_kernel.
 // One workgroup per (b, query block), one half-wave per entry (lane = column).
 // ---------------------------------------------------------------------------
 template <int D, int BS, int HF>
@@ -917,35 +929,26 @@ __global__ __launch_bounds__(256) void decide_kernel(TokParams p) {
   const unsigned long long halfmask = half ? 0xffffffff00000000ull : 0xffffffffull;
   for (int e = e0 + (tid >> 5); e - (tid >> 5) < e1; e += 8) {
     const bool valid = e < e1;
-    int cls = kGeneral, fk = 0, dt = 0;
-    FrameAt kat{0, 0};
+    // the tile's 32 query rows lie in frame qat.f; each key column v of it in
+    // one key frame fk (its 32 keys may cross one frame boundary, N_t >= 32)
+    bool open_tile = true;
+    int fk = 0, v = 0;
     if (valid) {
       const int k0 = p.cols[e] * 32;
-      kat = FrameAt{k0 / p.Nt, k0 - (k0 / p.Nt) * p.Nt};
-      const TileInfo ti = classify(p, q0, qat, k0, kat, s_w, s_ret);
-      cls = ti.cls;
-      fk = ti.fk;
-      dt = ti.fq > ti.fk ? ti.fq - ti.fk : ti.fk - ti.fq;
+      open_tile = !(q0 + 31 < p.S && k0 + 31 < p.S && qat.u + 31 < p.Nt);
+      const int kt = k0 + col;
+      fk = kt / p.Nt;
+      v = kt - fk * p.Nt;
     }
     bool act = false, inact = false;
-    if (cls == kNone || cls == kAllNear || cls == kCutNear) {
-      // selected count of the column: none, all 32 rows, or its in-window rows
-      int c = cls == kNone ? 0 : 32;
-      if (cls == kCutNear) {
-        const int v = kat.u + col, w = s_w[dt];
-        c = max(0, min(qat.u + 31, v + w) - max(qat.u, v - w) + 1);
-      }
-      act = c >= min_c;
-      inact = !act;
-    } else if (cls == kAllScored || cls == kCutScored) {
-      // the column's n logits in P(i, j) (all 32 rows, or its in-window rows)
-      int nin = 32;
-      if (cls == kCutScored) {
-        const int v = kat.u + col, w = s_w[dt];
-        nin = max(0, min(qat.u + 31, v + w) - max(qat.u, v - w) + 1);
-      }
-      if (nin == 0) {
-        act = 0 >= min_c;
+    if (valid && !open_tile) {
+      // the column's pairs in P(qat.f, fk): its in-window rows, if retained
+      const int t = qat.f > fk ? qat.f - fk : fk - qat.f;
+      const int w = s_w[t];
+      const int nin = s_ret[t] ? max(0, min(qat.u + 31, v + w) - max(qat.u, v - w) + 1) : 0;
+      if (t <= 1 || nin == 0) {
+        // all of them selected (t <= 1), or none exist
+        act = (t <= 1 ? nin : 0) >= min_c;
         inact = !act;
       } else {
         const float* cs = p.colsum + ((eb + (size_t)e) * 32 + col) * 2;
@@ -966,7 +969,7 @@ __global__ __launch_bounds__(256) void decide_kernel(TokParams p) {
       }
     }
     const int n_act = __popcll(__ballot(act) & halfmask), n_in = __popcll(__ballot(inact) & halfmask);
-    const bool decided = cls != kGeneral && (n_act >= min_a || 32 - n_in < min_a);
+    const bool decided = !open_tile && (n_act >= min_a || 32 - n_in < min_a);
     if (valid && col == 0) {
       if (decided) p.flags[eb + e] = n_act >= min_a ? 1 : 0;
       p.und[eb + e] = decided ? 0 : 1;
