@@ -54,6 +54,7 @@ constexpr int kRingMax = 16;            // ring depth limit (key blocks)
 constexpr int kTokLdsBytes = 160 * 1024; // LDS per workgroup on gfx950
 constexpr int kDone = 0x3fffffff;       // progress of a wave that reads no more blocks
 constexpr int kOpenChunk = 16;          // candidate entries per wavefront of mark_open_kernel
+constexpr int kDecideUnroll = 4;        // entries per half-wave of decide_kernel with loads in flight
 
 typedef int intx4 __attribute__((ext_vector_type(4)));
 #define DR_LDS __attribute__((address_space(3)))
@@ -927,52 +928,66 @@ __global__ __launch_bounds__(256) void decide_kernel(TokParams p) {
   const int e0 = p.row_ptr[a], e1 = p.row_ptr[a + 1];
   const size_t eb = (size_t)b * p.nnz;
   const unsigned long long halfmask = half ? 0xffffffff00000000ull : 0xffffffffull;
-  for (int e = e0 + (tid >> 5); e - (tid >> 5) < e1; e += 8) {
-    const bool valid = e < e1;
-    // the tile's 32 query rows lie in frame qat.f; each key column v of it in
-    // one key frame fk (its 32 keys may cross one frame boundary, N_t >= 32)
-    bool open_tile = true;
-    int fk = 0, v = 0;
-    if (valid) {
-      const int k0 = p.cols[e] * 32;
-      open_tile = !(q0 + 31 < p.S && k0 + 31 < p.S && qat.u + 31 < p.Nt);
-      const int kt = k0 + col;
-      fk = kt / p.Nt;
-      v = kt - fk * p.Nt;
+  const bool rows_one_frame = q0 + 31 < p.S && qat.u + 31 < p.Nt;
+  const floatx2* colsum = reinterpret_cast<const floatx2*>(p.colsum);
+  // kDecideUnroll entries per half-wave in flight: their loads first
+  for (int base = e0 + (tid >> 5); base - (tid >> 5) < e1; base += 8 * kDecideUnroll) {
+    int k0s[kDecideUnroll];
+    floatx2 sums[kDecideUnroll];
+#pragma unroll
+    for (int j = 0; j < kDecideUnroll; ++j) {
+      const int e = base + 8 * j;
+      k0s[j] = e < e1 ? p.cols[e] * 32 : p.S;
+      // read whether or not the entry needs it: unused values are discarded
+      sums[j] = e < e1 ? colsum[(eb + (size_t)e) * 32 + col] : floatx2{0.f, 0.f};
     }
-    bool act = false, inact = false;
-    if (valid && !open_tile) {
-      // the column's pairs in P(qat.f, fk): its in-window rows, if retained
-      const int t = qat.f > fk ? qat.f - fk : fk - qat.f;
-      const int w = s_w[t];
-      const int nin = s_ret[t] ? max(0, min(qat.u + 31, v + w) - max(qat.u, v - w) + 1) : 0;
-      if (t <= 1 || nin == 0) {
-        // all of them selected (t <= 1), or none exist
-        act = (t <= 1 ? nin : 0) >= min_c;
-        inact = !act;
-      } else {
-        const float* cs = p.colsum + ((eb + (size_t)e) * 32 + col) * 2;
-        const double n = (double)nin, u = 0x1p-24;
-        const double S1 = cs[0], Q = cs[1], T = s_thra[fk];
-        const double Qhi = Q * (1.0 + 20.0 * u);                 // >= the exact sum of squares
-        const double e1s = 20.0 * u * sqrt(n * Qhi);               // >= |S1 - the exact sum|
-        const double sa = fmax(0.0, fabs(S1) - e1s);
-        const double var = fmax(0.0, Qhi - sa * sa / n) / n;      // >= the population variance
-        const double A = n * T - S1;                               // n (T - mean), within e1s
-        if (__builtin_isfinite(T) && A - e1s > 0.0) {
-          const double d = (A - e1s) / n;                          // <= T - mean
-          inact = n * var / (var + d * d) * (1.0 + 1e-12) < (double)min_c;
-        } else if (__builtin_isfinite(T) && -A - e1s > 0.0) {
-          const double d = (-A - e1s) / n;                         // <= mean - T
-          act = (n - n * var / (var + d * d)) * (1.0 - 1e-12) > (double)(min_c - 1);
+#pragma unroll
+    for (int j = 0; j < kDecideUnroll; ++j) {
+      const int e = base + 8 * j;
+      const bool valid = e < e1;
+      const int k0 = k0s[j];
+      // the tile's 32 query rows lie in frame qat.f; each key column v of it
+      // in one key frame fk (its 32 keys may cross one frame boundary, N_t >= 32)
+      const bool open_tile = !(valid && rows_one_frame && k0 + 31 < p.S);
+      bool act = false, inact = false;
+      if (!open_tile) {
+        const int kt = k0 + col;
+        const int fk = kt / p.Nt, v = kt - fk * p.Nt;
+        // the column's pairs in P(qat.f, fk): its in-window rows, if retained
+        const int t = qat.f > fk ? qat.f - fk : fk - qat.f;
+        const int w = s_w[t];
+        const int nin = s_ret[t] ? max(0, min(qat.u + 31, v + w) - max(qat.u, v - w) + 1) : 0;
+        if (t <= 1 || nin == 0) {
+          // all of them selected (t <= 1), or none exist
+          act = (t <= 1 ? nin : 0) >= min_c;
+          inact = !act;
+        } else {
+          // with n values, mean m, population variance var and the threshold T:
+          // M = n Qhi - sa^2 >= n^2 var, dn = n (T - m) or n (m - T) less e1s;
+          // the Cantelli tests n var / (var + d^2) < min_c and
+          // n d^2 / (var + d^2) > min_c - 1 multiplied through by n^2 (var + d^2)
+          const double n = (double)nin, u = 0x1p-24;
+          const double S1 = sums[j][0], Q = sums[j][1], T = s_thra[fk];
+          const double Qhi = Q * (1.0 + 20.0 * u);                               // >= the exact sum of squares
+          const double e1s = 20.0 * u * (double)sqrtf((float)(n * Qhi)) * (1.0 + 1e-6);  // >= |S1 - the exact sum|
+          const double sa = fmax(0.0, fabs(S1) - e1s);
+          const double M = fmax(0.0, n * Qhi - sa * sa);
+          const double A = n * T - S1;                                             // n (T - m), within e1s
+          if (__builtin_isfinite(T) && A - e1s > 0.0) {
+            const double dn = A - e1s;
+            inact = n * M * (1.0 + 1e-12) < (double)min_c * (M + dn * dn);
+          } else if (__builtin_isfinite(T) && -A - e1s > 0.0) {
+            const double dn = -A - e1s;
+            act = n * dn * dn * (1.0 - 1e-12) > (double)(min_c - 1) * (M + dn * dn);
+          }
         }
       }
-    }
-    const int n_act = __popcll(__ballot(act) & halfmask), n_in = __popcll(__ballot(inact) & halfmask);
-    const bool decided = !open_tile && (n_act >= min_a || 32 - n_in < min_a);
-    if (valid && col == 0) {
-      if (decided) p.flags[eb + e] = n_act >= min_a ? 1 : 0;
-      p.und[eb + e] = decided ? 0 : 1;
+      const int n_act = __popcll(__ballot(act) & halfmask), n_in = __popcll(__ballot(inact) & halfmask);
+      const bool decided = !open_tile && (n_act >= min_a || 32 - n_in < min_a);
+      if (valid && col == 0) {
+        if (decided) p.flags[eb + e] = n_act >= min_a ? 1 : 0;
+        p.und[eb + e] = decided ? 0 : 1;
+      }
     }
   }
 }

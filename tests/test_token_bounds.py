@@ -68,16 +68,17 @@ def decide(cs, cq, n, T, min_c, widen=True):
         nn = float(ni)
         S1, Q = float(cs[i]), float(cq[i])
         Qhi = Q * (1.0 + 20.0 * U) if widen else Q
-        e1s = 20.0 * U * math.sqrt(nn * Qhi) if widen else 0.0
+        e1s = 20.0 * U * float(np.sqrt(np.float32(nn * Qhi))) * (1.0 + 1e-6) if widen else 0.0
         sa = max(0.0, abs(S1) - e1s)
-        var = max(0.0, Qhi - sa * sa / nn) / nn
+        M = max(0.0, nn * Qhi - sa * sa)          # >= n^2 x the population variance
         A = nn * float(T[i]) - S1
+        # Cantelli, multiplied through by n^2 (var + d^2)
         if A - e1s > 0.0:
-            d = (A - e1s) / nn
-            inact[i] = nn * var / (var + d * d) * (1.0 + 1e-12) < min_c
+            dn = A - e1s
+            inact[i] = nn * M * (1.0 + 1e-12) < min_c * (M + dn * dn)
         elif -A - e1s > 0.0:
-            d = (-A - e1s) / nn
-            act[i] = (nn - nn * var / (var + d * d)) * (1.0 - 1e-12) > min_c - 1
+            dn = -A - e1s
+            act[i] = nn * dn * dn * (1.0 - 1e-12) > (min_c - 1) * (M + dn * dn)
     return act, inact
 
 
