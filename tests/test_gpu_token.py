@@ -112,6 +112,19 @@ def test_token_select_straddling_blocks_bs64_hf1_batch2():
     assert d >= 0.5 * c
 
 
+def test_token_select_straddling_blocks_bs32_hf1_batch2():
+    """B_s = 32 (the decision pass and the open-entry kernel): 6 frames of 200
+    tokens, so query and key blocks straddle frames, D = 64, 3 heads, batch 2
+    (the column sums and open marks of each batch element apart), one fused
+    head, theta = (0.3, 0.5)."""
+    G.log("[token] B_s = 32 straddling, H_f = 1, batch 2")
+    rng = np.random.default_rng(19)
+    qb = _random_bits(rng, (2, 3, 1200, 64))
+    kb = _random_bits(rng, (2, 3, 1200, 64))
+    d, c = _run_and_compare(qb, kb, 6, 200, 32, 1.2, 0.5, 0.3, 0.5, -0.5, 1.5, 1, label="bs32")
+    assert d >= 0.75 * c                          # 1839 of 2248 are decisive
+
+
 def test_token_select_block_size_128():
     """B_s = 128: 6 frames of 200 tokens (blocks span up to 2 frames), D = 128,
     2 heads fused, theta = (0.2, 0.4)."""
