@@ -248,8 +248,6 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreParams p, con
   // element i of this lane is (row 8*(i/4) + 4*half + i%4, key block t*32 + m32).
   // A tile's 32 bitmaps and positions are wave-uniform: scalar loads of both
   // halves' rows, selected per lane.
-  typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
-  typedef int i32x4_t __attribute__((ext_vector_type(4)));
   struct Desc {
     unsigned int b[32];
     int ps[32];

@@ -4,7 +4,7 @@
 // [DR] = "DynamicRad: Content-Adaptive Sparse Attention for Long Video
 // Diffusion", arXiv 2604.20470.
 //
-// One mask per batch element, shared by every head. Four launches:
+// One mask per batch element, shared by every head. Launches:
 //   stats:    a workgroup of 8 wavefronts owns 256 query tokens (8 / 4 query
 //             blocks); it walks the union of their candidate key blocks in
 //             ascending order, staging each key block of the H_f fused heads in
@@ -17,18 +17,24 @@
 //             formula in float64, and the highest score with its position);
 //             each wave keeps its own LDS accumulators, merged in a fixed order
 //             into one partial per workgroup: no floating-point atomics.
+//             At B_s = 32 it also stores, for tiles whose query rows lie in
+//             one frame, each key column's float32 sum and sum of squares of
+//             its logits in P.
 //   reduce:   per frame pair, the workgroup partials merged in workgroup order:
 //             mu, sigma (population), tau(t) by decay state (Eq. 11), and the
 //             threshold in score units thr = mu + tau * (sigma + eps) (Eq. 10
 //             rearranged), rounded up to float so that s >= thr in float32 is
-//             exactly (double) s >= mu + tau * (sigma + eps).
-//   mark:     the same walk and tiles; a pair is selected iff it is a
-//             candidate pair (Eqs. 6-7) and t <= 1 (tau = -inf) or s >= thr.
-//             Per block pair, key tokens are active iff their selected share
-//             of the query tokens exceeds theta_c, and the block pair is kept
-//             iff the active share of the key tokens exceeds theta_m; one flag
-//             per candidate entry. A frame pair with a selected t > 1 pair is
-//             marked as served.
+//             exactly (double) s >= mu + tau * (sigma + eps). A frame pair is
+//             served iff its highest score reaches thr.
+//   mark:     a pair is selected iff it is a candidate pair (Eqs. 6-7) and
+//             t <= 1 (tau = -inf) or s >= thr. Per block pair, key tokens are
+//             active iff their selected share of the query tokens exceeds
+//             theta_c, and the block pair is kept iff the active share of the
+//             key tokens exceeds theta_m; one flag per candidate entry.
+//             B_s > 32: the stats pass's walk and tiles (mark_kernel).
+//             B_s = 32: decide_kernel fixes every flag that the column sums
+//             determine (exact counts, or Cantelli bounds on each column's
+//             count), and mark_open_kernel computes the tiles of the rest.
 //   fallback: for each unserved frame pair (safeguard (ii)), the block pair
 //             holding its highest-scoring pair is re-decided with that pair
 //             added, by the same tile and selection code.
@@ -382,12 +388,12 @@ struct Lds {
 };
 
 // Mark-kernel LDS beyond the shared layout: thresholds (score and logit
-// units) and served flags per frame pair, the column counts and arrivals per ring buffer (B_s > 32), and
+// units) per frame pair, the column counts and arrivals per ring buffer (B_s > 32), and
 // the split's flags.
 template <int D, int BS, int HF>
 __host__ __device__ size_t mark_extra(int Sb, int Nf, int FR, int nb) {
   using G = Geo<D, BS, HF>;
-  return (size_t)FR * Nf * 12 + (G::WPQ > 1 ? (size_t)G::QB * nb * (BS + 1) * 4 : 0) +
+  return (size_t)FR * Nf * 8 + (G::WPQ > 1 ? (size_t)G::QB * nb * (BS + 1) * 4 : 0) +
          (size_t)G::QB * Lds<D, BS, HF>::max_steps(Sb);
 }
 
@@ -1099,8 +1105,7 @@ __global__ __launch_bounds__(kThreads) void mark_kernel(TokParams p) {
   Lds<D, BS, HF> L(smem, p.Sb, p.Nf, p.nb);
   const int MS = Lds<D, BS, HF>::max_steps(p.Sb);
   float* thr_l = reinterpret_cast<float*>(L.rest);                      // [FR][Nf]
-  int* served_l = reinterpret_cast<int*>(thr_l + p.FR * p.Nf);          // [FR][Nf]
-  float* thra_l = reinterpret_cast<float*>(served_l + p.FR * p.Nf);    // [FR][Nf] in logit units
+  float* thra_l = thr_l + p.FR * p.Nf;                                  // [FR][Nf] in logit units
   int* colcnt = reinterpret_cast<int*>(thra_l + p.FR * p.Nf);           // [QB][nb][BS] when BS > 32
   int* arrive = colcnt + (G::WPQ > 1 ? G::QB * L.nb * BS : 0);           // [QB][nb] when BS > 32
   unsigned char* flags_l = reinterpret_cast<unsigned char*>(arrive + (G::WPQ > 1 ? G::QB * L.nb : 0));  // [QB][MS]
@@ -1116,7 +1121,6 @@ __global__ __launch_bounds__(kThreads) void mark_kernel(TokParams p) {
     const float thr = fq < p.Nf ? p.thr[(size_t)b * p.Nf * p.Nf + (size_t)fq * p.Nf + fk] : INFINITY;
     thr_l[i] = thr;
     thra_l[i] = logit_threshold(thr, p.scale);
-    served_l[i] = 0;
   }
   for (int n = 1 + tid; n <= BS; n += kThreads) {
     min_c[n] = min_count(n, p.theta_c);
@@ -1144,8 +1148,7 @@ __global__ __launch_bounds__(kThreads) void mark_kernel(TokParams p) {
   wait_vmcnt<0>();
 
   // selected count of key column lane % 32 of the tile (q0, ktok0) over the
-  // wave's 32 query rows (the same value in both half-waves); marks served
-  // frame pairs
+  // wave's 32 query rows (the same value in both half-waves)
   auto tile_count = [&](const unsigned char* kbuf, int ksub, int ktok0, FrameAt kat) -> int {
     const TileInfo ti = classify(p, q0, qat, ktok0, kat, L.s_w, L.s_ret);
     if (ti.cls == kNone) return 0;
@@ -1160,7 +1163,6 @@ __global__ __launch_bounds__(kThreads) void mark_kernel(TokParams p) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) below += (int)(__float_as_uint(acc[i] - ta) >> 31);
       const int c = 16 - below;
-      if (__ballot(c != 0) != 0ull && lane == 0) served_l[(ti.fq - f_lo) * p.Nf + ti.fk] = 1;
       return c + __shfl_xor(c, 32);
     } else {
       const TileFrames f = tile_frames_at(p, qat, kat, ktok0, lane);
@@ -1168,16 +1170,6 @@ __global__ __launch_bounds__(kThreads) void mark_kernel(TokParams p) {
       const float thr1 = (f.kvalid && f.f0 + 1 - f_lo < p.FR) ? thr_l[(f.f0 + 1 - f_lo) * p.Nf + f.fk] : INFINITY;
       unsigned inP2;
       select_bits(p, acc, f, q0, half, L.s_w, L.s_ret, thr0, thr1, sel, inP2);
-      // frame pairs with a selected t > 1 pair are served
-      const unsigned s2 = sel & inP2;
-      if (s2) {
-        for (int i = 0; i < 16; ++i)
-          if ((s2 >> i) & 1u) {
-            int u = f.u0 + row_of(i, half);
-            const int fq = f.f0 + (u >= p.Nt ? 1 : 0);
-            served_l[(fq - f_lo) * p.Nf + f.fk] = 1;
-          }
-      }
     }
     const int c = __popc(sel);
     return c + __shfl_xor(c, 32);
@@ -1234,8 +1226,7 @@ __global__ __launch_bounds__(kThreads) void mark_kernel(TokParams p) {
   }
   if (wave < kWaves) ring_leave(L, wave, lane, gave_up);
   __syncthreads();
-  // write out this split's flags (a contiguous run of each candidate row) and
-  // the served frame pairs
+  // write out this split's flags (a contiguous run of each candidate row)
   if (n > 0 && wave < G::QB && a0 + wave < p.Sb) {
     const int last = L.steps[n - 1];
     const int lo = pos_lo[wave];
@@ -1243,11 +1234,6 @@ __global__ __launch_bounds__(kThreads) void mark_kernel(TokParams p) {
     unsigned char* out = p.flags + (long long)b * p.nnz + p.row_ptr[a0 + wave] + lo;
     for (int i = lane; i < hi - lo; i += 64) out[i] = flags_l[wave * MS + i];
   }
-  for (int i = tid; i < p.FR * p.Nf; i += kThreads)
-    if (served_l[i]) {
-      const int fr = i / p.Nf, fk = i - fr * p.Nf;
-      p.served[(size_t)b * p.Nf * p.Nf + (size_t)(f_lo + fr) * p.Nf + fk] = 1;
-    }
 }
 
 // ---------------------------------------------------------------------------
