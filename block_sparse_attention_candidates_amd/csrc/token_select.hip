@@ -41,6 +41,8 @@
 //   compact:  one wavefront per (b, query block): flags -> ascending kept list,
 //             written for every head (flag_compact_kernel, shared with the
 //             static decay-state selector).
+#include <type_traits>
+
 #include "dr_internal.h"
 #include "lds_dma.h"
 
@@ -620,193 +622,212 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(TokParams p) {
                     __popc(L.bits[qb * L.nword + wi] & ((1u << (kb & 31)) - 1u)));
   }
 
-  // Per-lane running statistics, four sets: query frame f0w + fo (the wave's
-  // 32 rows span at most two frames) x key frame parity kp. Keys are walked in
-  // ascending order and the 32 keys of a tile span at most two adjacent frames,
-  // so the set of parity kp holds one key frame (tag0 / tag1) at a time; it is
-  // reduced over the wave and merged into the wave's LDS statistics once the
-  // walk has passed that frame. Per tile, a lane sums its (at most 16) logits
-  // and their squares in float32; the set adds those tile sums, scaled, as
-  // float64 power sums. The highest score keeps its position for safeguard (ii).
-  double rs[4] = {0.0, 0.0, 0.0, 0.0}, rq[4] = {0.0, 0.0, 0.0, 0.0};
-  int rn[4] = {0, 0, 0, 0};
-  float rm[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-  unsigned int rl[4] = {0xffffffffu, 0xffffffffu, 0xffffffffu, 0xffffffffu};
-  int tag0 = -1, tag1 = -1;   // key frame held by the parity-0 / parity-1 sets
-  auto tag_of = [&](int kp) -> int { return kp ? tag1 : tag0; };
-  auto set_tag = [&](int kp, int f) {
-    if (kp) tag1 = f;
-    else tag0 = f;
-  };
-  auto flush = [&](int kp) {
-    if (tag_of(kp) < 0) return;
+  // Per-lane running statistics, 2 * NF sets: query frame f0w + fo (fo < NF;
+  // NF = 2 only for a wave whose 32 rows cross a frame boundary, so that the
+  // other waves keep half the state and stay within the register budget) x key
+  // frame parity kp. Keys are walked in ascending order and the 32 keys of a
+  // tile span at most two adjacent frames, so the set of parity kp holds one key
+  // frame (tag0 / tag1) at a time; it is reduced over the wave and merged into
+  // the wave's LDS statistics once the walk has passed that frame. Per tile, a
+  // lane sums its (at most 16) logits and their squares in float32; the set adds
+  // those tile sums, scaled, as float64 power sums. The highest score keeps its
+  // position for safeguard (ii).
+  const int j0 = step_begin(s_nsteps, split);
+  bool gave_up = false;
+  if (wave >= kWaves) ring_load<D, BS, HF>(p, b, L, n, wave - kWaves, lane);
+  auto run = [&](auto nf_tag) {
+    constexpr int NF = decltype(nf_tag)::value, NS = 2 * NF;
+    double rs[NS], rq[NS];
+    int rn[NS];
+    float rm[NS];
+    unsigned int rl[NS];
 #pragma unroll
-    for (int fo = 0; fo < 2; ++fo) {
-      const int x = 2 * fo + kp;
-      int cnt = rn[x];
-#pragma unroll
-      for (int off = 32; off > 0; off >>= 1) cnt += __shfl_xor(cnt, off);
-      if (cnt > 0) {
-        const double sum = wave_sum(rs[x]), sq = wave_sum(rq[x]);
-        const unsigned long long mx = wave_max(rl[x] == 0xffffffffu ? 0ull : pack_max(rm[x], rl[x]));
-        const double nn = (double)cnt, mean = sum / nn;
-        double m2 = sq - sum * mean;
-        if (m2 < 0.0) m2 = 0.0;
-        if (lane == 0) merge(mine[fo * p.Nf + tag_of(kp)], nn, mean, m2, mx);
-      }
+    for (int x = 0; x < NS; ++x) {
       rs[x] = rq[x] = 0.0;
       rn[x] = 0;
       rm[x] = -INFINITY;
       rl[x] = 0xffffffffu;
     }
-    set_tag(kp, -1);
-  };
-  // add a lane's tile sums to set x (x may differ between lanes)
-  auto add = [&](int x, double ts, double tq, int tn, float tm, unsigned int tl) {
+    int tag0 = -1, tag1 = -1;   // key frame held by the parity-0 / parity-1 sets
+    auto tag_of = [&](int kp) -> int { return kp ? tag1 : tag0; };
+    auto set_tag = [&](int kp, int f) {
+      if (kp) tag1 = f;
+      else tag0 = f;
+    };
+    auto flush = [&](int kp) {
+      if (tag_of(kp) < 0) return;
 #pragma unroll
-    for (int y = 0; y < 4; ++y)
-      if (y == x) {
-        rs[y] += ts;
-        rq[y] += tq;
-        rn[y] += tn;
-        if (tm > rm[y] || (tm == rm[y] && tl < rl[y])) {
-          rm[y] = tm;
-          rl[y] = tl;
+      for (int fo = 0; fo < NF; ++fo) {
+        const int x = 2 * fo + kp;
+        int cnt = rn[x];
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) cnt += __shfl_xor(cnt, off);
+        if (cnt > 0) {
+          const double sum = wave_sum(rs[x]), sq = wave_sum(rq[x]);
+          const unsigned long long mx = wave_max(rl[x] == 0xffffffffu ? 0ull : pack_max(rm[x], rl[x]));
+          const double nn = (double)cnt, mean = sum / nn;
+          double m2 = sq - sum * mean;
+          if (m2 < 0.0) m2 = 0.0;
+          if (lane == 0) merge(mine[fo * p.Nf + tag_of(kp)], nn, mean, m2, mx);
         }
+        rs[x] = rq[x] = 0.0;
+        rn[x] = 0;
+        rm[x] = -INFINITY;
+        rl[x] = 0xffffffffu;
       }
-  };
+      set_tag(kp, -1);
+    };
+    // add a lane's tile sums to set x (x may differ between lanes)
+    auto add = [&](int x, double ts, double tq, int tn, float tm, unsigned int tl) {
+#pragma unroll
+      for (int y = 0; y < NS; ++y)
+        if (y == x) {
+          rs[y] += ts;
+          rq[y] += tq;
+          rn[y] += tn;
+          if (tm > rm[y] || (tm == rm[y] && tl < rl[y])) {
+            rm[y] = tm;
+            rl[y] = tl;
+          }
+        }
+    };
 
-  // key blocks stream through the LDS ring; a compute wave visits only its own
-  const int j0 = step_begin(s_nsteps, split);
-  bool gave_up = false;
-  if (wave >= kWaves) ring_load<D, BS, HF>(p, b, L, n, wave - kWaves, lane);
-  if (active_wave) {
-    walk_own(L, L.bits + qb * L.nword, n, j0, [&](int j, int kb) __attribute__((always_inline)) {
-      const int ent = entry++;
-      ring_wait<D, BS, HF>(p, L, wave, lane, j, gave_up);
-      const unsigned char* kbuf = L.kbuf(j);
-      const int info = L.sinfo[j];
-      const FrameAt kat0{info & 255, info >> 8};
-#pragma unroll 1
-      for (int ksub = 0; ksub < BS / 32; ++ksub) {
-        const int ktok0 = kb * BS + 32 * ksub;
-        if (ktok0 >= p.S) break;
-        const FrameAt kat = frame_after(kat0, 32 * ksub, p.Nt);
-        const TileInfo ti = classify(p, q0, qat, ktok0, kat, L.s_w, L.s_ret);
-        if (ti.cls == kNone || ti.cls == kAllNear) continue;      // no t > 1 pair of P
-        // retire the sets whose key frame the walk has passed
-        const int fk_first = kat.f;
+    // key blocks stream through the LDS ring; a compute wave visits only its own
+    if (active_wave) {
+      walk_own(L, L.bits + qb * L.nword, n, j0, [&](int j, int kb) __attribute__((always_inline)) {
+        const int ent = entry++;
+        ring_wait<D, BS, HF>(p, L, wave, lane, j, gave_up);
+        const unsigned char* kbuf = L.kbuf(j);
+        const int info = L.sinfo[j];
+        const FrameAt kat0{info & 255, info >> 8};
+  #pragma unroll 1
+        for (int ksub = 0; ksub < BS / 32; ++ksub) {
+          const int ktok0 = kb * BS + 32 * ksub;
+          if (ktok0 >= p.S) break;
+          const FrameAt kat = frame_after(kat0, 32 * ksub, p.Nt);
+          const TileInfo ti = classify(p, q0, qat, ktok0, kat, L.s_w, L.s_ret);
+          if (ti.cls == kNone || ti.cls == kAllNear) continue;      // no t > 1 pair of P
+          // retire the sets whose key frame the walk has passed
+          const int fk_first = kat.f;
+  #pragma unroll
+          for (int kp = 0; kp < 2; ++kp)
+            if (tag_of(kp) >= 0 && tag_of(kp) < fk_first) flush(kp);
+          const floatx16 acc = tile_scores<D, BS, HF>(qf, kbuf, ksub, lane);
+          if (ti.cls == kAllScored) {
+            // all 1024 pairs in P(fq, fk): one set, no masks. Sums of the lane's
+            // 16 logits in float32, scaled into the float64 set; the scale is
+            // positive, so the tile maximum scales to the maximum score.
+            set_tag(ti.fk & 1, ti.fk);
+            const int x = 2 * (ti.fq - f0w) + (ti.fk & 1);
+            float ts = 0.f, tq = 0.f, m = -INFINITY;
+  #pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              ts += acc[i];
+              tq = fmaf(acc[i], acc[i], tq);
+              m = fmaxf(m, acc[i]);
+            }
+            // the tile's key-column sums for the decision pass (B_s = 32): lanes
+            // l and l ^ 32 hold the two 16-row halves of column l % 32
+            const float cs = sum_halves(ts), cq = sum_halves(tq);
+            const float ms = m * p.scale;
+            float cur = rm[0];
 #pragma unroll
-        for (int kp = 0; kp < 2; ++kp)
-          if (tag_of(kp) >= 0 && tag_of(kp) < fk_first) flush(kp);
-        const floatx16 acc = tile_scores<D, BS, HF>(qf, kbuf, ksub, lane);
-        if (ti.cls == kAllScored) {
-          // all 1024 pairs in P(fq, fk): one set, no masks. Sums of the lane's
-          // 16 logits in float32, scaled into the float64 set; the scale is
-          // positive, so the tile maximum scales to the maximum score.
-          set_tag(ti.fk & 1, ti.fk);
-          const int x = 2 * (ti.fq - f0w) + (ti.fk & 1);
-          float ts = 0.f, tq = 0.f, m = -INFINITY;
-#pragma unroll
+            for (int y = 1; y < NS; ++y)
+              if (x == y) cur = rm[y];
+            unsigned int loc = 0xffffffffu;
+            if (__ballot(ms >= cur) != 0ull) {
+              // first of the lane's rows reaching m: rows ascend with i, and so
+              // does the position u * N_t + v
+              int first = 15;
+  #pragma unroll
+              for (int i = 15; i >= 0; --i)
+                if (acc[i] == m) first = i;
+              loc = (unsigned)((qat.u + row_of(first, half)) * p.Nt + (kat.u + (lane & 31)));
+            }
+            const double sc = (double)p.scale;
+            add(x, (double)ts * sc, (double)tq * (sc * sc), 16, ms, loc);
+            if constexpr (BS == 32) {
+              // stored after the set update: the spill reloads there wait for
+              // every memory operation in flight, this store included
+              compiler_fence();
+              floatx2* o = reinterpret_cast<floatx2*>(p.colsum) + ((size_t)b * p.nnz + (size_t)ent) * 32;
+              if (lane < 32) o[lane] = floatx2{cs, cq};
+            }
+            continue;
+          }
+          // general tile: pairs split by query frame f0 + fo and the lane's key frame
+          const TileFrames f = tile_frames_at(p, qat, kat, ktok0, lane);
+          set_tag(fk_first & 1, fk_first);
+          if (kat.u + min(31, p.S - 1 - ktok0) >= p.Nt) set_tag((fk_first + 1) & 1, fk_first + 1);
+          const int t0 = f.f0 > f.fk ? f.f0 - f.fk : f.fk - f.f0;
+          const int t1 = f.f0 + 1 > f.fk ? f.f0 + 1 - f.fk : f.fk - f.f0 - 1;
+          const bool ok0 = f.kvalid && t0 > 1 && t0 < p.Nf && L.s_ret[t0];
+          const bool ok1 = f.kvalid && t1 > 1 && t1 < p.Nf && L.s_ret[t1];
+          const int w0 = t0 < p.Nf ? L.s_w[t0] : 0, w1 = t1 < p.Nf ? L.s_w[t1] : 0;
+          // per query frame f0 (suffix 0) and f0 + 1 (suffix 1); scalars, so that
+          // a lane-dependent choice never indexes memory
+          float ts0 = 0.f, tq0 = 0.f, ts1 = 0.f, tq1 = 0.f;
+          int tn0 = 0, tn1 = 0;
+          float tm0 = -INFINITY, tm1 = -INFINITY;
+          unsigned int tl0 = 0xffffffffu, tl1 = 0xffffffffu;
+  #pragma unroll
           for (int i = 0; i < 16; ++i) {
-            ts += acc[i];
-            tq = fmaf(acc[i], acc[i], tq);
-            m = fmaxf(m, acc[i]);
+            const int r = row_of(i, half);
+            if (q0 + r >= p.S) continue;
+            int u = f.u0 + r;
+            const bool second = u >= p.Nt;
+            if (second) u -= p.Nt;
+            const int du = u > f.uk ? u - f.uk : f.uk - u;
+            if (!(second ? (ok1 && du <= w1) : (ok0 && du <= w0))) continue;
+            const float a = acc[i];
+            const float v = a * p.scale;
+            const unsigned int loc = (unsigned)(u * p.Nt + f.uk);
+            // rows ascend with i: the first maximum has the lowest position
+            if (second) {
+              ts1 += a;
+              tq1 = fmaf(a, a, tq1);
+              ++tn1;
+              if (v > tm1) {
+                tm1 = v;
+                tl1 = loc;
+              }
+            } else {
+              ts0 += a;
+              tq0 = fmaf(a, a, tq0);
+              ++tn0;
+              if (v > tm0) {
+                tm0 = v;
+                tl0 = loc;
+              }
+            }
           }
-          // the tile's key-column sums for the decision pass (B_s = 32): lanes
-          // l and l ^ 32 hold the two 16-row halves of column l % 32
-          const float cs = sum_halves(ts), cq = sum_halves(tq);
-          const float ms = m * p.scale;
-          const float cur = x == 0 ? rm[0] : (x == 1 ? rm[1] : (x == 2 ? rm[2] : rm[3]));
-          unsigned int loc = 0xffffffffu;
-          if (__ballot(ms >= cur) != 0ull) {
-            // first of the lane's rows reaching m: rows ascend with i, and so
-            // does the position u * N_t + v
-            int first = 15;
-#pragma unroll
-            for (int i = 15; i >= 0; --i)
-              if (acc[i] == m) first = i;
-            loc = (unsigned)((qat.u + row_of(first, half)) * p.Nt + (kat.u + (lane & 31)));
-          }
+          const int kp = f.fk & 1;
           const double sc = (double)p.scale;
-          add(x, (double)ts * sc, (double)tq * (sc * sc), 16, ms, loc);
+          if (tn0 > 0) add(kp, (double)ts0 * sc, (double)tq0 * (sc * sc), tn0, tm0, tl0);
+          if constexpr (NF == 2) {
+            if (tn1 > 0) add(2 + kp, (double)ts1 * sc, (double)tq1 * (sc * sc), tn1, tm1, tl1);
+          }
           if constexpr (BS == 32) {
-            // stored after the set update: the spill reloads there wait for
-            // every memory operation in flight, this store included
-            compiler_fence();
-            floatx2* o = reinterpret_cast<floatx2*>(p.colsum) + ((size_t)b * p.nnz + (size_t)ent) * 32;
-            if (lane < 32) o[lane] = floatx2{cs, cq};
-          }
-          continue;
-        }
-        // general tile: pairs split by query frame f0 + fo and the lane's key frame
-        const TileFrames f = tile_frames_at(p, qat, kat, ktok0, lane);
-        set_tag(fk_first & 1, fk_first);
-        if (kat.u + min(31, p.S - 1 - ktok0) >= p.Nt) set_tag((fk_first + 1) & 1, fk_first + 1);
-        const int t0 = f.f0 > f.fk ? f.f0 - f.fk : f.fk - f.f0;
-        const int t1 = f.f0 + 1 > f.fk ? f.f0 + 1 - f.fk : f.fk - f.f0 - 1;
-        const bool ok0 = f.kvalid && t0 > 1 && t0 < p.Nf && L.s_ret[t0];
-        const bool ok1 = f.kvalid && t1 > 1 && t1 < p.Nf && L.s_ret[t1];
-        const int w0 = t0 < p.Nf ? L.s_w[t0] : 0, w1 = t1 < p.Nf ? L.s_w[t1] : 0;
-        // per query frame f0 (suffix 0) and f0 + 1 (suffix 1); scalars, so that
-        // a lane-dependent choice never indexes memory
-        float ts0 = 0.f, tq0 = 0.f, ts1 = 0.f, tq1 = 0.f;
-        int tn0 = 0, tn1 = 0;
-        float tm0 = -INFINITY, tm1 = -INFINITY;
-        unsigned int tl0 = 0xffffffffu, tl1 = 0xffffffffu;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int r = row_of(i, half);
-          if (q0 + r >= p.S) continue;
-          int u = f.u0 + r;
-          const bool second = u >= p.Nt;
-          if (second) u -= p.Nt;
-          const int du = u > f.uk ? u - f.uk : f.uk - u;
-          if (!(second ? (ok1 && du <= w1) : (ok0 && du <= w0))) continue;
-          const float a = acc[i];
-          const float v = a * p.scale;
-          const unsigned int loc = (unsigned)(u * p.Nt + f.uk);
-          // rows ascend with i: the first maximum has the lowest position
-          if (second) {
-            ts1 += a;
-            tq1 = fmaf(a, a, tq1);
-            ++tn1;
-            if (v > tm1) {
-              tm1 = v;
-              tl1 = loc;
-            }
-          } else {
-            ts0 += a;
-            tq0 = fmaf(a, a, tq0);
-            ++tn0;
-            if (v > tm0) {
-              tm0 = v;
-              tl0 = loc;
+            if (ti.cls == kCutScored || key_straddle(p, q0, qat, ktok0, ti)) {
+              // the rows lie in one query frame and each key column in one frame
+              // pair (a tile cut by the window, or whose keys cross a frame
+              // boundary): the columns' in-P sums for the decision pass (after
+              // the set update, as above)
+              const float cs = sum_halves(ts0), cq = sum_halves(tq0);
+              compiler_fence();
+              floatx2* o = reinterpret_cast<floatx2*>(p.colsum) + ((size_t)b * p.nnz + (size_t)ent) * 32;
+              if (lane < 32) o[lane] = floatx2{cs, cq};
             }
           }
         }
-        const int kp = f.fk & 1;
-        const double sc = (double)p.scale;
-        if (tn0 > 0) add(kp, (double)ts0 * sc, (double)tq0 * (sc * sc), tn0, tm0, tl0);
-        if (tn1 > 0) add(2 + kp, (double)ts1 * sc, (double)tq1 * (sc * sc), tn1, tm1, tl1);
-        if constexpr (BS == 32) {
-          if (ti.cls == kCutScored || key_straddle(p, q0, qat, ktok0, ti)) {
-            // the rows lie in one query frame and each key column in one frame
-            // pair (a tile cut by the window, or whose keys cross a frame
-            // boundary): the columns' in-P sums for the decision pass (after
-            // the set update, as above)
-            const float cs = sum_halves(ts0), cq = sum_halves(tq0);
-            compiler_fence();
-            floatx2* o = reinterpret_cast<floatx2*>(p.colsum) + ((size_t)b * p.nnz + (size_t)ent) * 32;
-            if (lane < 32) o[lane] = floatx2{cs, cq};
-          }
-        }
-      }
-    });
-  }
-  if (wave < kWaves) ring_leave(L, wave, lane, gave_up);
-  flush(0);
-  flush(1);
+      });
+    }
+    if (wave < kWaves) ring_leave(L, wave, lane, gave_up);
+    flush(0);
+    flush(1);
+  };
+  if (active_wave && qat.u + 31 >= p.Nt) run(std::integral_constant<int, 2>{});
+  else run(std::integral_constant<int, 1>{});
   __syncthreads();
   // merge the waves in order into the workgroup partial: [FR][Nf] per workgroup
   const int f_lo = (a0 * BS) / p.Nt;
