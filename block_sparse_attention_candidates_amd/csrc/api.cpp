@@ -150,9 +150,10 @@ TokWs tok_ws(const dr_dims* d, const dr_radial_cfg* c, int Sb, long long S, long
   off = align256(off + fpairs * sizeof(int));
   w.flags = off;
   off = align256(off + (size_t)d->batch * nnz);
-  w.decide = c->block_size == 32;
+  w.decide = c->block_size <= 64;   // one 32 x 32 tile's column sums per sub-tile pair
+  const size_t tiles = w.decide ? (size_t)(c->block_size / 32) * (c->block_size / 32) : 0;
   w.colsum = off;
-  if (w.decide) off = align256(off + (size_t)d->batch * nnz * 32 * 2 * sizeof(float));
+  if (w.decide) off = align256(off + (size_t)d->batch * nnz * tiles * 32 * 2 * sizeof(float));
   w.und = off;
   if (w.decide) off = align256(off + (size_t)d->batch * nnz);
   w.total = off;

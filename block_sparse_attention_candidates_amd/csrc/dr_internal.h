@@ -285,10 +285,10 @@ struct TokParams {
   double* fn;          // [B][Nf][Nf] size of P(i, j) for t > 1 (0: none)
   int* served;         // [B][Nf][Nf] 1 if some t > 1 pair is selected
   unsigned char* flags;  // [B][nnz] block decision per candidate entry
-  // B_s = 32 only (else null): per candidate entry whose tile lies in one
-  // P(i, j) with t > 1, each key column's sum of logits and of their squares
-  // (float32, [B][nnz][32][2]); and whether the mark pass must decide the
-  // entry ([B][nnz], 1) or its flag is already fixed (0)
+  // B_s <= 64 only (else null): per candidate entry and 32 x 32 tile of it
+  // whose query rows lie in one frame, each key column's sum of logits in P
+  // and of their squares (float32, [B][nnz][(B_s/32)^2][32][2]); and whether
+  // the mark pass must decide the entry ([B][nnz], 1) or its flag is fixed (0)
   float* colsum;
   unsigned char* und;
 };

@@ -62,7 +62,10 @@ constexpr int kRingMax = 16;            // ring depth limit (key blocks)
 constexpr int kTokLdsBytes = 160 * 1024; // LDS per workgroup on gfx950
 constexpr int kDone = 0x3fffffff;       // progress of a wave that reads no more blocks
 constexpr int kOpenChunk = 16;          // candidate entries per wavefront of mark_open_kernel
-constexpr int kDecideUnroll = 4;        // entries per half-wave of decide_kernel with loads in flight
+constexpr int kDecideUnroll = 4;        // entries per lane group of decide_kernel with loads in flight
+// Block sizes whose mark pass is the decision pass plus the open-entry kernel
+// (one block pair = (B_s / 32)^2 tiles of 32 x 32, each with its own column sums).
+constexpr int kDecideMaxBs = 64;
 
 typedef int intx4 __attribute__((ext_vector_type(4)));
 #define DR_LDS __attribute__((address_space(3)))
@@ -301,6 +304,14 @@ __device__ __forceinline__ TileInfo classify(const TokParams& p, int q0, FrameAt
 // frame pair.
 __device__ __forceinline__ bool key_straddle(const TokParams& p, int q0, FrameAt q, int k0, const TileInfo& ti) {
   return ti.cls == kGeneral && q0 + 31 < p.S && k0 + 31 < p.S && q.u + 31 < p.Nt;
+}
+
+// Key-column sums of tile (row tile sub, key sub-block ksub) of candidate entry
+// ent of batch element b: 32 (sum, sum of squares) pairs.
+template <int BS>
+__device__ __forceinline__ floatx2* colsum_of(const TokParams& p, int b, long long ent, int sub, int ksub) {
+  constexpr int QS = BS / 32;
+  return reinterpret_cast<floatx2*>(p.colsum) + (((size_t)b * p.nnz + (size_t)ent) * (QS * QS) + sub * QS + ksub) * 32;
 }
 
 // Selection bits (one per element i) of a tile under the thresholds of the
@@ -612,11 +623,11 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(TokParams p) {
   const int f0w = q0 / p.Nt;
   const FrameAt qat{f0w, q0 - f0w * p.Nt};   // frame and index of the wave's first row
   Stat* mine = acc_l + wave * 2 * p.Nf;
-  // B_s = 32: candidate entry of the wave's current step. The walk visits the
+  // B_s <= 64: candidate entry of the wave's current step. The walk visits the
   // wave's candidates in ascending key order, one entry after another, from
   // the first at or after the split's first step.
   int entry = 0;
-  if (BS == 32 && active_wave && n > 0) {
+  if (BS <= kDecideMaxBs && active_wave && n > 0) {
     const int kb = L.steps[0], wi = kb >> 5;
     entry = uniform(p.row_ptr[a] + L.pre[qb * L.nword + wi] +
                     __popc(L.bits[qb * L.nword + wi] & ((1u << (kb & 31)) - 1u)));
@@ -746,12 +757,11 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(TokParams p) {
             }
             const double sc = (double)p.scale;
             add(x, (double)ts * sc, (double)tq * (sc * sc), 16, ms, loc);
-            if constexpr (BS == 32) {
-              // stored after the set update: the spill reloads there wait for
+            if constexpr (BS <= kDecideMaxBs) {
+              // stored after the set update: spill reloads there would wait for
               // every memory operation in flight, this store included
               compiler_fence();
-              floatx2* o = reinterpret_cast<floatx2*>(p.colsum) + ((size_t)b * p.nnz + (size_t)ent) * 32;
-              if (lane < 32) o[lane] = floatx2{cs, cq};
+              if (lane < 32) colsum_of<BS>(p, b, ent, sub, ksub)[lane] = floatx2{cs, cq};
             }
             continue;
           }
@@ -807,7 +817,7 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(TokParams p) {
           if constexpr (NF == 2) {
             if (tn1 > 0) add(2 + kp, (double)ts1 * sc, (double)tq1 * (sc * sc), tn1, tm1, tl1);
           }
-          if constexpr (BS == 32) {
+          if constexpr (BS <= kDecideMaxBs) {
             if (ti.cls == kCutScored || key_straddle(p, q0, qat, ktok0, ti)) {
               // the rows lie in one query frame and each key column in one frame
               // pair (a tile cut by the window, or whose keys cross a frame
@@ -815,8 +825,7 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(TokParams p) {
               // the set update, as above)
               const float cs = sum_halves(ts0), cq = sum_halves(tq0);
               compiler_fence();
-              floatx2* o = reinterpret_cast<floatx2*>(p.colsum) + ((size_t)b * p.nnz + (size_t)ent) * 32;
-              if (lane < 32) o[lane] = floatx2{cs, cq};
+              if (lane < 32) colsum_of<BS>(p, b, ent, sub, ksub)[lane] = floatx2{cs, cq};
             }
           }
         }
@@ -936,12 +945,15 @@ __device__ __forceinline__ bool block_kept(const TokParams& p, const int* cnt, i
 // ---------------------------------------------------------------------------
 template <int D, int BS, int HF>
 __global__ __launch_bounds__(256) void decide_kernel(TokParams p) {
-  static_assert(BS == 32, "one 32x32 tile per block pair");
+  static_assert(BS == 32 || BS == 64, "a block pair's key columns on one lane group");
+  constexpr int QS = BS / 32;           // 32-row (and 32-key) sub-tiles per side
+  constexpr int EPW = 64 / BS;          // entries per wavefront (lane group = BS lanes)
+  constexpr int GROUPS = 256 / BS;      // lane groups per workgroup
   __shared__ int s_w[kMaxTokenFrames], s_ret[kMaxTokenFrames];
   __shared__ float s_thra[kMaxTokenFrames];   // logit threshold against key frame fk
-  const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5, col = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, col = tid % BS, grp = tid / BS;
   const int a = blockIdx.x, b = blockIdx.y;
-  const int q0 = a * 32;
+  const int q0 = a * BS;
   const FrameAt qat{q0 / p.Nt, q0 - (q0 / p.Nt) * p.Nt};
   for (int t = tid; t < p.Nf; t += 256) {
     int w, sf;
@@ -951,39 +963,49 @@ __global__ __launch_bounds__(256) void decide_kernel(TokParams p) {
     s_thra[t] = logit_threshold(p.thr[((size_t)b * p.Nf + qat.f) * p.Nf + t], p.scale);
   }
   __syncthreads();
-  const int min_c = min_count(32, p.theta_c), min_a = min_count(32, p.theta_m);
+  const int min_c = min_count(BS, p.theta_c), min_a = min_count(BS, p.theta_m);
   const int e0 = p.row_ptr[a], e1 = p.row_ptr[a + 1];
   const size_t eb = (size_t)b * p.nnz;
-  const unsigned long long halfmask = half ? 0xffffffff00000000ull : 0xffffffffull;
-  const bool rows_one_frame = q0 + 31 < p.S && qat.u + 31 < p.Nt;
-  const floatx2* colsum = reinterpret_cast<const floatx2*>(p.colsum);
-  // kDecideUnroll entries per half-wave in flight: their loads first
-  for (int base = e0 + (tid >> 5); base - (tid >> 5) < e1; base += 8 * kDecideUnroll) {
+  const unsigned long long gmask = EPW == 1 ? ~0ull : ((lane >> 5) ? 0xffffffff00000000ull : 0xffffffffull);
+  // every row of the block valid and in frame qat.f
+  const bool rows_one_frame = q0 + BS - 1 < p.S && qat.u + BS - 1 < p.Nt;
+  const int ksub = col >> 5, c32 = col & 31;   // this lane's key sub-block and column in it
+  // kDecideUnroll entries per lane group in flight: their loads first
+  for (int base = e0 + grp; base - grp < e1; base += GROUPS * kDecideUnroll) {
     int k0s[kDecideUnroll];
-    floatx2 sums[kDecideUnroll];
+    floatx2 sums[kDecideUnroll][QS];
 #pragma unroll
     for (int j = 0; j < kDecideUnroll; ++j) {
-      const int e = base + 8 * j;
-      k0s[j] = e < e1 ? p.cols[e] * 32 : p.S;
-      // read whether or not the entry needs it: unused values are discarded
-      sums[j] = e < e1 ? colsum[(eb + (size_t)e) * 32 + col] : floatx2{0.f, 0.f};
+      const int e = base + GROUPS * j;
+      k0s[j] = e < e1 ? p.cols[e] * BS : p.S;
+      // read whether or not the entry needs them: unused values are discarded
+#pragma unroll
+      for (int sub = 0; sub < QS; ++sub)
+        sums[j][sub] = e < e1 ? colsum_of<BS>(p, b, e, sub, ksub)[c32] : floatx2{0.f, 0.f};
     }
 #pragma unroll
     for (int j = 0; j < kDecideUnroll; ++j) {
-      const int e = base + 8 * j;
+      const int e = base + GROUPS * j;
       const bool valid = e < e1;
       const int k0 = k0s[j];
-      // the tile's 32 query rows lie in frame qat.f; each key column v of it
-      // in one key frame fk (its 32 keys may cross one frame boundary, N_t >= 32)
-      const bool open_tile = !(valid && rows_one_frame && k0 + 31 < p.S);
+      // the block's query rows lie in frame qat.f; each key column of it in
+      // one key frame fk (its keys may cross one frame boundary, N_t >= B_s)
+      const bool open_tile = !(valid && rows_one_frame && k0 + BS - 1 < p.S);
       bool act = false, inact = false;
       if (!open_tile) {
         const int kt = k0 + col;
         const int fk = kt / p.Nt, v = kt - fk * p.Nt;
-        // the column's pairs in P(qat.f, fk): its in-window rows, if retained
+        // the column's pairs in P(qat.f, fk): its in-window rows, if retained,
+        // per 32-row sub-tile
         const int t = qat.f > fk ? qat.f - fk : fk - qat.f;
         const int w = s_w[t];
-        const int nin = s_ret[t] ? max(0, min(qat.u + 31, v + w) - max(qat.u, v - w) + 1) : 0;
+        int nin = 0, nsub[QS];
+#pragma unroll
+        for (int sub = 0; sub < QS; ++sub) {
+          const int u0 = qat.u + 32 * sub;
+          nsub[sub] = s_ret[t] ? max(0, min(u0 + 31, v + w) - max(u0, v - w) + 1) : 0;
+          nin += nsub[sub];
+        }
         if (t <= 1 || nin == 0) {
           // all of them selected (t <= 1), or none exist
           act = (t <= 1 ? nin : 0) >= min_c;
@@ -992,9 +1014,18 @@ __global__ __launch_bounds__(256) void decide_kernel(TokParams p) {
           // with n values, mean m, population variance var and the threshold T:
           // M = n Qhi - sa^2 >= n^2 var, dn = n (T - m) or n (m - T) less e1s;
           // the Cantelli tests n var / (var + d^2) < min_c and
-          // n d^2 / (var + d^2) > min_c - 1 multiplied through by n^2 (var + d^2)
+          // n d^2 / (var + d^2) > min_c - 1 multiplied through by n^2 (var + d^2).
+          // A sub-tile's sums exist wherever it has in-window rows (the
+          // statistics pass stores them for every such tile).
           const double n = (double)nin, u = 0x1p-24;
-          const double S1 = sums[j][0], Q = sums[j][1], T = s_thra[fk];
+          double S1 = 0.0, Q = 0.0;
+#pragma unroll
+          for (int sub = 0; sub < QS; ++sub)
+            if (nsub[sub] > 0) {
+              S1 += (double)sums[j][sub][0];
+              Q += (double)sums[j][sub][1];
+            }
+          const double T = s_thra[fk];
           const double Qhi = Q * (1.0 + 20.0 * u);                               // >= the exact sum of squares
           const double e1s = 20.0 * u * (double)sqrtf((float)(n * Qhi)) * (1.0 + 1e-6);  // >= |S1 - the exact sum|
           const double sa = fmax(0.0, fabs(S1) - e1s);
@@ -1009,8 +1040,8 @@ __global__ __launch_bounds__(256) void decide_kernel(TokParams p) {
           }
         }
       }
-      const int n_act = __popcll(__ballot(act) & halfmask), n_in = __popcll(__ballot(inact) & halfmask);
-      const bool decided = !open_tile && (n_act >= min_a || 32 - n_in < min_a);
+      const int n_act = __popcll(__ballot(act) & gmask), n_in = __popcll(__ballot(inact) & gmask);
+      const bool decided = !open_tile && (n_act >= min_a || BS - n_in < min_a);
       if (valid && col == 0) {
         if (decided) p.flags[eb + e] = n_act >= min_a ? 1 : 0;
         p.und[eb + e] = decided ? 0 : 1;
@@ -1029,9 +1060,9 @@ __global__ __launch_bounds__(256) void decide_kernel(TokParams p) {
 // each open entry's key fragments straight from memory. Served frame pairs
 // are already final (reduce kernel).
 // ---------------------------------------------------------------------------
-template <int D, int HF>
+template <int D, int BS, int HF>
 __global__ __launch_bounds__(256) void mark_open_kernel(TokParams p) {
-  constexpr int BS = 32;
+  constexpr int QS = BS / 32;           // 32-row (and 32-key) sub-tiles per side
   __shared__ int s_w[kMaxTokenFrames], s_ret[kMaxTokenFrames];
   const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5, wave = tid >> 6;
   const int b = blockIdx.y;
@@ -1058,7 +1089,7 @@ __global__ __launch_bounds__(256) void mark_open_kernel(TokParams p) {
   int a = lo, a_end = uniform(p.row_ptr[a + 1]);
   const float* thr = p.thr + (size_t)b * p.Nf * p.Nf;
   bf16x8 qf[HF][D / 16];
-  int a_loaded = -1;
+  int q_loaded = -1;   // first row of the query fragments in registers
   while (open) {
     const long long e = c0 + __ffsll(open) - 1;
     open &= open - 1;
@@ -1066,49 +1097,66 @@ __global__ __launch_bounds__(256) void mark_open_kernel(TokParams p) {
       ++a;
       a_end = uniform(p.row_ptr[a + 1]);
     }
-    const int q0 = a * BS;
-    if (a != a_loaded) {
-      load_q<D, HF>(p, b, q0, lane, qf);
-      a_loaded = a;
-    }
-    const int nq = min(BS, p.S - q0);
-    const FrameAt qat{q0 / p.Nt, q0 - (q0 / p.Nt) * p.Nt};
-    const int k0 = uniform(p.cols[e]) * BS;
-    const FrameAt kat{k0 / p.Nt, k0 - (k0 / p.Nt) * p.Nt};
-    const int nk = min(BS, p.S - k0);
-    const TileInfo ti = classify(p, q0, qat, k0, kat, s_w, s_ret);
-    int c = ti.cls == kAllNear ? 32 : 0;
-    if (ti.cls != kNone && ti.cls != kAllNear) {
-      // key fragments of every fused head (rows past S read the last token;
-      // those columns are outside P)
-      const int key = min(k0 + (lane & 31), p.S - 1);
-      floatx16 acc = {};
+    const int kb0 = uniform(p.cols[e]) * BS;
+    const int nq = min(BS, p.S - a * BS), nk = min(BS, p.S - kb0);
+    // selected count of key column 32 * ksub + lane % 32, summed over the
+    // block's 32-row sub-tiles (both half-waves hold it)
+    int cnt[QS];
 #pragma unroll
-      for (int h = 0; h < HF; ++h) {
-        const uint16_t* row = p.k + ((size_t)(b * p.H + h) * p.S + key) * D;
-        bf16x8 kf[D / 16];
-#pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk)
-          kf[kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(row + (2 * kk + half) * 8));
-#pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[h][kk], kf[kk], acc, 0, 0, 0);
+    for (int ks = 0; ks < QS; ++ks) cnt[ks] = 0;
+#pragma unroll 1
+    for (int sub = 0; sub < QS; ++sub) {
+      const int q0 = a * BS + 32 * sub;
+      if (q0 >= p.S) break;
+      if (q0 != q_loaded) {
+        load_q<D, HF>(p, b, q0, lane, qf);
+        q_loaded = q0;
       }
-      if (ti.cls == kAllScored) {
-        const float ta = logit_threshold(thr[ti.fq * p.Nf + ti.fk], p.scale);
-        int below = 0;
+      const FrameAt qat{q0 / p.Nt, q0 - (q0 / p.Nt) * p.Nt};
 #pragma unroll
-        for (int i = 0; i < 16; ++i) below += (int)(__float_as_uint(acc[i] - ta) >> 31);
-        c = 16 - below;
-      } else {
-        const TileFrames f = tile_frames_at(p, qat, kat, k0, lane);
-        const float thr0 = f.kvalid ? thr[f.f0 * p.Nf + f.fk] : INFINITY;
-        const float thr1 = (f.kvalid && f.f0 + 1 < p.Nf) ? thr[(f.f0 + 1) * p.Nf + f.fk] : INFINITY;
-        unsigned sel, inP2;
-        select_bits(p, acc, f, q0, half, s_w, s_ret, thr0, thr1, sel, inP2);
-        c = __popc(sel);
+      for (int ks = 0; ks < QS; ++ks) {
+        const int k0 = kb0 + 32 * ks;
+        if (k0 >= p.S) break;
+        const FrameAt kat{k0 / p.Nt, k0 - (k0 / p.Nt) * p.Nt};
+        const TileInfo ti = classify(p, q0, qat, k0, kat, s_w, s_ret);
+        int c = ti.cls == kAllNear ? 32 : 0;
+        if (ti.cls != kNone && ti.cls != kAllNear) {
+          // key fragments of every fused head (rows past S read the last token;
+          // those columns are outside P)
+          const int key = min(k0 + (lane & 31), p.S - 1);
+          floatx16 acc = {};
+#pragma unroll
+          for (int h = 0; h < HF; ++h) {
+            const uint16_t* row = p.k + ((size_t)(b * p.H + h) * p.S + key) * D;
+            bf16x8 kf[D / 16];
+#pragma unroll
+            for (int kk = 0; kk < D / 16; ++kk)
+              kf[kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(row + (2 * kk + half) * 8));
+#pragma unroll
+            for (int kk = 0; kk < D / 16; ++kk)
+              acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[h][kk], kf[kk], acc, 0, 0, 0);
+          }
+          if (ti.cls == kAllScored) {
+            const float ta = logit_threshold(thr[ti.fq * p.Nf + ti.fk], p.scale);
+            int below = 0;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) below += (int)(__float_as_uint(acc[i] - ta) >> 31);
+            c = 16 - below;
+          } else {
+            const TileFrames f = tile_frames_at(p, qat, kat, k0, lane);
+            const float thr0 = f.kvalid ? thr[f.f0 * p.Nf + f.fk] : INFINITY;
+            const float thr1 = (f.kvalid && f.f0 + 1 < p.Nf) ? thr[(f.f0 + 1) * p.Nf + f.fk] : INFINITY;
+            unsigned sel, inP2;
+            select_bits(p, acc, f, q0, half, s_w, s_ret, thr0, thr1, sel, inP2);
+            c = __popc(sel);
+          }
+          c += __shfl_xor(c, 32);
+        }
+        cnt[ks] += c;
       }
-      c += __shfl_xor(c, 32);
     }
+    // lane l decides key column l of the block (B_s = 64) or l % 32 (B_s = 32)
+    const int c = QS == 1 ? cnt[0] : cnt[(lane >> 5) % QS];
     const int n_act = __popcll(__ballot(lane < nk && c >= min_count(nq, p.theta_c)));
     if (lane == 0) p.flags[eb + e] = n_act >= min_count(nk, p.theta_m) ? 1 : 0;
   }
@@ -1397,12 +1445,12 @@ hipError_t launch_all(TokParams p, int B, hipStream_t stream) {
   hipLaunchKernelGGL(reduce_kernel, dim3((unsigned)((p.Nf * p.Nf + 255) / 256), (unsigned)B), dim3(256), 0, stream,
                      p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  if constexpr (BS == 32) {
+  if constexpr (BS <= kDecideMaxBs) {
     if (!p.colsum || !p.und) return hipErrorInvalidValue;
     hipLaunchKernelGGL((decide_kernel<D, BS, HF>), dim3((unsigned)p.Sb, (unsigned)B), dim3(256), 0, stream, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const long long chunks = (p.nnz + kOpenChunk - 1) / kOpenChunk;
-    hipLaunchKernelGGL((mark_open_kernel<D, HF>), dim3((unsigned)((chunks + 3) / 4), (unsigned)B), dim3(256), 0,
+    hipLaunchKernelGGL((mark_open_kernel<D, BS, HF>), dim3((unsigned)((chunks + 3) / 4), (unsigned)B), dim3(256), 0,
                        stream, p);
   } else {
     hipLaunchKernelGGL((mark_kernel<D, BS, HF>), grid, dim3(kThreads), lds_mark, stream, p);

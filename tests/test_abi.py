@@ -155,8 +155,12 @@ def test_token_select_validation(dynrad_lib):
     # thr 64 B -> 256; maxima 128 B -> 256; counts 128 B -> 256; served 64 B -> 256; flags 64 B -> 256;
     # B_s = 32: column sums 64 entries x 32 columns x 8 B = 16384; undecided marks 64 B -> 256
     assert size.value == 2560 + 5 * 256 + 16384 + 256
-    cfg64 = _cfg(4, 64, 64, 1.0, 2.0)           # B_s = 64: no column sums
+    cfg64 = _cfg(4, 64, 64, 1.0, 2.0)           # B_s = 64: four 32 x 32 tiles' column sums per entry
     assert dynrad_lib.dr_token_select_workspace(ctypes.byref(dims), ctypes.byref(cfg64), ctypes.byref(tok), 16,
+                                                ctypes.byref(size)) == L.DR_OK
+    assert size.value == 2560 + 5 * 256 + 16 * 4 * 32 * 8 + 256
+    cfg128 = _cfg(4, 64, 128, 1.0, 2.0)         # B_s = 128: the ring mark pass, no column sums
+    assert dynrad_lib.dr_token_select_workspace(ctypes.byref(dims), ctypes.byref(cfg128), ctypes.byref(tok), 4,
                                                 ctypes.byref(size)) == L.DR_OK
     assert size.value == 2560 + 5 * 256
 
