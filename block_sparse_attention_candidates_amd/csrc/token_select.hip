@@ -17,9 +17,9 @@
 //             formula in float64, and the highest score with its position);
 //             each wave keeps its own LDS accumulators, merged in a fixed order
 //             into one partial per workgroup: no floating-point atomics.
-//             At B_s = 32 it also stores, for tiles whose query rows lie in
-//             one frame, each key column's float32 sum and sum of squares of
-//             its logits in P.
+//             At B_s <= 64 it also stores, for 32 x 32 tiles whose query rows
+//             lie in one frame, each key column's float32 sum and sum of
+//             squares of its logits in P.
 //   reduce:   per frame pair, the workgroup partials merged in workgroup order:
 //             mu, sigma (population), tau(t) by decay state (Eq. 11), and the
 //             threshold in score units thr = mu + tau * (sigma + eps) (Eq. 10
@@ -31,8 +31,8 @@
 //             active iff their selected share of the query tokens exceeds
 //             theta_c, and the block pair is kept iff the active share of the
 //             key tokens exceeds theta_m; one flag per candidate entry.
-//             B_s > 32: the stats pass's walk and tiles (mark_kernel).
-//             B_s = 32: decide_kernel fixes every flag that the column sums
+//             B_s = 128: the stats pass's walk and tiles (mark_kernel).
+//             B_s <= 64: decide_kernel fixes every flag that the column sums
 //             determine (exact counts, or Cantelli bounds on each column's
 //             count), and mark_open_kernel computes the tiles of the rest.
 //   fallback: for each unserved frame pair (safeguard (ii)), the block pair
@@ -737,7 +737,7 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(TokParams p) {
               tq = fmaf(acc[i], acc[i], tq);
               m = fmaxf(m, acc[i]);
             }
-            // the tile's key-column sums for the decision pass (B_s = 32): lanes
+            // the tile's key-column sums for the decision pass (B_s <= 64): lanes
             // l and l ^ 32 hold the two 16-row halves of column l % 32
             const float cs = sum_halves(ts), cq = sum_halves(tq);
             const float ms = m * p.scale;
@@ -925,12 +925,13 @@ __device__ __forceinline__ bool block_kept(const TokParams& p, const int* cnt, i
 }
 
 // ---------------------------------------------------------------------------
-// Pass 3a (B_s = 32): candidate entries whose flag follows without their
-// logits. When a tile's 32 query rows lie in one frame (and it stays clear of
+// Pass 3a (B_s <= 64): candidate entries whose flag follows without their
+// logits. When a block's query rows lie in one frame (and it stays clear of
 // the sequence end), each key column lies in one frame pair (also when the
 // keys cross a frame boundary), and its selected count is known outright if
 // that pair has t <= 1 (its in-window rows) or no pair in P (none). For t > 1,
 // Cantelli's inequality bounds the count of the column's n in-window logits
+// (over the block's 32-row tiles, whose column sums add)
 // at or above the logit threshold T: at most n v / (v + d^2) of them lie d or
 // more above their mean (v: population variance), and as many at most d or
 // more below it. Mean and variance come from the statistics pass's float32
@@ -941,7 +942,7 @@ __device__ __forceinline__ bool block_kept(const TokParams& p, const int* cnt, i
 // once enough columns are. Exact: a fixed flag is the flag the mark pass would
 // compute. The other entries (und = 1: query rows crossing a frame boundary,
 // the sequence end, columns the bound leaves open) go to mark_open_kernel.
-// One workgroup per (b, query block), one half-wave per entry (lane = column).
+// One workgroup per (b, query block), B_s lanes per entry (lane = key column).
 // ---------------------------------------------------------------------------
 template <int D, int BS, int HF>
 __global__ __launch_bounds__(256) void decide_kernel(TokParams p) {
@@ -1051,10 +1052,11 @@ __global__ __launch_bounds__(256) void decide_kernel(TokParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// Pass 3b (B_s = 32): the entries the decision pass left open, decided as the
-// mark pass below decides them. Few stay open (3.6% at wan14b_720p + "mid":
-// tiles cut by a frame or window edge, every entry of a query block that
-// straddles two frames), so there is no staging ring: one wavefront per
+// Pass 3b (B_s <= 64): the entries the decision pass left open, decided as the
+// mark pass below decides them. Few stay open (1.4% at wan14b_720p + "mid",
+// 2.5% at hunyuan_720p: every entry of a query block that straddles two
+// frames, the sequence end, columns the bound leaves open), so there is no
+// staging ring: one wavefront per
 // kOpenChunk consecutive candidate entries (rows with many open entries are
 // spread over many wavefronts) loads its query block's fragments and reads
 // each open entry's key fragments straight from memory. Served frame pairs
