@@ -41,6 +41,8 @@
 //   compact:  one wavefront per (b, query block): flags -> ascending kept list,
 //             written for every head (flag_compact_kernel, shared with the
 //             static decay-state selector).
+#include <cstdlib>
+#include <cstring>
 #include <type_traits>
 
 #include "dr_internal.h"
@@ -1431,6 +1433,12 @@ int ring_depth(int Sb, int Nf, int FR) {
   return 0;
 }
 
+// Whether the environment asks for the ring mark pass at every block size.
+inline bool ring_mark_requested() {
+  const char* v = std::getenv("DR_TOKEN_RING_MARK");
+  return v && std::strcmp(v, "0") != 0 && v[0] != '\0';
+}
+
 // Pass 5 (ordered compaction of the flags into kept lists of every head) is
 // flag_compact_kernel below.
 template <int D, int BS, int HF>
@@ -1447,16 +1455,21 @@ hipError_t launch_all(TokParams p, int B, hipStream_t stream) {
   hipLaunchKernelGGL(reduce_kernel, dim3((unsigned)((p.Nf * p.Nf + 255) / 256), (unsigned)B), dim3(256), 0, stream,
                      p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
+  // DR_TOKEN_RING_MARK=1 (a reference path for tests) runs the ring mark pass
+  // at B_s <= 64 too: the decision and open-entry passes must give its flags
+  bool ring = true;
   if constexpr (BS <= kDecideMaxBs) {
-    if (!p.colsum || !p.und) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((decide_kernel<D, BS, HF>), dim3((unsigned)p.Sb, (unsigned)B), dim3(256), 0, stream, p);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    const long long chunks = (p.nnz + kOpenChunk - 1) / kOpenChunk;
-    hipLaunchKernelGGL((mark_open_kernel<D, BS, HF>), dim3((unsigned)((chunks + 3) / 4), (unsigned)B), dim3(256), 0,
-                       stream, p);
-  } else {
-    hipLaunchKernelGGL((mark_kernel<D, BS, HF>), grid, dim3(kThreads), lds_mark, stream, p);
+    if (!ring_mark_requested()) {
+      ring = false;
+      if (!p.colsum || !p.und) return hipErrorInvalidValue;
+      hipLaunchKernelGGL((decide_kernel<D, BS, HF>), dim3((unsigned)p.Sb, (unsigned)B), dim3(256), 0, stream, p);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+      const long long chunks = (p.nnz + kOpenChunk - 1) / kOpenChunk;
+      hipLaunchKernelGGL((mark_open_kernel<D, BS, HF>), dim3((unsigned)((chunks + 3) / 4), (unsigned)B), dim3(256),
+                         0, stream, p);
+    }
   }
+  if (ring) hipLaunchKernelGGL((mark_kernel<D, BS, HF>), grid, dim3(kThreads), lds_mark, stream, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL((fallback_kernel<D, BS, HF>), dim3((unsigned)(p.Nf * p.Nf), (unsigned)B), dim3(64), 0, stream,
                      p);

@@ -179,7 +179,11 @@ dr_status dr_score_select(const dr_dims* dims, const dr_radial_cfg* cfg, const d
  * Outputs: kept_col / kept_cnt in the layout of dr_score_select.
  * Limits: tokens_per_frame in [32, 65535], num_frames <= 64, fused_heads in
  * {1, 2} (<= heads), eps > 0, tau_near and tau_far not NaN (+-inf allowed).
- * Deterministic: statistics are merged in a fixed order (no float atomics). */
+ * Deterministic: statistics are merged in a fixed order (no float atomics).
+ * At block size 32 and 64 most block decisions are fixed from per-column sums
+ * of the statistics pass (exactly: the same flags as computing every tile);
+ * the environment variable DR_TOKEN_RING_MARK=1, read at each call, makes the
+ * library compute every tile instead (a reference path for tests). */
 typedef struct dr_token_cfg {
   int32_t fused_heads;  /* H_f: 1 or 2 ([DR] Table 4: 2)                   */
   int32_t reserved;     /* must be 0                                        */

@@ -182,3 +182,62 @@ def test_token_select_deterministic_and_band():
     density = sum(len(x) for x in lists) / Sb ** 2
     G.log(f"   {band} near-band block pairs kept; mask density {density:.3f} "
           f"(candidates {cand.nnz / Sb ** 2:.3f})")
+
+
+def _kept_by_row(kept, cand, B, H):
+    """Kept lists of every (b, h, row) as compact host arrays (entries past a
+    row's count are not part of the result)."""
+    import torch
+    cnt = kept.kept_cnt.view(B * H, cand.num_blocks).cpu().numpy()
+    col = kept.kept_col.view(B * H, cand.nnz).cpu().numpy()
+    rp = cand.row_ptr.cpu().numpy()
+    out = []
+    for bh in range(B * H):
+        for a in range(cand.num_blocks):
+            out.append(col[bh, rp[a]:rp[a] + cnt[bh, a]].copy())
+    return out
+
+
+@pytest.mark.parametrize("case", ["wan13b_480p_mid", "bs64_mid"])
+def test_decision_pass_equals_ring_mark(case, monkeypatch):
+    """At B_s <= 64 the mark pass is the decision kernel (flags fixed from the
+    statistics pass's column sums by exact counts or Cantelli bounds) plus the
+    open-entry kernel; DR_TOKEN_RING_MARK=1 selects the ring mark pass, which
+    computes every tile. The kept lists must be equal on every row: the full
+    wan13b_480p shape under Table 2 "mid" (B_s = 32), and a B_s = 64 layout
+    whose blocks straddle frames (9 frames of 40x42 tokens)."""
+    import torch
+    G.log(f"[token] decision pass vs ring mark: {case}")
+    if case == "wan13b_480p_mid":
+        w, (tn, tf) = workloads.token_workload("wan13b_480p", "mid")
+        q, k, _ = G.device_qkv("wan13b_480p")
+        bs = w.block_size
+    else:
+        pr = workloads.TOKEN_PRESETS["mid"]
+        w = dataclasses.replace(workloads.get_workload("hunyuan_720p"), name="tok_bs64", heads=3, num_frames=9,
+                                frame_h=40, frame_w=42, seed=23, gamma=pr["gamma"], lam=pr["lam"],
+                                theta_c=pr["theta_c"], theta_m=pr["theta_m"])
+        tn, tf = pr["tau_near"], pr["tau_far"]
+        qb, kb, _ = workloads.qkv(w, as_bits=True)
+        q, k = _device(qb), _device(kb)
+        bs = 64
+    cand = G.dr().build_candidates(G.dr().radial_cfg(w.num_frames, w.tokens_per_frame, bs, w.gamma, w.lam,
+                                                     w.theta_c, w.theta_m))
+    B, H = q.shape[0], q.shape[1]
+    monkeypatch.delenv("DR_TOKEN_RING_MARK", raising=False)
+    fast = G.dr().token_select(q, k, cand, tn, tf, fused_heads=2)
+    torch.cuda.synchronize()
+    monkeypatch.setenv("DR_TOKEN_RING_MARK", "1")
+    # the library reads the C environment at each call: the setting must be visible there
+    import ctypes
+    libc = ctypes.CDLL(None)
+    libc.getenv.restype = ctypes.c_char_p
+    assert libc.getenv(b"DR_TOKEN_RING_MARK") == b"1"
+    ring = G.dr().token_select(q, k, cand, tn, tf, fused_heads=2)
+    torch.cuda.synchronize()
+    monkeypatch.delenv("DR_TOKEN_RING_MARK")
+    assert torch.equal(fast.kept_cnt, ring.kept_cnt), "kept counts differ"
+    lf, lr = _kept_by_row(fast, cand, B, H), _kept_by_row(ring, cand, B, H)
+    for i, (x, y) in enumerate(zip(lf, lr)):
+        np.testing.assert_array_equal(x, y, err_msg=f"{case}: row {i % cand.num_blocks} of (b, h) {i // cand.num_blocks}")
+    G.log(f"   {case}: {int(fast.kept_cnt.sum())} kept block pairs, equal")
