@@ -11,6 +11,7 @@
 
 #include "../../include/dynrad.h"
 #include "dr_internal.h"
+#include "token.h"
 
 namespace {
 

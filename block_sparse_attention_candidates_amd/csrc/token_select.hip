@@ -46,6 +46,7 @@
 #include <type_traits>
 
 #include "dr_internal.h"
+#include "token.h"
 #include "lds_dma.h"
 
 namespace dr {
