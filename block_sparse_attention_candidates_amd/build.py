@@ -31,8 +31,11 @@ COMMON = [
 
 
 # attention: inputs are finite (bf16 activations); without NaN semantics the
-# compiler drops the canonicalising copies in front of every float max
-EXTRA = {"attention.hip": ["-fno-honor-nans"]}
+# compiler drops the canonicalising copies in front of every float max. Its
+# machine scheduler runs the iterative ILP strategy: the same arithmetic and
+# bitwise the same outputs, measured 2-4% faster than the default order
+# (dense and dynamic-threshold launches, 1-2% static-ratio).
+EXTRA = {"attention.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]}
 
 
 def _run(cmd, verbose):

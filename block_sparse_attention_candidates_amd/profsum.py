@@ -88,11 +88,14 @@ ATTENTION_SOURCES = ("attention.hip", "groups.hip", "lds_dma.h", "dr_internal.h"
 
 
 def attention_source_digest() -> str:
-    """SHA-256 over the attention kernel's source files, in a fixed order."""
+    """SHA-256 over the attention kernel's source files, in a fixed order, and
+    the compiler flags its file is built with."""
+    from block_sparse_attention_candidates_amd import build
     h = hashlib.sha256()
     for name in ATTENTION_SOURCES:
         with open(os.path.join(PKG, "csrc", name), "rb") as fh:
             h.update(fh.read())
+    h.update(" ".join(build.COMMON[:-2] + build.EXTRA.get("attention.hip", [])).encode())
     return h.hexdigest()
 
 
