@@ -74,6 +74,20 @@ def test_traffic_scaling(tmp_path, monkeypatch):
     assert saved["w/static"]["attention_src_sha256"] == P.attention_source_digest()
 
 
+def test_attention_digest_follows_sources_and_flags(monkeypatch):
+    """The traffic record is tied to the attention kernel as built: its digest
+    changes with attention.hip's compiler flags and with the include path
+    left out (so it is the same on every machine)."""
+    from block_sparse_attention_candidates_amd import build
+    d0 = P.attention_source_digest()
+    monkeypatch.setitem(build.EXTRA, "attention.hip", build.EXTRA["attention.hip"][:1])
+    assert P.attention_source_digest() != d0
+    monkeypatch.undo()
+    assert P.attention_source_digest() == d0
+    monkeypatch.setattr(build, "COMMON", build.COMMON[:-1] + ["/elsewhere/include"])
+    assert P.attention_source_digest() == d0
+
+
 def test_sq_summary(tmp_path):
     """MFMA busy = MFMA busy cycles / SIMD-cycles; VALU busy = 4 x active VALU
     quad-cycles / SIMD-cycles; waits per wave-cycle; the last dispatch of the
